@@ -1,0 +1,88 @@
+"""Seeded synthetic inputs shared by the tests, the smoke check and the bench.
+
+This module holds none of the method's arithmetic: it only draws random
+numbers and lets PyTorch convert them to bfloat16 (round-to-nearest-even).
+The same tensor is then handed to both the GPU library and the CPU oracle.
+
+Distributions follow the transformer-shaped workloads the method is
+evaluated on: activations ~N(0,1), weights ~N(0,0.02), residual inputs with
+1% outliers scaled by 100, RMSNorm weights ~N(1,0.1), uniform integer
+targets, positions 0..max_pos-1 (optionally shuffled).
+"""
+import numpy as np
+import torch
+
+
+def _gen(seed):
+    return np.random.Generator(np.random.PCG64(int(seed)))
+
+
+def _cuda_gen(seed):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(int(seed))
+    return g
+
+
+def normal_bf16(shape, seed, std=1.0, mean=0.0, device="cpu"):
+    """bf16 tensor with entries ~N(mean, std^2)."""
+    shape = tuple(int(s) for s in shape)
+    if str(device).startswith("cuda"):
+        x = torch.randn(shape, generator=_cuda_gen(seed), device=device, dtype=torch.float32)
+    else:
+        x = torch.from_numpy(_gen(seed).standard_normal(shape, dtype=np.float32))
+    if std != 1.0:
+        x = x * std
+    if mean != 0.0:
+        x = x + mean
+    return x.to(torch.bfloat16)
+
+
+def outlier_bf16(shape, seed, p=0.01, scale=100.0, device="cpu"):
+    """~N(0,1) bf16 with each entry independently multiplied by `scale` with
+    probability `p` (independent Bernoulli mask per tensor)."""
+    shape = tuple(int(s) for s in shape)
+    if str(device).startswith("cuda"):
+        g = _cuda_gen(seed)
+        x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+        u = torch.rand(shape, generator=g, device=device, dtype=torch.float32)
+    else:
+        g = _gen(seed)
+        x = torch.from_numpy(g.standard_normal(shape, dtype=np.float32))
+        u = torch.from_numpy(g.random(shape, dtype=np.float32))
+    x = torch.where(u < p, x * scale, x)
+    return x.to(torch.bfloat16)
+
+
+def uniform_int(n, high, seed, device="cpu"):
+    """int32 tensor of n values uniform in [0, high)."""
+    if str(device).startswith("cuda"):
+        return torch.randint(0, int(high), (int(n),), generator=_cuda_gen(seed), device=device,
+                             dtype=torch.int32)
+    return torch.from_numpy(_gen(seed).integers(0, int(high), int(n), dtype=np.int32))
+
+
+def positions(n, max_pos, seed=None):
+    """Positions 0..n-1 modulo max_pos, shuffled when a seed is given."""
+    p = np.arange(int(n), dtype=np.int64) % int(max_pos)
+    if seed is not None:
+        p = _gen(seed).permutation(p)
+    return torch.from_numpy(p.astype(np.int32))
+
+
+def integer_bf16(shape, seed, lo=-8, hi=8):
+    """bf16 tensor of small integers in [lo, hi] (exactly representable)."""
+    shape = tuple(int(s) for s in shape)
+    x = _gen(seed).integers(lo, hi + 1, shape).astype(np.float32)
+    return torch.from_numpy(x).to(torch.bfloat16)
+
+
+def bits(t):
+    """numpy uint16 view of a bf16 tensor's bit patterns (copied to host)."""
+    assert t.dtype == torch.bfloat16
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def from_bits(b):
+    """bf16 tensor from numpy uint16 bit patterns."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
