@@ -1,0 +1,231 @@
+/*
+ * tbik.h -- C ABI of libtbik.so: tree-based invariant kernels (TBIK) for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes comes from these web pages:
+ *  [TBIK]  "Deterministic Inference across Tensor Parallel Sizes That
+ *          Eliminates Training-Inference Mismatch" (Zhang et al.), summary
+ *          page: Abstract (TP-invariant matmul and reduction primitives;
+ *          intra- and inter-GPU reduction orders aligned by one hierarchical
+ *          binary tree); "technical framework" (shard, reduce locally per
+ *          GPU, then combine GPUs by a binary tree); "key design".
+ *  [ROUND] winzheng.jp article on rounding-location alignment (Ke, Cai,
+ *          Wang), "surgical fix: three nodes": RoPE, SwiGLU and residual
+ *          RMSNorm keep fp32 intermediates and round to bf16 only at the
+ *          output.
+ *  [ISO]   nxmr.cn brief on SkyRL IsoExec, section 叁: an execution contract
+ *          with a fixed accumulation blocking; train and inference logprobs
+ *          compared bit by bit.
+ *  [DT]    "09｜分布式训练、数值稳定性与评测证据", section 2.1.1: a row-
+ *          parallel layer's shards each produce a full-shape partial output
+ *          that is summed.
+ *  [ND]    "01-推理阶段的非确定性", sections 2 and 5: the order of a
+ *          parallel sum, and atomics, change results.
+ *
+ * THE TREE.  Every fp32 reduction in this library (GEMM over K, row sums)
+ * follows one fixed tree over n leaves: T = the largest power of two <= 8
+ * dividing n; group g holds leaves [g*n/T, (g+1)*n/T); inside a group,
+ * neighbours are added level by level and an odd last element moves up one
+ * level unchanged; the T group sums are combined by a perfect binary tree.
+ * A tensor-parallel shard t of tp (tp | T) owns groups [t*T/tp,(t+1)*T/tp):
+ * its partial is a node of the tree, and combining the tp partials is the
+ * tree's top log2(tp) levels.  Results are therefore bit-identical for any
+ * tp in {1,2,4,8} that divides T, for any batch size, and for any launch
+ * configuration.  No kernel uses atomics.
+ *
+ * CONVENTIONS (all entry points).
+ *  - bf16 values are passed as 16-bit patterns (tbik_bf16).
+ *  - Every data pointer is DEVICE memory owned by the caller; the library
+ *    never allocates, frees or keeps a pointer after the call returns.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Outputs are valid once the stream reaches the call.
+ *  - Arguments are validated on the host before any launch; an invalid
+ *    call returns a negative TBIK_ERR_* code and launches nothing.
+ *  - Data pointers must be 16-byte aligned; leading dimensions (in
+ *    elements) must be multiples of 8.  Violations return TBIK_ERR_ALIGN.
+ *  - Outputs must not overlap inputs unless stated otherwise.
+ *  - Inputs must be finite; non-finite inputs give unspecified values (but
+ *    never out-of-bounds accesses).
+ *  - Entry points are thread-safe (no global mutable state).
+ */
+#ifndef TBIK_H
+#define TBIK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t tbik_bf16;
+
+enum {
+    TBIK_OK = 0,
+    TBIK_ERR_NULL = -1,       /* a required pointer is NULL                     */
+    TBIK_ERR_SHAPE = -2,      /* a size is negative, K % 64 != 0, ld too small  */
+    TBIK_ERR_TP = -3,         /* tp not in {1,2,4,8} or does not divide T       */
+    TBIK_ERR_ALIGN = -4,      /* pointer not 16-byte aligned or ld % 8 != 0     */
+    TBIK_ERR_WORKSPACE = -5,  /* workspace missing or too small                 */
+    TBIK_ERR_LAUNCH = -6,     /* the HIP runtime rejected a launch              */
+    TBIK_ERR_ARG = -7         /* another argument is out of range               */
+};
+
+enum { TBIK_LEAF_MFMA = 0, TBIK_LEAF_SCALAR = 1 };
+
+/* Library version as major*10000 + minor*100 + patch. */
+int tbik_version(void);
+
+/* Static description of an error code (never NULL). */
+const char *tbik_strerror(int code);
+
+/* T of the tree over n leaves (1, 2, 4 or 8); 0 when n <= 0. */
+int tbik_tree_groups(int64_t n);
+
+/* ------------------------------------------------------------------------
+ * GEMM:  C[i,j] = TREE_b( leaf_b(i,j) ),  b = 0 .. K/64-1,
+ *        leaf_b(i,j) = sum_{k=64b}^{64b+63} A[i,k] * W[j,k]   (fp32, from +0)
+ * [TBIK] Abstract (TP-invariant matrix multiplication); [ISO] 叁 (fixed
+ * accumulation blocking: 64-wide K blocks).
+ *
+ *  A       [M, K] bf16, row-major, row stride lda (elements)
+ *  W       [N, K] bf16, row-major, row stride ldw (the nn.Linear layout)
+ *  C       [M, N] fp32, row stride ldc; may be NULL if C_bf16 is given
+ *  C_bf16  [M, N] bf16 (round-to-nearest-even of C), row stride ldc; NULL
+ *          to skip.  At least one of C, C_bf16 is required.
+ *  K       positive multiple of 64.
+ *  leaf_mode
+ *    TBIK_LEAF_MFMA    a leaf is two chained v_mfma_f32_16x16x32_bf16 from a
+ *                      zero accumulator (k 0..31 then 32..63 of the block).
+ *                      The same instruction sequence is used for every
+ *                      shape, tile and tp, so the bits do not depend on M,
+ *                      on the row's position in the batch or on tp.
+ *    TBIK_LEAF_SCALAR  a leaf is 64 sequential fp32 fma in increasing k;
+ *                      bit-exact with the CPU oracle.  Slow; for checking.
+ * ---------------------------------------------------------------------- */
+int tbik_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
+              float *C, int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K,
+              int leaf_mode, void *stream);
+
+/* Strided-batched form: for b in [0,batch): A + b*strideA, W + b*strideW,
+ * C + b*strideC, C_bf16 + b*strideC (strides in elements, multiples of 8).
+ * Each batch entry is computed exactly as tbik_gemm would compute it. */
+int tbik_gemm_strided_batched(const tbik_bf16 *A, int64_t lda, int64_t strideA,
+                              const tbik_bf16 *W, int64_t ldw, int64_t strideW,
+                              float *C, int64_t ldc, int64_t strideC, tbik_bf16 *C_bf16,
+                              int M, int N, int K, int batch, int leaf_mode, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Simulated tensor-parallel GEMM ([DT] 2.1.1 row-parallel partial sums;
+ * [TBIK] "technical framework").  K is split into tp shards aligned with
+ * the tree's groups; shard t computes its partial P_t (a node of the tree)
+ * into ws[t] = ws + t*M*N (fp32, dense [M,N]); a combine kernel then runs
+ * the top log2(tp) levels of the tree over the tp partials into C/C_bf16.
+ * The result is bit-identical to tbik_gemm with the same leaf_mode.  ws
+ * keeps the partials after the call (they are what real TP would exchange).
+ *  tp      1, 2, 4 or 8; must divide T of the tree over K/64 leaves.
+ *  ws      device workspace of at least tbik_gemm_tpsim_workspace_bytes().
+ * ---------------------------------------------------------------------- */
+size_t tbik_gemm_tpsim_workspace_bytes(int M, int N, int K, int tp);
+
+int tbik_gemm_tpsim(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
+                    float *C, int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int tp,
+                    int leaf_mode, float *ws, size_t ws_bytes, void *stream);
+
+/* Only the combine step of tbik_gemm_tpsim: C = top tree over ws[0..tp-1]
+ * (dense [tp][M][N] fp32 partials).  Lets a caller that produced the
+ * partials elsewhere (e.g. on several GPUs) finish the same tree. */
+int tbik_tree_combine(const float *ws, int tp, float *C, int64_t ldc, tbik_bf16 *C_bf16,
+                      int M, int N, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Fused residual-add + RMSNorm ([ROUND] "three nodes"; [TBIK] reduction
+ * primitives).  Per row, all intermediates fp32:
+ *   h = x + r;  r_out = bf16(h);  ss = TREE_j(h_j * h_j);  mean = ss / H;
+ *   rstd = 1 / sqrt(mean + eps)   (correctly rounded divide and sqrt);
+ *   y = bf16((h * rstd) * w).
+ *  x, r, y, r_out  [rows, H] bf16 with row stride ld; r_out may be NULL.
+ *  w               [H] bf16.
+ *  H               1 .. 65536;  eps >= 0.
+ * ---------------------------------------------------------------------- */
+int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
+                          tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,
+                          float eps, void *stream);
+
+/* ------------------------------------------------------------------------
+ * RoPE, rotate-half pairing ([ROUND] "three nodes": fp32 intermediates).
+ * For token t, head h, i < d/2, with c = cos_tab[pos[t], i], s = sin_tab[..]:
+ *   y[i]       = bf16(x[i]*c - x[i+d/2]*s)
+ *   y[i+d/2]   = bf16(x[i+d/2]*c + x[i]*s)
+ * each product rounded to fp32 separately (no fma).
+ *  x, y      [T, heads, d] bf16; token stride ld_token >= heads*d; heads
+ *            contiguous with stride d.  y == x (in place) is allowed.
+ *  pos       [T] int32, each in [0, max_pos) (out-of-range positions are
+ *            clamped to the table; the result is then unspecified).
+ *  cos_tab, sin_tab  [max_pos, d/2] fp32 (see tbik_rope_table).
+ *  d         even, 2 .. 1024, d/2 a multiple of 4.
+ * ---------------------------------------------------------------------- */
+int tbik_rope(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float *cos_tab,
+              const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+              int max_pos, void *stream);
+
+/* HOST helper: cos_tab/sin_tab (host memory, [max_pos, d/2] fp32) with
+ * angle = p * theta^(-2i/d) evaluated in binary64 and cos/sin rounded once
+ * to fp32 (an fp32 angle would lose ~1e-3 rad at p ~ 3e4). */
+int tbik_rope_table(double theta, int head_dim, int max_pos, float *cos_tab, float *sin_tab);
+
+/* ------------------------------------------------------------------------
+ * SwiGLU ([ROUND] "three nodes"): out = bf16((g / (1 + EXP(-g))) * u), all
+ * fp32, one correctly rounded division.  EXP is the library's fp32
+ * exponential (Cody-Waite reduction, degree-7 Taylor polynomial; < 1 ulp).
+ *  gate, up, out  [rows, cols] bf16 with row strides ld_gate, ld_up, ld_out.
+ * ---------------------------------------------------------------------- */
+int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows,
+                int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Log-softmax + target gather ([TBIK] reduction primitives; [ISO] 叁 logprob
+ * comparison).  Per row i:
+ *   m = max_j x_j (exact);  e_j = EXP(x_j - m);  s = TREE_j(e_j);
+ *   out_lp[i] = (x_{t_i} - m) - LOG(s).
+ * The tree's T groups are the vocab-parallel shards: with tp > 1 the
+ * library materialises each shard's partial sum in ws (what vocab-parallel
+ * ranks would exchange) and combines them with the top of the tree; the
+ * result is bit-identical for every tp.
+ *  logits   [M, V] fp32, row stride ld.
+ *  targets  [M] int32 in [0, V) (out-of-range targets: out_lp = NaN).
+ *  out_lp   [M] fp32.
+ *  ws       at least tbik_logsoftmax_workspace_bytes(M, V, tp) bytes.
+ * ---------------------------------------------------------------------- */
+size_t tbik_logsoftmax_workspace_bytes(int M, int V, int tp);
+
+int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targets,
+                           float *out_lp, int M, int V, int tp, float *ws, size_t ws_bytes,
+                           void *stream);
+
+/* ------------------------------------------------------------------------
+ * Causal softmax over attention scores (decoder composition).
+ *   z_j = S[i,j] * scale;  visible keys j <= i + offset;
+ *   m = max of visible z;  e_j = EXP(z_j - m) if visible else +0;
+ *   s = TREE_j(e_j) over all Lk keys;  P[i,j] = bf16(e_j / s).
+ *  S  [batch][Lq, Lk] fp32 (row stride ld_s, batch stride stride_s)
+ *  P  [batch][Lq, Lk] bf16 (row stride ld_p, batch stride stride_p)
+ *  offset >= 0;  Lk <= 65536.
+ * ---------------------------------------------------------------------- */
+int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf16 *P,
+                        int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
+                        float scale, void *stream);
+
+/* ------------------------------------------------------------------------
+ * The library's fp32/bf16 primitives applied elementwise (for checking):
+ *  op 0: EXP(x)   op 1: LOG(x)   op 2: bf16 round-to-nearest-even of x,
+ *  widened back to fp32.   x, y: [n] fp32 device arrays.
+ * ---------------------------------------------------------------------- */
+enum { TBIK_PRIM_EXP = 0, TBIK_PRIM_LOG = 1, TBIK_PRIM_BF16 = 2 };
+
+int tbik_primitive(int op, const float *x, float *y, int64_t n, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TBIK_H */

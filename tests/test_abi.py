@@ -1,0 +1,145 @@
+"""CPU checks of the C ABI boundary (no kernel is launched here).
+
+* every function declared in include/tbik.h is exported by libtbik.so;
+* invalid arguments are rejected on the host with the documented code
+  (every case below fails validation, so no device pointer is touched);
+* the host RoPE-table helper equals the oracle's table bit for bit.
+"""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, E_NULL, E_SHAPE, E_TP, E_ALIGN, E_WS, E_LAUNCH, E_ARG = 0, -1, -2, -3, -4, -5, -6, -7
+
+FAKE = C.c_void_p(1 << 20)        # aligned, never dereferenced (validation fails first)
+FAKE2 = C.c_void_p(2 << 20)
+FAKE3 = C.c_void_p(3 << 20)
+MISAL = C.c_void_p((1 << 20) + 4)
+
+
+@pytest.fixture(scope="module")
+def L():
+    import tp_invariant_numerics_amd as t
+    return t.lib()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "tbik.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tbik_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("tbik_gemm", "tbik_gemm_tpsim", "tbik_rmsnorm_residual", "tbik_logsoftmax_gather",
+              "tbik_rope", "tbik_swiglu"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_version_and_strerror(L):
+    import tp_invariant_numerics_amd as t
+    assert t.tbik_version() >= 10000
+    for code in (OK, E_NULL, E_SHAPE, E_TP, E_ALIGN, E_WS, E_LAUNCH, E_ARG, 17):
+        assert isinstance(t.tbik_strerror(code), str) and t.tbik_strerror(code)
+
+
+def test_tree_groups(L):
+    assert [L.tbik_tree_groups(n) for n in (0, 1, 3, 6, 12, 28, 224, 151936)] == \
+        [0, 1, 1, 2, 4, 4, 8, 8]
+
+
+def test_gemm_validation(L):
+    g = L.tbik_gemm
+    # A NULL / W NULL / both outputs NULL
+    assert g(None, 64, FAKE, 64, FAKE2, 64, None, 4, 4, 64, 0, None) == E_NULL
+    assert g(FAKE, 64, None, 64, FAKE2, 64, None, 4, 4, 64, 0, None) == E_NULL
+    assert g(FAKE, 64, FAKE2, 64, None, 64, None, 4, 4, 64, 0, None) == E_NULL
+    # K not a positive multiple of 64, negative sizes, small leading dims
+    assert g(FAKE, 128, FAKE2, 128, FAKE3, 64, None, 4, 4, 100, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 0, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, -1, 4, 64, 0, None) == E_SHAPE
+    assert g(FAKE, 32, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 8, None, 4, 16, 64, 0, None) == E_SHAPE
+    # alignment: misaligned pointer, leading dimension not a multiple of 8
+    assert g(MISAL, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_ALIGN
+    assert g(FAKE, 68, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_ALIGN
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 12, None, 4, 4, 64, 0, None) == E_ALIGN
+    # leaf mode
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 7, None) == E_ARG
+    # tree groups beyond the supported depth (K = 64 * 1031, a prime leaf count)
+    assert g(FAKE, 66000, FAKE2, 66000, FAKE3, 64, None, 1, 1, 64 * 1031, 0, None) == E_SHAPE
+
+
+def test_gemm_tpsim_validation(L):
+    g = L.tbik_gemm_tpsim
+    # tp not in {1,2,4,8}; tp not dividing T (K = 64*28 has T = 4)
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 3, 0, FAKE, 1 << 20, None) == E_TP
+    assert g(FAKE, 1792, FAKE2, 1792, FAKE3, 64, None, 4, 4, 1792, 8, 0, FAKE, 1 << 20,
+             None) == E_TP
+    # workspace missing / too small
+    assert g(FAKE, 1024, FAKE2, 1024, FAKE3, 64, None, 4, 4, 1024, 2, 0, None, 0,
+             None) == E_WS
+    need = L.tbik_gemm_tpsim_workspace_bytes(4, 4, 1024, 2)
+    assert need == 2 * 4 * 4 * 4
+    assert g(FAKE, 1024, FAKE2, 1024, FAKE3, 64, None, 4, 4, 1024, 2, 0, FAKE, need - 1,
+             None) == E_WS
+
+
+def test_combine_validation(L):
+    assert L.tbik_tree_combine(None, 2, FAKE, 8, None, 1, 8, None) == E_NULL
+    assert L.tbik_tree_combine(FAKE, 3, FAKE2, 8, None, 1, 8, None) == E_TP
+    assert L.tbik_tree_combine(FAKE, 2, FAKE2, 4, None, 1, 8, None) == E_SHAPE
+
+
+def test_rowop_validation(L):
+    r = L.tbik_rmsnorm_residual
+    assert r(None, FAKE, FAKE, FAKE, None, 1, 64, 64, 1e-6, None) == E_NULL
+    assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 0, 64, 1e-6, None) == E_SHAPE
+    assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 64, 32, 1e-6, None) == E_SHAPE
+    assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 64, 64, -1.0, None) == E_ARG
+    assert r(FAKE, FAKE, FAKE, MISAL, None, 1, 64, 64, 1e-6, None) == E_ALIGN
+    ro = L.tbik_rope
+    assert ro(FAKE, FAKE, None, FAKE, FAKE, 1, 1, 128, 128, 16, None) == E_NULL
+    assert ro(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 130, 136, 16, None) == E_SHAPE
+    assert ro(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, 128, 128, 16, None) == E_SHAPE
+    sw = L.tbik_swiglu
+    assert sw(FAKE, None, FAKE, 1, 8, 8, 8, 8, None) == E_NULL
+    assert sw(FAKE, FAKE, FAKE, 1, 16, 8, 16, 16, None) == E_SHAPE
+    assert sw(FAKE, FAKE, MISAL, 1, 8, 8, 8, 8, None) == E_ALIGN
+    ls = L.tbik_logsoftmax_gather
+    assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 3, FAKE, 1 << 20, None) == E_TP
+    assert ls(FAKE, 24, FAKE, FAKE, 2, 12, 8, FAKE, 1 << 20, None) == E_TP   # T(12) = 4
+    assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 1, None, 0, None) == E_WS
+    assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 1, FAKE, 4, None) == E_WS
+    sc = L.tbik_softmax_causal
+    assert sc(FAKE, 64, 0, FAKE2, 64, 0, 4, 64, 1, -1, 1.0, None) == E_SHAPE
+    assert sc(FAKE, 64, 0, FAKE2, 64, 0, 4, 64, 1, 0, float("inf"), None) == E_ARG
+    assert L.tbik_primitive(9, FAKE, FAKE2, 4, None) == E_ARG
+    assert L.tbik_primitive(0, None, FAKE2, 4, None) == E_NULL
+
+
+def test_empty_shapes_are_no_ops(L):
+    # M = 0 / rows = 0 return OK before touching any pointer or launching
+    assert L.tbik_gemm(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 0, 4, 64, 0, None) == OK
+    assert L.tbik_rmsnorm_residual(FAKE, FAKE, FAKE, FAKE2, None, 0, 64, 64, 1e-6, None) == OK
+    assert L.tbik_swiglu(FAKE, FAKE, FAKE2, 0, 8, 8, 8, 8, None) == OK
+    assert L.tbik_primitive(0, FAKE, FAKE2, 0, None) == OK
+
+
+def test_rope_table_equals_oracle(orc):
+    import tp_invariant_numerics_amd as t
+    for theta, d, maxp in ((1e6, 128, 32768), (1e4, 64, 4096), (500000.0, 16, 100)):
+        c, s = t.tbik_rope_table(theta, d, maxp)
+        oc, os_ = orc.rope_table(theta, d, maxp)
+        assert np.array_equal(c.numpy().view(np.uint32), oc.view(np.uint32))
+        assert np.array_equal(s.numpy().view(np.uint32), os_.view(np.uint32))

@@ -1,0 +1,325 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Bit-exact for: the primitives (EXP, LOG, bf16 rounding), the scalar-leaf
+GEMM and its simulated tensor-parallel partials, residual RMSNorm, RoPE,
+SwiGLU, log-softmax + gather (including its shard sums) and the causal
+softmax.  The MFMA-leaf GEMM has hardware-defined leaf bits, so it is held
+to: bitwise invariance across tp and batch size (TBIK summary page,
+Abstract), a normwise error <= 1e-5 against the binary64 product, an
+elementwise summation bound, and exact results on integer data.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import tp_invariant_numerics_amd as tb
+from tp_invariant_numerics_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    tb.lib()
+
+
+def u32(x):
+    return np.ascontiguousarray(np.asarray(x, np.float32)).view(np.uint32)
+
+
+def f32_bits_t(t):
+    return t.detach().cpu().numpy().view(np.uint32)
+
+
+def same_bits(a, b):
+    return np.array_equal(np.asarray(a).view(np.uint32), np.asarray(b).view(np.uint32))
+
+
+def bits(t):
+    return inputs.bits(t)
+
+
+# ------------------------------------------------------------------ primitives
+@pytest.mark.parametrize("op", [tb.PRIM_EXP, tb.PRIM_LOG, tb.PRIM_BF16])
+def test_primitives_bitexact(orc, op):
+    rng = np.random.default_rng(100 + op)
+    pats = rng.integers(0, 2 ** 32, 1 << 22, dtype=np.uint64).astype(np.uint32)
+    if op == tb.PRIM_EXP:
+        # dense coverage of the finite-result range too
+        extra = np.linspace(-110, 95, 1 << 20, dtype=np.float32).view(np.uint32)
+    elif op == tb.PRIM_LOG:
+        extra = np.arange(1, 1 << 20, dtype=np.uint32)            # subnormals
+    else:
+        extra = np.arange(0, 1 << 20, dtype=np.uint32) * 4093
+    x = np.concatenate([pats, extra]).view(np.float32)
+    say("primitive", op, x.size)
+    y = tb.tbik_primitive(op, torch.from_numpy(x).to(DEV)).cpu().numpy()
+    if op == tb.PRIM_EXP:
+        ref = orc.expf(x)
+    elif op == tb.PRIM_LOG:
+        ref = orc.logf(x)
+    else:
+        ref = orc.bf16_to_f32(orc.f32_to_bf16(x))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert same_bits(y[~nan], ref[~nan])
+
+
+# ------------------------------------------------------------------ GEMM
+def _gen_gemm(M, N, K, seed, wstd=1.0):
+    A = inputs.normal_bf16((M, K), seed)
+    W = inputs.normal_bf16((N, K), seed + 1, std=wstd)
+    return A, W
+
+
+SCALAR_SHAPES = [(16, 256, 1024), (37, 83, 448), (1, 7, 64), (5, 33, 1792), (32, 64, 14336),
+                 (3, 9, 64 * 11), (2, 5, 64 * 25)]
+
+
+@pytest.mark.parametrize("M,N,K", SCALAR_SHAPES)
+def test_gemm_scalar_bitexact(orc, M, N, K):
+    A, W = _gen_gemm(M, N, K, 1000 + K)
+    say("scalar gemm", M, N, K)
+    C, Cb = tb.tbik_gemm(A.to(DEV), W.to(DEV), leaf_mode=tb.LEAF_SCALAR, want_bf16=True)
+    ref = orc.gemm(bits(A), bits(W))
+    assert same_bits(C.cpu().numpy(), ref)
+    assert np.array_equal(bits(Cb), orc.f32_to_bf16(ref).reshape(M, N))
+
+
+def test_gemm_scalar_leaf_probes_golden(orc):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "gemm_leaf_probes.txt")
+    for line in open(path):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        K, big, expected = (int(t) for t in line.split())
+        A = torch.ones((1, K), dtype=torch.bfloat16)
+        W = torch.ones((1, K), dtype=torch.bfloat16)
+        W[0, big] = 2.0 ** 24
+        say("leaf probe", K, big)
+        C, _ = tb.tbik_gemm(A.to(DEV), W.to(DEV), leaf_mode=tb.LEAF_SCALAR)
+        assert C.item() == float(expected), (K, big, C.item())
+
+
+@pytest.mark.parametrize("M,N,K,tps", [(16, 256, 1024, (1, 2, 4, 8)),
+                                       (8, 40, 14336, (1, 2, 4, 8)),
+                                       (5, 24, 64 * 28, (1, 2, 4))])
+def test_gemm_tpsim_scalar_bitexact(orc, M, N, K, tps):
+    A, W = _gen_gemm(M, N, K, 2000 + K, wstd=0.02)
+    for tp in tps:
+        say("tpsim scalar", M, N, K, tp)
+        C, _, ws = tb.tbik_gemm_tpsim(A.to(DEV), W.to(DEV), tp, leaf_mode=tb.LEAF_SCALAR)
+        refC, refws = orc.gemm_tpsim(bits(A), bits(W), tp)
+        assert same_bits(C.cpu().numpy(), refC), tp
+        assert same_bits(ws.cpu().numpy(), refws), tp
+
+
+@pytest.mark.parametrize("M,N,K,tps", [(16, 256, 1024, (1, 2, 4, 8)),
+                                       (1, 4096, 14336, (1, 2, 4, 8)),
+                                       (32, 4096, 14336, (1, 2, 4, 8)),
+                                       (256, 4096, 14336, (1, 2, 4, 8)),
+                                       (77, 300, 64 * 28, (1, 2, 4))])
+def test_gemm_mfma_tp_invariant(M, N, K, tps):
+    A = inputs.normal_bf16((M, K), 3000 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 3001 + M, std=0.02, device=DEV)
+    say("mfma tp invariance", M, N, K)
+    ref, _ = tb.tbik_gemm(A, W)
+    refb = f32_bits_t(ref)
+    for tp in tps:
+        C, _, ws = tb.tbik_gemm_tpsim(A, W, tp)
+        assert np.array_equal(f32_bits_t(C), refb), tp
+        # the combine of the partials equals the top of the tree
+        again = tb.tbik_tree_combine(ws)
+        assert np.array_equal(f32_bits_t(again), refb), tp
+
+
+def test_gemm_mfma_batch_invariant():
+    K, N = 14336, 4096
+    A = inputs.normal_bf16((256, K), 4000, device=DEV)
+    W = inputs.normal_bf16((N, K), 4001, std=0.02, device=DEV)
+    ref, _ = tb.tbik_gemm(A, W)
+    refb = f32_bits_t(ref)
+    bad = []
+    for M in range(1, 257):
+        C, _ = tb.tbik_gemm(A[:M], W)
+        if not np.array_equal(f32_bits_t(C), refb[:M]):
+            bad.append(M)
+    assert not bad, bad
+    # rows at other offsets and in permuted order
+    g = torch.Generator().manual_seed(5)
+    perm = torch.randperm(256, generator=g).to(DEV)
+    C, _ = tb.tbik_gemm(A[perm].contiguous(), W)
+    assert np.array_equal(f32_bits_t(C), refb[perm.cpu().numpy()])
+    for off, M in ((3, 17), (100, 33), (200, 56), (255, 1)):
+        C, _ = tb.tbik_gemm(A[off:off + M], W)
+        assert np.array_equal(f32_bits_t(C), refb[off:off + M]), (off, M)
+
+
+def test_gemm_mfma_column_slices_invariant():
+    # column-parallel slices of W give the same bits as the full product
+    K, N, M = 4096, 1024, 64
+    A = inputs.normal_bf16((M, K), 4100, device=DEV)
+    W = inputs.normal_bf16((N, K), 4101, std=0.02, device=DEV)
+    ref = f32_bits_t(tb.tbik_gemm(A, W)[0])
+    for lo, hi in ((0, 256), (256, 512), (8, 136), (1000, 1024)):
+        C, _ = tb.tbik_gemm(A, W[lo:hi])
+        assert np.array_equal(f32_bits_t(C), ref[:, lo:hi]), (lo, hi)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 256, 1024), (64, 256, 14336), (40, 96, 4096),
+                                   (1, 64, 14336), (300, 70, 2048)])
+def test_gemm_mfma_accuracy(orc, M, N, K):
+    A, W = _gen_gemm(M, N, K, 5000 + M, wstd=0.02)
+    say("mfma accuracy", M, N, K)
+    C = tb.tbik_gemm(A.to(DEV), W.to(DEV))[0].cpu().numpy().astype(np.float64)
+    C64 = orc.gemm_f64(bits(A), bits(W))
+    rel = np.max(np.abs(C - C64)) / np.max(np.abs(C64))
+    assert rel <= 1e-5, rel
+    # summation bound valid for any fp32 order, with u = 2^-23 to allow
+    # truncating accumulation inside the matrix unit
+    a = orc.bf16_to_f32(bits(A)).astype(np.float64)
+    w = orc.bf16_to_f32(bits(W)).astype(np.float64)
+    nb = K // 64
+    T = orc.tree_T(nb)
+    d = math.ceil(math.log2(max(1, nb // T))) + int(math.log2(T))
+    n = 64 + d
+    u = 2.0 ** -23
+    bound = n * u / (1 - n * u) * (np.abs(a) @ np.abs(w).T)
+    assert np.all(np.abs(C - C64) <= bound)
+
+
+def test_gemm_mfma_integer_exact(orc):
+    for (M, N, K) in ((16, 256, 1024), (33, 40, 14336)):
+        A = inputs.integer_bf16((M, K), 6000 + M, -4, 4)
+        W = inputs.integer_bf16((N, K), 6001 + M, -4, 4)
+        C = tb.tbik_gemm(A.to(DEV), W.to(DEV))[0].cpu().numpy()
+        ai = A.float().numpy().astype(np.int64)
+        wi = W.float().numpy().astype(np.int64)
+        assert np.array_equal(C.astype(np.int64), ai @ wi.T)
+
+
+def test_gemm_mfma_bf16_output_is_rounded_fp32(orc):
+    A, W = _gen_gemm(48, 200, 2048, 7000)
+    C, Cb = tb.tbik_gemm(A.to(DEV), W.to(DEV), want_bf16=True)
+    assert np.array_equal(bits(Cb), orc.f32_to_bf16(C.cpu().numpy()).reshape(48, 200))
+    _, Cb2 = tb.tbik_gemm(A.to(DEV), W.to(DEV), want_fp32=False, want_bf16=True)
+    assert np.array_equal(bits(Cb2), bits(Cb))
+
+
+def test_gemm_strided_batched_equals_single(orc):
+    B, M, N, K = 3, 40, 72, 512
+    A = inputs.normal_bf16((B, M, K), 7100, device=DEV)
+    W = inputs.normal_bf16((B, N, K), 7101, device=DEV)
+    C, _ = tb.tbik_gemm_strided_batched(A, W)
+    Cs, _ = tb.tbik_gemm_strided_batched(A, W, leaf_mode=tb.LEAF_SCALAR)
+    for b in range(B):
+        one, _ = tb.tbik_gemm(A[b], W[b])
+        assert np.array_equal(f32_bits_t(C[b]), f32_bits_t(one))
+        assert same_bits(Cs[b].cpu().numpy(), orc.gemm(bits(A[b]), bits(W[b])))
+
+
+# ------------------------------------------------------------------ RMSNorm
+@pytest.mark.parametrize("rows,H", [(1, 4096), (7, 4096), (256, 4096), (4096, 4096),
+                                    (5, 2048), (3, 5120), (4, 1000), (9, 96), (2, 8), (3, 4104)])
+def test_rmsnorm_bitexact(orc, rows, H):
+    x = inputs.outlier_bf16((rows, H), 8000 + H)
+    r = inputs.outlier_bf16((rows, H), 8001 + H)
+    w = inputs.normal_bf16((H,), 8002 + H, std=0.1, mean=1.0)
+    say("rmsnorm", rows, H)
+    y, r_out = tb.tbik_rmsnorm_residual(x.to(DEV), r.to(DEV), w.to(DEV), 1e-6)
+    ry, rr = orc.rmsnorm_residual(bits(x), bits(r), bits(w), 1e-6)
+    assert np.array_equal(bits(y), ry)
+    assert np.array_equal(bits(r_out), rr)
+
+
+def test_rmsnorm_rows_invariant():
+    x = inputs.outlier_bf16((512, 4096), 8100, device=DEV)
+    r = inputs.outlier_bf16((512, 4096), 8101, device=DEV)
+    w = inputs.normal_bf16((4096,), 8102, std=0.1, mean=1.0, device=DEV)
+    y, _ = tb.tbik_rmsnorm_residual(x, r, w)
+    for lo, hi in ((0, 1), (5, 6), (100, 357)):
+        y2, _ = tb.tbik_rmsnorm_residual(x[lo:hi], r[lo:hi], w)
+        assert torch.equal(y2.view(torch.int16), y[lo:hi].view(torch.int16))
+
+
+# ------------------------------------------------------------------ RoPE
+@pytest.mark.parametrize("T,heads,d", [(2048, 16, 128), (33, 3, 64), (5, 1, 8)])
+def test_rope_bitexact(orc, T, heads, d):
+    x = inputs.normal_bf16((T, heads, d), 9000 + T)
+    pos = inputs.positions(T, 32768, seed=9)
+    pos = torch.from_numpy((pos.numpy().astype(np.int64) * 13 % 32768).astype(np.int32))
+    c, s = orc.rope_table(1e6, d, 32768)
+    say("rope", T, heads, d)
+    y = tb.tbik_rope(x.to(DEV), pos.to(DEV), torch.from_numpy(c).to(DEV),
+                     torch.from_numpy(s).to(DEV))
+    ref = orc.rope(bits(x), pos.numpy(), c, s)
+    assert np.array_equal(bits(y), ref)
+
+
+def test_rope_in_place(orc):
+    x = inputs.normal_bf16((64, 4, 128), 9100)
+    pos = inputs.positions(64, 32768, seed=3)
+    c, s = orc.rope_table(1e6, 128, 32768)
+    xd = x.to(DEV)
+    tb.tbik_rope(xd, pos.to(DEV), torch.from_numpy(c).to(DEV), torch.from_numpy(s).to(DEV), y=xd)
+    assert np.array_equal(bits(xd), orc.rope(bits(x), pos.numpy(), c, s))
+
+
+# ------------------------------------------------------------------ SwiGLU
+@pytest.mark.parametrize("rows,cols", [(64, 14336), (4096, 14336), (3, 17), (5, 40)])
+def test_swiglu_bitexact(orc, rows, cols):
+    g = inputs.normal_bf16((rows, cols), 9500 + rows, std=3.0)
+    u = inputs.normal_bf16((rows, cols), 9501 + rows)
+    say("swiglu", rows, cols)
+    y = tb.tbik_swiglu(g.to(DEV), u.to(DEV))
+    assert np.array_equal(bits(y), orc.swiglu(bits(g), bits(u)))
+
+
+def test_swiglu_extreme_gates(orc):
+    vals = np.array([0, -0.0, 1, -1, 88, -88, 89, -89, 100, -100, 1e-30, -1e-30, 3e38, -3e38],
+                    np.float32)
+    g = torch.from_numpy(np.tile(vals, 8).reshape(8, -1)).to(torch.bfloat16)
+    u = inputs.normal_bf16(g.shape, 9600)
+    y = tb.tbik_swiglu(g.to(DEV), u.to(DEV))
+    assert np.array_equal(bits(y), orc.swiglu(bits(g), bits(u)))
+
+
+# ------------------------------------------------------------------ log-softmax
+@pytest.mark.parametrize("M,V,tps", [(8, 151936, (1, 2, 4, 8)), (16, 32000, (1, 2, 4, 8)),
+                                     (5, 1000, (1, 2, 4, 8)), (3, 12, (1, 2, 4)),
+                                     (4, 7, (1,))])
+def test_logsoftmax_bitexact(orc, M, V, tps):
+    rng = np.random.default_rng(V)
+    logits = (rng.standard_normal((M, V)) * 3).astype(np.float32)
+    tgt = rng.integers(0, V, M).astype(np.int32)
+    ld = (V + 7) // 8 * 8
+    dev_logits = torch.zeros((M, ld), dtype=torch.float32, device=DEV)
+    dev_logits[:, :V] = torch.from_numpy(logits).to(DEV)
+    for tp in tps:
+        say("logsoftmax", M, V, tp)
+        lp, ws = tb.tbik_logsoftmax_gather(dev_logits[:, :V], torch.from_numpy(tgt).to(DEV), tp)
+        ref, nodes = orc.logsoftmax_gather(logits, tgt, tp)
+        assert same_bits(lp.cpu().numpy(), ref), tp
+        got_nodes = tb.logsoftmax_shard_nodes(ws, M, tp).cpu().numpy()
+        assert same_bits(got_nodes, nodes), tp
+
+
+# ------------------------------------------------------------------ causal softmax
+@pytest.mark.parametrize("B,Lq,Lk,offset", [(2, 512, 512, 0), (3, 64, 128, 64), (1, 9, 24, 0)])
+def test_softmax_causal_bitexact(orc, B, Lq, Lk, offset):
+    rng = np.random.default_rng(Lk + offset)
+    S = (rng.standard_normal((B, Lq, Lk)) * 30).astype(np.float32)
+    scale = np.float32(1 / math.sqrt(128))
+    say("softmax_causal", B, Lq, Lk, offset)
+    P = tb.tbik_softmax_causal(torch.from_numpy(S).to(DEV), offset, float(scale))
+    for b in range(B):
+        assert np.array_equal(bits(P[b]), orc.softmax_causal(S[b], offset, scale))

@@ -1,0 +1,307 @@
+"""tp_invariant_numerics_amd -- tree-based invariant kernels (TBIK) on MI355X.
+
+Thin Python binding of libtbik.so (C ABI in include/tbik.h).  Every function
+here only checks tensor dtypes/devices, allocates outputs with PyTorch and
+passes raw device pointers plus the current HIP stream to the library; all
+arithmetic runs in the library's HIP kernels.  There is no fallback: if the
+library is missing or no GPU is present, the call raises.
+
+Function names mirror the C entry points (``tbik_gemm`` -> ``tbik_gemm``).
+"""
+import ctypes as C
+import os
+
+import torch
+
+from . import build as _build
+
+__all__ = [
+    "TbikError", "lib", "tbik_version", "tbik_strerror", "tbik_tree_groups", "tbik_gemm",
+    "tbik_gemm_strided_batched", "tbik_gemm_tpsim", "tbik_gemm_tpsim_workspace_bytes",
+    "tbik_tree_combine", "tbik_rmsnorm_residual", "tbik_rope", "tbik_rope_table",
+    "tbik_swiglu", "tbik_logsoftmax_gather", "tbik_logsoftmax_workspace_bytes",
+    "tbik_softmax_causal", "tbik_primitive", "LEAF_MFMA", "LEAF_SCALAR",
+]
+
+LEAF_MFMA = 0
+LEAF_SCALAR = 1
+PRIM_EXP, PRIM_LOG, PRIM_BF16 = 0, 1, 2
+
+_lib = None
+
+
+class TbikError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__("%s: %s (code %d)" % (what, _strerror(code), code))
+        self.code = code
+
+
+def _strerror(code):
+    try:
+        return lib().tbik_strerror(code).decode()
+    except Exception:  # pragma: no cover - library not loadable
+        return "error"
+
+
+_SIGS = None
+
+
+def _sigs():
+    p, i32, i64, f32, f64, sz = C.c_void_p, C.c_int, C.c_int64, C.c_float, C.c_double, C.c_size_t
+    return {
+        "tbik_version": (i32, []),
+        "tbik_strerror": (C.c_char_p, [i32]),
+        "tbik_tree_groups": (i32, [i64]),
+        "tbik_gemm": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, p]),
+        "tbik_gemm_strided_batched": (i32, [p, i64, i64, p, i64, i64, p, i64, i64, p, i32, i32,
+                                            i32, i32, i32, p]),
+        "tbik_gemm_tpsim_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "tbik_gemm_tpsim": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, i32, p, sz, p]),
+        "tbik_tree_combine": (i32, [p, i32, p, i64, p, i32, i32, p]),
+        "tbik_rmsnorm_residual": (i32, [p, p, p, p, p, i32, i32, i64, f32, p]),
+        "tbik_rope": (i32, [p, p, p, p, p, i32, i32, i32, i64, i32, p]),
+        "tbik_rope_table": (i32, [f64, i32, i32, p, p]),
+        "tbik_swiglu": (i32, [p, p, p, i32, i32, i64, i64, i64, p]),
+        "tbik_logsoftmax_workspace_bytes": (sz, [i32, i32, i32]),
+        "tbik_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p, sz, p]),
+        "tbik_softmax_causal": (i32, [p, i64, i64, p, i64, i64, i32, i32, i32, i32, f32, p]),
+        "tbik_primitive": (i32, [i32, p, p, i64, p]),
+    }
+
+
+def lib():
+    """Load libtbik.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            raise RuntimeError("libtbik.so is not built (%s); run __graft_entry__.build()"
+                               % _build.LIB)
+        L = C.CDLL(_build.LIB)
+        for name, (res, args) in _sigs().items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensor must be on a HIP device")
+
+
+def _chk(rc, what):
+    if rc != 0:
+        raise TbikError(rc, what)
+
+
+def _ld(t):
+    """Row stride (elements) of a 2-D tensor with unit column stride."""
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with contiguous rows")
+    return t.stride(0)
+
+
+def _bits(t):
+    if t.dtype != torch.bfloat16:
+        raise ValueError("expected bfloat16")
+    return t
+
+
+# --- info -------------------------------------------------------------------
+
+def tbik_version():
+    return lib().tbik_version()
+
+
+def tbik_strerror(code):
+    return _strerror(code)
+
+
+def tbik_tree_groups(n):
+    return lib().tbik_tree_groups(n)
+
+
+# --- GEMM ---------------------------------------------------------------------
+
+def tbik_gemm(A, W, leaf_mode=LEAF_MFMA, out=None, out_bf16=None, want_fp32=True,
+              want_bf16=False):
+    """C = A @ W^T with the tree over 64-wide K blocks.  A [M,K], W [N,K] bf16.
+    Returns (C fp32 or None, C_bf16 or None)."""
+    _bits(A); _bits(W); _need_gpu(A, W)
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("K mismatch")
+    if out is None and want_fp32:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if out_bf16 is None and want_bf16:
+        out_bf16 = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    ref = out if out is not None else out_bf16
+    ldc = _ld(ref) if ref is not None else N
+    if out is not None and out_bf16 is not None and _ld(out_bf16) != ldc:
+        raise ValueError("C and C_bf16 must share the row stride")
+    rc = lib().tbik_gemm(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(out), ldc, _ptr(out_bf16),
+                         M, N, K, leaf_mode, _stream())
+    _chk(rc, "tbik_gemm")
+    return out, out_bf16
+
+
+def tbik_gemm_strided_batched(A, W, leaf_mode=LEAF_MFMA, want_fp32=True, want_bf16=False):
+    """A [B,M,K], W [B,N,K] bf16 (contiguous rows) -> (C [B,M,N] fp32, C_bf16)."""
+    _bits(A); _bits(W); _need_gpu(A, W)
+    B, M, K = A.shape
+    N = W.shape[1]
+    if A.stride(2) != 1 or W.stride(2) != 1:
+        raise ValueError("rows must be contiguous")
+    out = torch.empty((B, M, N), dtype=torch.float32, device=A.device) if want_fp32 else None
+    outb = torch.empty((B, M, N), dtype=torch.bfloat16, device=A.device) if want_bf16 else None
+    rc = lib().tbik_gemm_strided_batched(_ptr(A), A.stride(1), A.stride(0), _ptr(W), W.stride(1),
+                                         W.stride(0), _ptr(out), N, M * N, _ptr(outb), M, N, K, B,
+                                         leaf_mode, _stream())
+    _chk(rc, "tbik_gemm_strided_batched")
+    return out, outb
+
+
+def tbik_gemm_tpsim_workspace_bytes(M, N, K, tp):
+    return lib().tbik_gemm_tpsim_workspace_bytes(M, N, K, tp)
+
+
+def tbik_gemm_tpsim(A, W, tp, leaf_mode=LEAF_MFMA, ws=None, out=None, out_bf16=None,
+                    want_bf16=False):
+    """Simulated K-sharded GEMM.  Returns (C fp32, C_bf16 or None, ws [tp,M,N])."""
+    _bits(A); _bits(W); _need_gpu(A, W)
+    M, K = A.shape
+    N = W.shape[0]
+    if ws is None:
+        ws = torch.empty((tp, M, N), dtype=torch.float32, device=A.device)
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if out_bf16 is None and want_bf16:
+        out_bf16 = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    rc = lib().tbik_gemm_tpsim(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(out), _ld(out),
+                               _ptr(out_bf16), M, N, K, tp, leaf_mode, _ptr(ws),
+                               ws.numel() * ws.element_size(), _stream())
+    _chk(rc, "tbik_gemm_tpsim")
+    return out, out_bf16, ws
+
+
+def tbik_tree_combine(ws, out=None, out_bf16=None):
+    """ws [tp,M,N] fp32 partials -> top tree -> C [M,N]."""
+    _need_gpu(ws)
+    tp, M, N = ws.shape
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=ws.device)
+    rc = lib().tbik_tree_combine(_ptr(ws), tp, _ptr(out), _ld(out), _ptr(out_bf16), M, N,
+                                 _stream())
+    _chk(rc, "tbik_tree_combine")
+    return out
+
+
+# --- row ops ------------------------------------------------------------------
+
+def tbik_rmsnorm_residual(x, r, w, eps=1e-6, y=None, r_out=None, want_r_out=True):
+    _bits(x); _bits(r); _bits(w); _need_gpu(x, r, w)
+    rows, H = x.shape
+    ld = _ld(x)
+    if _ld(r) != ld:
+        raise ValueError("x and r must share the row stride")
+    if y is None:
+        y = torch.empty_like(x)
+    if r_out is None and want_r_out:
+        r_out = torch.empty_like(x)
+    rc = lib().tbik_rmsnorm_residual(_ptr(x), _ptr(r), _ptr(w), _ptr(y), _ptr(r_out), rows, H, ld,
+                                     float(eps), _stream())
+    _chk(rc, "tbik_rmsnorm_residual")
+    return y, r_out
+
+
+def tbik_rope(x, pos, cos_tab, sin_tab, y=None):
+    """x [T, heads, d] bf16 (heads contiguous); pos [T] int32; tables [max_pos, d/2]."""
+    _bits(x); _need_gpu(x, pos, cos_tab, sin_tab)
+    T, heads, d = x.shape
+    if x.stride(2) != 1 or x.stride(1) != d:
+        raise ValueError("heads must be contiguous with stride head_dim")
+    if y is None:
+        y = torch.empty_like(x)
+    rc = lib().tbik_rope(_ptr(x), _ptr(y), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T, heads, d,
+                         x.stride(0), cos_tab.shape[0], _stream())
+    _chk(rc, "tbik_rope")
+    return y
+
+
+def tbik_rope_table(theta, head_dim, max_pos):
+    """Host helper: (cos, sin) CPU float32 tensors [max_pos, head_dim/2]."""
+    half = head_dim // 2
+    c = torch.empty((max_pos, half), dtype=torch.float32)
+    s = torch.empty((max_pos, half), dtype=torch.float32)
+    rc = lib().tbik_rope_table(float(theta), head_dim, max_pos, _ptr(c), _ptr(s))
+    _chk(rc, "tbik_rope_table")
+    return c, s
+
+
+def tbik_swiglu(gate, up, out=None):
+    _bits(gate); _bits(up); _need_gpu(gate, up)
+    rows, cols = gate.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.bfloat16, device=gate.device)
+    rc = lib().tbik_swiglu(_ptr(gate), _ptr(up), _ptr(out), rows, cols, _ld(gate), _ld(up),
+                           _ld(out), _stream())
+    _chk(rc, "tbik_swiglu")
+    return out
+
+
+def tbik_logsoftmax_workspace_bytes(M, V, tp):
+    return lib().tbik_logsoftmax_workspace_bytes(M, V, tp)
+
+
+def tbik_logsoftmax_gather(logits, targets, tp=1, ws=None, out=None):
+    """logits [M,V] fp32, targets [M] int32 -> (lp [M] fp32, ws)."""
+    _need_gpu(logits, targets)
+    M, V = logits.shape
+    nbytes = tbik_logsoftmax_workspace_bytes(M, V, tp)
+    if ws is None:
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=logits.device)
+    if out is None:
+        out = torch.empty((M,), dtype=torch.float32, device=logits.device)
+    rc = lib().tbik_logsoftmax_gather(_ptr(logits), _ld(logits), _ptr(targets), _ptr(out), M, V,
+                                      tp, _ptr(ws), ws.numel() * 4, _stream())
+    _chk(rc, "tbik_logsoftmax_gather")
+    return out, ws
+
+
+def logsoftmax_shard_nodes(ws, M, tp):
+    """View of the per-row shard partial sums inside a log-softmax workspace."""
+    return ws[M * 16: M * 16 + M * tp].view(M, tp)
+
+
+def tbik_softmax_causal(S, offset, scale, P=None):
+    """S [B, Lq, Lk] fp32 -> P [B, Lq, Lk] bf16."""
+    _need_gpu(S)
+    B, Lq, Lk = S.shape
+    if S.stride(2) != 1:
+        raise ValueError("rows must be contiguous")
+    if P is None:
+        P = torch.empty((B, Lq, Lk), dtype=torch.bfloat16, device=S.device)
+    rc = lib().tbik_softmax_causal(_ptr(S), S.stride(1), S.stride(0), _ptr(P), P.stride(1),
+                                   P.stride(0), Lq, Lk, B, offset, float(scale), _stream())
+    _chk(rc, "tbik_softmax_causal")
+    return P
+
+
+def tbik_primitive(op, x, y=None):
+    _need_gpu(x)
+    if y is None:
+        y = torch.empty_like(x)
+    rc = lib().tbik_primitive(op, _ptr(x), _ptr(y), x.numel(), _stream())
+    _chk(rc, "tbik_primitive")
+    return y

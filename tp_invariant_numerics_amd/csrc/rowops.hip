@@ -1,0 +1,518 @@
+// rowops.hip -- TP-invariant row reductions and fp32-intermediate nodes.
+//
+//  * residual-add + RMSNorm, RoPE, SwiGLU: fp32 intermediates, one bf16
+//    rounding at the output (rounding-alignment article, "three nodes").
+//  * log-softmax + target gather and the causal softmax: the row sum
+//    follows the library's tree (TBIK summary page, Abstract: TP-invariant
+//    reduction primitives); the vocab groups of the tree are the shards of
+//    a vocab-parallel layout.
+//
+// Row trees are evaluated in three stages that reproduce the same PAIR
+// structure: (1) each thread reduces an aligned chunk of CH = 2^c leaves
+// (2^c divides the group size, so PAIR's first c levels are perfect trees
+// over exactly these chunks); (2) PAIR's remaining levels run level by level
+// in LDS (ping-pong buffers, one barrier per level, odd last element carried);
+// (3) the perfect tree over the T group sums.  No atomics.
+#include "tbik_device.h"
+#include "tbik_internal.h"
+#include "../../include/tbik.h"
+
+namespace tbik {
+
+static int check_launch() {
+  return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH;
+}
+
+template <int CH>
+__device__ __forceinline__ float chunk_tree(float (&v)[CH]) {
+#pragma unroll
+  for (int w = CH; w > 1; w >>= 1) {
+#pragma unroll
+    for (int q = 0; q < w / 2; ++q) v[q] = v[2 * q] + v[2 * q + 1];
+  }
+  return v[0];
+}
+
+// PAIR levels over `groups` independent groups of m values each, stored
+// compactly (group g at src[g*m .. g*m+m)).  Leaves each group's PAIR value
+// at src'[g] (returned pointer).  Must be called by all threads of the block.
+template <int NT>
+__device__ __forceinline__ float *lds_pair(float *src, float *dst, int m, int groups) {
+  while (m > 1) {
+    const int half = m >> 1;
+    const int nm = half + (m & 1);
+    for (int idx = threadIdx.x; idx < groups * nm; idx += NT) {
+      const int g = idx / nm;
+      const int i = idx - g * nm;
+      const float *sg = src + g * m;
+      dst[idx] = (i < half) ? sg[2 * i] + sg[2 * i + 1] : sg[m - 1];
+    }
+    __syncthreads();
+    float *t = src; src = dst; dst = t;
+    m = nm;
+  }
+  return src;
+}
+
+// Root of the row tree given nch = T*gc chunk values in buf_a (visible to
+// all threads).  buf_b is scratch of the same size.
+template <int NT>
+__device__ __forceinline__ float lds_row_tree(float *buf_a, float *buf_b, int gc, int T) {
+  float *g = lds_pair<NT>(buf_a, buf_b, gc, T);
+  float *other = (g == buf_a) ? buf_b : buf_a;
+  float *root = lds_pair<NT>(g, other, T, 1);
+  return root[0];
+}
+
+// ---- bf16 chunk loads -------------------------------------------------------
+template <int CH>
+__device__ __forceinline__ void load_bf16(float (&v)[CH], const uint16_t *p) {
+  if constexpr (CH >= 8) {
+#pragma unroll
+    for (int q = 0; q < CH / 8; ++q) {
+      u32x4 u = *reinterpret_cast<const u32x4 *>(p + 8 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[8 * q + 2 * e] = __uint_as_float(u[e] << 16);
+        v[8 * q + 2 * e + 1] = __uint_as_float(u[e] & 0xffff0000u);
+      }
+    }
+  } else if constexpr (CH == 4) {
+    u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+    v[0] = __uint_as_float(u[0] << 16); v[1] = __uint_as_float(u[0] & 0xffff0000u);
+    v[2] = __uint_as_float(u[1] << 16); v[3] = __uint_as_float(u[1] & 0xffff0000u);
+  } else {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) v[e] = bf2f(p[e]);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[CH]) {
+  if constexpr (CH >= 8) {
+#pragma unroll
+    for (int q = 0; q < CH / 8; ++q) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        u[e] = (uint32_t)f2bf(v[8 * q + 2 * e]) | ((uint32_t)f2bf(v[8 * q + 2 * e + 1]) << 16);
+      *reinterpret_cast<u32x4 *>(p + 8 * q) = u;
+    }
+  } else if constexpr (CH == 4) {
+    u32x2 u;
+    u[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+    u[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    *reinterpret_cast<u32x2 *>(p) = u;
+  } else {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) p[e] = f2bf(v[e]);
+  }
+}
+
+template <int CH>
+__device__ __forceinline__ void load_f32(float (&v)[CH], const float *p) {
+  if constexpr (CH >= 4) {
+#pragma unroll
+    for (int q = 0; q < CH / 4; ++q) {
+      f32x4 u = *reinterpret_cast<const f32x4 *>(p + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * q + e] = u[e];
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) v[e] = p[e];
+  }
+}
+
+// Largest power of two <= 16 dividing G.
+static int chunk_for(int64_t G) {
+  int ch = 16;
+  while (ch > 1 && (G % ch) != 0) ch >>= 1;
+  return ch;
+}
+
+// =============================================================================
+// residual-add + RMSNorm: one workgroup per row.
+// =============================================================================
+constexpr int kRowThreads = 256;
+
+template <int CH>
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, uint16_t *r_out,
+          int H, int64_t ld, float eps, int T) {
+  extern __shared__ float lds[];
+  const int nch = H / CH;
+  const int gc = nch / T;
+  const int64_t base = (int64_t)blockIdx.x * ld;
+  const uint16_t *xr = x + base;
+  const uint16_t *rr = r + base;
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float a[CH], b[CH], sq[CH];
+    load_bf16<CH>(a, xr + ch * CH);
+    load_bf16<CH>(b, rr + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      a[e] = a[e] + b[e];          // h
+      sq[e] = a[e] * a[e];
+    }
+    if (r_out) store_bf16<CH>(r_out + base + ch * CH, a);
+    lds[ch] = chunk_tree<CH>(sq);
+  }
+  __syncthreads();
+  const float ss = lds_row_tree<kRowThreads>(lds, lds + nch, gc, T);
+  const float mean = ss / (float)H;
+  const float rstd = 1.0f / __builtin_sqrtf(mean + eps);
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float a[CH], b[CH], ww[CH];
+    load_bf16<CH>(a, xr + ch * CH);
+    load_bf16<CH>(b, rr + ch * CH);
+    load_bf16<CH>(ww, w + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) a[e] = ((a[e] + b[e]) * rstd) * ww[e];
+    store_bf16<CH>(y + base + ch * CH, a);
+  }
+}
+
+int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+                            uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
+                            float eps, hipStream_t s) {
+  const int T = tree_T(H);
+  const int ch = chunk_for(H / T);
+  const int nch = H / ch;
+  if (nch > 8192) return TBIK_ERR_SHAPE;
+  const size_t lds = 2 * (size_t)nch * sizeof(float);
+  dim3 grid((unsigned)rows), block(kRowThreads);
+  switch (ch) {
+    case 16: hipLaunchKernelGGL(k_rmsnorm<16>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 8: hipLaunchKernelGGL(k_rmsnorm<8>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 4: hipLaunchKernelGGL(k_rmsnorm<4>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 2: hipLaunchKernelGGL(k_rmsnorm<2>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    default: hipLaunchKernelGGL(k_rmsnorm<1>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+  }
+  return check_launch();
+}
+
+// =============================================================================
+// RoPE (rotate-half).  One thread = 4 consecutive pairs (i..i+3, i+h..i+h+3).
+// =============================================================================
+__global__ void __launch_bounds__(256)
+k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
+       const float *sin_tab, int T, int heads, int half, int64_t ld_token, int max_pos) {
+  const int q4 = half / 4;                       // 4-pair items per head
+  const int64_t total = (int64_t)T * heads * q4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += stride) {
+    const int64_t th = it / q4;
+    const int i = (int)(it - th * q4) * 4;
+    const int t = (int)(th / heads);
+    const int hd = (int)(th - (int64_t)t * heads);
+    int p = pos[t];
+    p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+    const int64_t off = (int64_t)t * ld_token + (int64_t)hd * 2 * half + i;
+    const u32x2 ua = *reinterpret_cast<const u32x2 *>(x + off);
+    const u32x2 ub = *reinterpret_cast<const u32x2 *>(x + off + half);
+    const f32x4 c = *reinterpret_cast<const f32x4 *>(cos_tab + (int64_t)p * half + i);
+    const f32x4 sn = *reinterpret_cast<const f32x4 *>(sin_tab + (int64_t)p * half + i);
+    float a[4] = {__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
+                  __uint_as_float(ua[1] << 16), __uint_as_float(ua[1] & 0xffff0000u)};
+    float b[4] = {__uint_as_float(ub[0] << 16), __uint_as_float(ub[0] & 0xffff0000u),
+                  __uint_as_float(ub[1] << 16), __uint_as_float(ub[1] & 0xffff0000u)};
+    uint16_t ya[4], yb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float ac = a[e] * c[e], bs = b[e] * sn[e];
+      const float bc = b[e] * c[e], as = a[e] * sn[e];
+      ya[e] = f2bf(ac - bs);
+      yb[e] = f2bf(bc + as);
+    }
+    u32x2 oa, ob;
+    oa[0] = (uint32_t)ya[0] | ((uint32_t)ya[1] << 16);
+    oa[1] = (uint32_t)ya[2] | ((uint32_t)ya[3] << 16);
+    ob[0] = (uint32_t)yb[0] | ((uint32_t)yb[1] << 16);
+    ob[1] = (uint32_t)yb[2] | ((uint32_t)yb[3] << 16);
+    *reinterpret_cast<u32x2 *>(y + off) = oa;
+    *reinterpret_cast<u32x2 *>(y + off + half) = ob;
+  }
+}
+
+int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
+                const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+                int max_pos, hipStream_t s) {
+  const int half = head_dim / 2;
+  const int64_t total = (int64_t)T * heads * (half / 4);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 262144) blocks = 262144;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_rope, dim3((unsigned)blocks), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab,
+                     T, heads, half, ld_token, max_pos);
+  return check_launch();
+}
+
+// =============================================================================
+// SwiGLU: out = bf16((g / (1 + EXP(-g))) * u).  8 elements per item.
+// =============================================================================
+__device__ __forceinline__ float swiglu1(float g, float u) {
+  const float den = 1.0f + exp_f32(-g);
+  const float silu = g / den;
+  return silu * u;
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+k_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols, int64_t ldg,
+         int64_t ldu, int64_t ldo) {
+  const int per = VEC ? 8 : 1;
+  const int items = cols / per;
+  const int64_t total = (int64_t)rows * items;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += stride) {
+    const int64_t row = it / items;
+    const int col = (int)(it - row * items) * per;
+    if constexpr (VEC) {
+      float gv[8], uv[8];
+      load_bf16<8>(gv, g + row * ldg + col);
+      load_bf16<8>(uv, u + row * ldu + col);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) gv[e] = swiglu1(gv[e], uv[e]);
+      store_bf16<8>(o + row * ldo + col, gv);
+    } else {
+      o[row * ldo + col] = f2bf(swiglu1(bf2f(g[row * ldg + col]), bf2f(u[row * ldu + col])));
+    }
+  }
+}
+
+int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
+                  int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s) {
+  const bool vec = (cols % 8) == 0;
+  const int64_t total = (int64_t)rows * (vec ? cols / 8 : cols);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 262144) blocks = 262144;
+  if (blocks < 1) blocks = 1;
+  if (vec)
+    hipLaunchKernelGGL(k_swiglu<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+  else
+    hipLaunchKernelGGL(k_swiglu<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+  return check_launch();
+}
+
+// =============================================================================
+// log-softmax + gather.
+//  pass 1: k_group_max    -> gmax[M][T]  (exact maxima; order-free)
+//  pass 2: k_group_sumexp -> gsum[M][T]  (EXP(x - m), PAIR inside the group)
+//  pass 3: k_lsm_finish   -> shard nodes [M][tp], perfect tree, LOG, gather
+// =============================================================================
+constexpr int kLsmThreads = 256;
+
+template <int CH>
+__global__ void __launch_bounds__(kLsmThreads)
+k_group_max(const float *logits, int64_t ld, int V, int T, float *gmax) {
+  __shared__ float red[kLsmThreads / 64];
+  const int row = blockIdx.y, g = blockIdx.x;
+  const int G = V / T;
+  const float *xg = logits + (int64_t)row * ld + (int64_t)g * G;
+  float m = -__builtin_inff();
+  for (int ch = threadIdx.x; ch < G / CH; ch += kLsmThreads) {
+    float v[CH];
+    load_f32<CH>(v, xg + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) m = __builtin_fmaxf(m, v[e]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+#pragma unroll
+    for (int q = 1; q < kLsmThreads / 64; ++q) r = __builtin_fmaxf(r, red[q]);
+    gmax[(int64_t)row * 8 + g] = r;
+  }
+}
+
+template <int CH>
+__global__ void __launch_bounds__(kLsmThreads)
+k_group_sumexp(const float *logits, int64_t ld, int V, int T, const float *gmax, float *gsum) {
+  extern __shared__ float lds[];
+  const int row = blockIdx.y, g = blockIdx.x;
+  const int G = V / T;
+  const int gc = G / CH;
+  float m = gmax[(int64_t)row * 8];
+  for (int q = 1; q < T; ++q) m = __builtin_fmaxf(m, gmax[(int64_t)row * 8 + q]);
+  const float *xg = logits + (int64_t)row * ld + (int64_t)g * G;
+  for (int ch = threadIdx.x; ch < gc; ch += kLsmThreads) {
+    float v[CH];
+    load_f32<CH>(v, xg + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) v[e] = exp_f32(v[e] - m);
+    lds[ch] = chunk_tree<CH>(v);
+  }
+  __syncthreads();
+  float *res = lds_pair<kLsmThreads>(lds, lds + gc, gc, 1);
+  if (threadIdx.x == 0) gsum[(int64_t)row * 8 + g] = res[0];
+}
+
+__global__ void __launch_bounds__(256)
+k_lsm_finish(const float *logits, int64_t ld, const int32_t *targets, int M, int V, int T, int tp,
+             const float *gmax, const float *gsum, float *shard, float *out) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= M) return;
+  float m = gmax[(int64_t)row * 8];
+  for (int q = 1; q < T; ++q) m = __builtin_fmaxf(m, gmax[(int64_t)row * 8 + q]);
+  float v[8];
+  for (int q = 0; q < 8; ++q) v[q] = (q < T) ? gsum[(int64_t)row * 8 + q] : 0.0f;
+  // shard nodes: perfect tree over each shard's T/tp groups
+  const int per = T / tp;
+  float nodes[8];
+  for (int t = 0; t < 8; ++t) {
+    if (t >= tp) break;
+    float u[8];
+    for (int q = 0; q < 8; ++q) u[q] = (q < per) ? v[t * per + q] : 0.0f;
+    for (int w = per; w > 1; w >>= 1)
+      for (int q = 0; q < w / 2; ++q) u[q] = u[2 * q] + u[2 * q + 1];
+    nodes[t] = u[0];
+    shard[(int64_t)row * tp + t] = u[0];
+  }
+  for (int w = tp; w > 1; w >>= 1)
+    for (int q = 0; q < w / 2; ++q) nodes[q] = nodes[2 * q] + nodes[2 * q + 1];
+  const float ssum = nodes[0];
+  const int tgt = targets[row];
+  if (tgt < 0 || tgt >= V) {
+    out[row] = __builtin_nanf("");
+    return;
+  }
+  out[row] = (logits[(int64_t)row * ld + tgt] - m) - log_f32(ssum);
+}
+
+int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out, int M,
+                      int V, int tp, float *ws, hipStream_t s) {
+  const int T = tree_T(V);
+  const int G = V / T;
+  const int ch = chunk_for(G);
+  const int gc = G / ch;
+  if (gc > 8192) return TBIK_ERR_SHAPE;
+  float *gmax = ws;
+  float *gsum = ws + (size_t)M * 8;
+  float *shard = ws + (size_t)M * 16;
+  dim3 grid((unsigned)T, (unsigned)M), block(kLsmThreads);
+  const size_t lds = 2 * (size_t)gc * sizeof(float);
+  switch (ch) {
+    case 16:
+      hipLaunchKernelGGL(k_group_max<16>, grid, block, 0, s, logits, ld, V, T, gmax);
+      hipLaunchKernelGGL(k_group_sumexp<16>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
+      break;
+    case 8:
+      hipLaunchKernelGGL(k_group_max<8>, grid, block, 0, s, logits, ld, V, T, gmax);
+      hipLaunchKernelGGL(k_group_sumexp<8>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
+      break;
+    case 4:
+      hipLaunchKernelGGL(k_group_max<4>, grid, block, 0, s, logits, ld, V, T, gmax);
+      hipLaunchKernelGGL(k_group_sumexp<4>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
+      break;
+    case 2:
+      hipLaunchKernelGGL(k_group_max<2>, grid, block, 0, s, logits, ld, V, T, gmax);
+      hipLaunchKernelGGL(k_group_sumexp<2>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
+      break;
+    default:
+      hipLaunchKernelGGL(k_group_max<1>, grid, block, 0, s, logits, ld, V, T, gmax);
+      hipLaunchKernelGGL(k_group_sumexp<1>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
+      break;
+  }
+  hipLaunchKernelGGL(k_lsm_finish, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, logits, ld,
+                     targets, M, V, T, tp, gmax, gsum, shard, out);
+  return check_launch();
+}
+
+// =============================================================================
+// causal softmax: one workgroup per (batch, query row).
+// =============================================================================
+template <int CH>
+__global__ void __launch_bounds__(kRowThreads)
+k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, int64_t ld_p,
+                 int64_t stride_p, int Lq, int Lk, int offset, float scale, int T) {
+  extern __shared__ float lds[];
+  __shared__ float red[kRowThreads / 64];
+  const int i = blockIdx.x, b = blockIdx.y;
+  const float *srow = S + (int64_t)b * stride_s + (int64_t)i * ld_s;
+  uint16_t *prow = P + (int64_t)b * stride_p + (int64_t)i * ld_p;
+  const int last = i + offset;
+  const int nch = Lk / CH;
+  const int gc = nch / T;
+  float m = -__builtin_inff();
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float v[CH];
+    load_f32<CH>(v, srow + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const float z = v[e] * scale;
+      if (ch * CH + e <= last) m = __builtin_fmaxf(m, z);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int q = 1; q < kRowThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float v[CH];
+    load_f32<CH>(v, srow + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) v[e] = (ch * CH + e <= last) ? exp_f32(v[e] * scale - m) : 0.0f;
+    lds[ch] = chunk_tree<CH>(v);
+  }
+  __syncthreads();
+  const float ssum = lds_row_tree<kRowThreads>(lds, lds + nch, gc, T);
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float v[CH];
+    load_f32<CH>(v, srow + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e)
+      v[e] = (ch * CH + e <= last) ? exp_f32(v[e] * scale - m) / ssum : 0.0f;
+    store_bf16<CH>(prow + ch * CH, v);
+  }
+}
+
+int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P,
+                          int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
+                          float scale, hipStream_t s) {
+  const int T = tree_T(Lk);
+  int ch = chunk_for(Lk / T);
+  if (ch > 8) ch = 8;       // keep bf16 stores 16-byte aligned or scalar
+  const int nch = Lk / ch;
+  if (nch > 8192) return TBIK_ERR_SHAPE;
+  const size_t lds = 2 * (size_t)nch * sizeof(float);
+  dim3 grid((unsigned)Lq, (unsigned)batch), block(kRowThreads);
+  switch (ch) {
+    case 8: hipLaunchKernelGGL(k_softmax_causal<8>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
+    case 4: hipLaunchKernelGGL(k_softmax_causal<4>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
+    case 2: hipLaunchKernelGGL(k_softmax_causal<2>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
+    default: hipLaunchKernelGGL(k_softmax_causal<1>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
+  }
+  return check_launch();
+}
+
+// =============================================================================
+// primitives, elementwise
+// =============================================================================
+__global__ void __launch_bounds__(256) k_primitive(int op, const float *x, float *y, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const float v = x[i];
+    float r;
+    if (op == TBIK_PRIM_EXP) r = exp_f32(v);
+    else if (op == TBIK_PRIM_LOG) r = log_f32(v);
+    else r = bf2f(f2bf(v));
+    y[i] = r;
+  }
+}
+
+int launch_primitive(int op, const float *x, float *y, int64_t n, hipStream_t s) {
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 262144) blocks = 262144;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_primitive, dim3((unsigned)blocks), dim3(256), 0, s, op, x, y, n);
+  return check_launch();
+}
+
+}  // namespace tbik

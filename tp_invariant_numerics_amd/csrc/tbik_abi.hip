@@ -1,0 +1,226 @@
+// tbik_abi.hip -- the extern "C" entry points of libtbik.so.
+//
+// Host-side validation happens before any HIP call; an invalid call
+// launches nothing and returns a TBIK_ERR_* code.  No entry point allocates
+// memory or keeps state between calls.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/tbik.h"
+#include "tbik_device.h"
+#include "tbik_internal.h"
+
+using tbik::GemmCall;
+
+namespace {
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool ld_ok(int64_t ld) { return ld > 0 && (ld % 8) == 0; }
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+bool tp_ok(int tp) { return tp == 1 || tp == 2 || tp == 4 || tp == 8; }
+
+// Common checks of a GEMM call (both modes).
+int check_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, const float *C,
+               int64_t ldc, const tbik_bf16 *Cb, int M, int N, int K, int leaf_mode) {
+  if (!A || !W || (!C && !Cb)) return TBIK_ERR_NULL;
+  if (M < 0 || N < 0 || K <= 0 || (K % 64) != 0) return TBIK_ERR_SHAPE;
+  if (lda < K || ldw < K || ldc < N) return TBIK_ERR_SHAPE;
+  if (!ld_ok(lda) || !ld_ok(ldw) || !ld_ok(ldc)) return TBIK_ERR_ALIGN;
+  if (!aligned16(A) || !aligned16(W) || (C && !aligned16(C)) || (Cb && !aligned16(Cb)))
+    return TBIK_ERR_ALIGN;
+  if (leaf_mode != TBIK_LEAF_MFMA && leaf_mode != TBIK_LEAF_SCALAR) return TBIK_ERR_ARG;
+  const int nb = K / 64;
+  if (nb / tbik::tree_T(nb) > tbik::kMaxGroupLeaves) return TBIK_ERR_SHAPE;
+  return TBIK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tbik_version(void) { return 1 * 10000 + 0 * 100 + 0; }
+
+const char *tbik_strerror(int code) {
+  switch (code) {
+    case TBIK_OK: return "ok";
+    case TBIK_ERR_NULL: return "a required pointer is NULL";
+    case TBIK_ERR_SHAPE: return "invalid shape (negative size, K not a positive multiple of 64, "
+                                "leading dimension too small, or size beyond the supported range)";
+    case TBIK_ERR_TP: return "tp must be 1, 2, 4 or 8 and divide the tree's group count T";
+    case TBIK_ERR_ALIGN: return "pointers must be 16-byte aligned and leading dimensions multiples of 8";
+    case TBIK_ERR_WORKSPACE: return "workspace missing or too small";
+    case TBIK_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case TBIK_ERR_ARG: return "argument out of range";
+  }
+  return "unknown error code";
+}
+
+int tbik_tree_groups(int64_t n) { return n <= 0 ? 0 : tbik::tree_T(n); }
+
+int tbik_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, float *C,
+              int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int leaf_mode, void *stream) {
+  return tbik_gemm_strided_batched(A, lda, 0, W, ldw, 0, C, ldc, 0, C_bf16, M, N, K, 1, leaf_mode,
+                                   stream);
+}
+
+int tbik_gemm_strided_batched(const tbik_bf16 *A, int64_t lda, int64_t strideA,
+                              const tbik_bf16 *W, int64_t ldw, int64_t strideW, float *C,
+                              int64_t ldc, int64_t strideC, tbik_bf16 *C_bf16, int M, int N,
+                              int K, int batch, int leaf_mode, void *stream) {
+  int rc = check_gemm(A, lda, W, ldw, C, ldc, C_bf16, M, N, K, leaf_mode);
+  if (rc) return rc;
+  if (batch < 0 || batch > 65535) return TBIK_ERR_SHAPE;
+  if (strideA < 0 || strideW < 0 || strideC < 0) return TBIK_ERR_SHAPE;
+  if ((strideA % 8) || (strideW % 8) || (strideC % 8)) return TBIK_ERR_ALIGN;
+  if (M == 0 || N == 0 || batch == 0) return TBIK_OK;
+  GemmCall c{};
+  c.A = A; c.lda = lda; c.strideA = strideA;
+  c.W = W; c.ldw = ldw; c.strideW = strideW;
+  c.C = C; c.Cb = C_bf16; c.ldc = ldc; c.strideC = strideC; c.part_stride = 0;
+  c.M = M; c.N = N; c.K = K; c.batch = batch; c.parts = 1; c.leaf_mode = leaf_mode;
+  return tbik::launch_gemm(c, as_stream(stream));
+}
+
+size_t tbik_gemm_tpsim_workspace_bytes(int M, int N, int K, int tp) {
+  if (M < 0 || N < 0 || tp < 1) return 0;
+  (void)K;
+  return (size_t)tp * (size_t)M * (size_t)N * sizeof(float);
+}
+
+int tbik_gemm_tpsim(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, float *C,
+                    int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int tp, int leaf_mode,
+                    float *ws, size_t ws_bytes, void *stream) {
+  int rc = check_gemm(A, lda, W, ldw, C, ldc, C_bf16, M, N, K, leaf_mode);
+  if (rc) return rc;
+  const int T = tbik::tree_T(K / 64);
+  if (!tp_ok(tp) || (T % tp) != 0) return TBIK_ERR_TP;
+  if (M == 0 || N == 0) return TBIK_OK;
+  if (!ws) return TBIK_ERR_WORKSPACE;
+  if (ws_bytes < tbik_gemm_tpsim_workspace_bytes(M, N, K, tp)) return TBIK_ERR_WORKSPACE;
+  if (!aligned16(ws)) return TBIK_ERR_ALIGN;
+  GemmCall c{};
+  c.A = A; c.lda = lda; c.strideA = 0;
+  c.W = W; c.ldw = ldw; c.strideW = 0;
+  c.C = ws; c.Cb = nullptr; c.ldc = N; c.strideC = 0; c.part_stride = (int64_t)M * N;
+  c.M = M; c.N = N; c.K = K; c.batch = 1; c.parts = tp; c.leaf_mode = leaf_mode;
+  rc = tbik::launch_gemm(c, as_stream(stream));
+  if (rc) return rc;
+  return tbik::launch_tree_combine(ws, tp, C, ldc, C_bf16, M, N, as_stream(stream));
+}
+
+int tbik_tree_combine(const float *ws, int tp, float *C, int64_t ldc, tbik_bf16 *C_bf16, int M,
+                      int N, void *stream) {
+  if (!ws || (!C && !C_bf16)) return TBIK_ERR_NULL;
+  if (!tp_ok(tp)) return TBIK_ERR_TP;
+  if (M < 0 || N < 0 || ldc < N) return TBIK_ERR_SHAPE;
+  if (!ld_ok(ldc)) return TBIK_ERR_ALIGN;
+  if (!aligned16(ws) || (C && !aligned16(C)) || (C_bf16 && !aligned16(C_bf16)))
+    return TBIK_ERR_ALIGN;
+  if (M == 0 || N == 0) return TBIK_OK;
+  return tbik::launch_tree_combine(ws, tp, C, ldc, C_bf16, M, N, as_stream(stream));
+}
+
+int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
+                          tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld, float eps,
+                          void *stream) {
+  if (!x || !r || !w || !y) return TBIK_ERR_NULL;
+  if (rows < 0 || H < 1 || H > 65536 || ld < H) return TBIK_ERR_SHAPE;
+  if (!(eps >= 0.0f) || isinf(eps)) return TBIK_ERR_ARG;
+  if (!ld_ok(ld)) return TBIK_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(r) || !aligned16(w) || !aligned16(y) ||
+      (r_out && !aligned16(r_out)))
+    return TBIK_ERR_ALIGN;
+  if (rows == 0) return TBIK_OK;
+  return tbik::launch_rmsnorm_residual(x, r, w, y, r_out, rows, H, ld, eps, as_stream(stream));
+}
+
+int tbik_rope(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float *cos_tab,
+              const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+              int max_pos, void *stream) {
+  if (!x || !y || !pos || !cos_tab || !sin_tab) return TBIK_ERR_NULL;
+  if (T < 0 || heads < 1 || max_pos < 1) return TBIK_ERR_SHAPE;
+  if (head_dim < 2 || head_dim > 1024 || (head_dim % 8) != 0) return TBIK_ERR_SHAPE;
+  if (ld_token < (int64_t)heads * head_dim) return TBIK_ERR_SHAPE;
+  if (!ld_ok(ld_token)) return TBIK_ERR_ALIGN;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
+      ((uintptr_t)pos & 3u))
+    return TBIK_ERR_ALIGN;
+  if (T == 0) return TBIK_OK;
+  return tbik::launch_rope(x, y, pos, cos_tab, sin_tab, T, heads, head_dim, ld_token, max_pos,
+                           as_stream(stream));
+}
+
+int tbik_rope_table(double theta, int head_dim, int max_pos, float *cos_tab, float *sin_tab) {
+  if (!cos_tab || !sin_tab) return TBIK_ERR_NULL;
+  if (!(theta > 0.0) || head_dim < 2 || (head_dim % 2) || max_pos < 1) return TBIK_ERR_ARG;
+  const int half = head_dim / 2;
+  for (int i = 0; i < half; ++i) {
+    // theta^(-2i/d) in binary64, then the angle p * freq in binary64
+    const double freq = pow(theta, -(2.0 * i) / (double)head_dim);
+    for (int p = 0; p < max_pos; ++p) {
+      const double ang = (double)p * freq;
+      cos_tab[(int64_t)p * half + i] = (float)cos(ang);
+      sin_tab[(int64_t)p * half + i] = (float)sin(ang);
+    }
+  }
+  return TBIK_OK;
+}
+
+int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows, int cols,
+                int64_t ld_gate, int64_t ld_up, int64_t ld_out, void *stream) {
+  if (!gate || !up || !out) return TBIK_ERR_NULL;
+  if (rows < 0 || cols < 0 || ld_gate < cols || ld_up < cols || ld_out < cols)
+    return TBIK_ERR_SHAPE;
+  if (!ld_ok(ld_gate) || !ld_ok(ld_up) || !ld_ok(ld_out)) return TBIK_ERR_ALIGN;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(out)) return TBIK_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return TBIK_OK;
+  return tbik::launch_swiglu(gate, up, out, rows, cols, ld_gate, ld_up, ld_out,
+                             as_stream(stream));
+}
+
+size_t tbik_logsoftmax_workspace_bytes(int M, int V, int tp) {
+  (void)V;
+  if (M < 0 || tp < 1) return 0;
+  return (size_t)M * (16 + (size_t)tp) * sizeof(float);
+}
+
+int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targets, float *out_lp,
+                           int M, int V, int tp, float *ws, size_t ws_bytes, void *stream) {
+  if (!logits || !targets || !out_lp) return TBIK_ERR_NULL;
+  if (M < 0 || V < 1 || ld < V) return TBIK_ERR_SHAPE;
+  if (!tp_ok(tp) || (tbik::tree_T(V) % tp) != 0) return TBIK_ERR_TP;
+  if (!ld_ok(ld)) return TBIK_ERR_ALIGN;
+  if (!aligned16(logits) || ((uintptr_t)targets & 3u) || ((uintptr_t)out_lp & 3u))
+    return TBIK_ERR_ALIGN;
+  if (M == 0) return TBIK_OK;
+  if (M > 65535) return TBIK_ERR_SHAPE;
+  if (!ws || ws_bytes < tbik_logsoftmax_workspace_bytes(M, V, tp)) return TBIK_ERR_WORKSPACE;
+  if ((uintptr_t)ws & 3u) return TBIK_ERR_ALIGN;
+  return tbik::launch_logsoftmax(logits, ld, targets, out_lp, M, V, tp, ws, as_stream(stream));
+}
+
+int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf16 *P,
+                        int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
+                        float scale, void *stream) {
+  if (!S || !P) return TBIK_ERR_NULL;
+  if (Lq < 0 || Lk < 1 || Lk > 65536 || batch < 0 || batch > 65535 || offset < 0)
+    return TBIK_ERR_SHAPE;
+  if (ld_s < Lk || ld_p < Lk || stride_s < 0 || stride_p < 0) return TBIK_ERR_SHAPE;
+  if (!ld_ok(ld_s) || !ld_ok(ld_p) || (stride_s % 8) || (stride_p % 8)) return TBIK_ERR_ALIGN;
+  if (!aligned16(S) || !aligned16(P)) return TBIK_ERR_ALIGN;
+  if (!isfinite(scale)) return TBIK_ERR_ARG;
+  if (Lq == 0 || batch == 0) return TBIK_OK;
+  return tbik::launch_softmax_causal(S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, batch, offset,
+                                     scale, as_stream(stream));
+}
+
+int tbik_primitive(int op, const float *x, float *y, int64_t n, void *stream) {
+  if (!x || !y) return TBIK_ERR_NULL;
+  if (op < TBIK_PRIM_EXP || op > TBIK_PRIM_BF16) return TBIK_ERR_ARG;
+  if (n < 0) return TBIK_ERR_SHAPE;
+  if (((uintptr_t)x & 3u) || ((uintptr_t)y & 3u)) return TBIK_ERR_ALIGN;
+  if (n == 0) return TBIK_OK;
+  return tbik::launch_primitive(op, x, y, n, as_stream(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,159 @@
+// tbik_device.h -- device-side numerics of libtbik (gfx950).
+//
+// bf16 rounding, the library-defined EXP/LOG, and the streaming form of the
+// reduction tree.  Written for this library only; the CPU oracle used by the
+// tests is an independent implementation of the same definitions.
+//
+// Every floating-point operation here must be one IEEE binary32 operation:
+// the library is compiled with -ffp-contract=off, without fast-math, with
+// IEEE denormals and correctly rounded fp32 divide/sqrt.  Hardware
+// transcendental instructions (v_exp_f32, v_log_f32, v_rsq_f32) are never
+// used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+namespace tbik {
+
+__device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest, ties to even; NaN -> quiet NaN.
+// Adding 0x7fff plus the lowest kept bit to the pattern carries into the
+// kept half exactly when the discarded half is above one half-unit, or is a
+// tie with an odd kept half.
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// --- EXP ---------------------------------------------------------------------
+// x = k ln2 + r, k = rint(x log2 e); r via two fma with ln2 split into
+// hi (ln2 rounded to a multiple of 2^-16, so k*hi is exact for |k| < 2^8)
+// and lo; e^r by the degree-7 Taylor polynomial (coefficients 1/n! rounded
+// to fp32) in Horner form with fma; 2^k applied as two power-of-two
+// multiplies so that a subnormal result is rounded once.
+__device__ __forceinline__ float exp_f32(float x) {
+  if (x != x) return x + x;
+  if (x > 89.0f) return __builtin_inff();
+  if (x < -104.0f) return 0.0f;
+  const float kf = __builtin_rintf(x * 0x1.715476p+0f);
+  const int k = (int)kf;
+  float r = __builtin_fmaf(-kf, 0x1.62e4p-1f, x);
+  r = __builtin_fmaf(-kf, 0x1.7f7d1cp-20f, r);
+  float p = 0x1.a01a02p-13f;                   // 1/7!
+  p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);   // 1/6!
+  p = __builtin_fmaf(p, r, 0x1.111112p-7f);    // 1/5!
+  p = __builtin_fmaf(p, r, 0x1.555556p-5f);    // 1/4!
+  p = __builtin_fmaf(p, r, 0x1.555556p-3f);    // 1/3!
+  p = __builtin_fmaf(p, r, 0.5f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  p = __builtin_fmaf(p, r, 1.0f);
+  const int k1 = k >> 1;
+  const int k2 = k - k1;
+  const float s1 = __uint_as_float((uint32_t)(k1 + 127) << 23);
+  const float s2 = __uint_as_float((uint32_t)(k2 + 127) << 23);
+  return (p * s1) * s2;
+}
+
+// --- LOG ---------------------------------------------------------------------
+// x = 2^k m, m in [sqrt(1/2), sqrt(2)); f = m - 1 (exact); s = f/(2+f);
+// log(1+f) = 2 atanh(s) = f - hfsq + s (hfsq + R(s^2)), hfsq = f^2/2,
+// R(z) = 2z/3 + 2z^2/5 + 2z^3/7 + 2z^4/9; then + k ln2 with the split ln2.
+__device__ __forceinline__ float log_f32(float x) {
+  if (x != x) return x + x;
+  if (x < 0.0f) return __builtin_nanf("");
+  if (x == 0.0f) return -__builtin_inff();
+  if (x == __builtin_inff()) return x;
+  uint32_t ix = __float_as_uint(x);
+  int k = 0;
+  if (ix < 0x00800000u) {                 // subnormal: scale by 2^25
+    x = x * 0x1p25f;
+    ix = __float_as_uint(x);
+    k = -25;
+  }
+  k += (int)(ix >> 23) - 127;
+  const uint32_t mant = ix & 0x007fffffu;
+  float m;
+  if (mant > 0x3504f3u) {                 // mantissa above that of fp32(sqrt 2)
+    m = __uint_as_float(mant | 0x3f000000u);
+    k += 1;
+  } else {
+    m = __uint_as_float(mant | 0x3f800000u);
+  }
+  const float f = m - 1.0f;
+  const float s = f / (2.0f + f);
+  const float z = s * s;
+  float R = __builtin_fmaf(z, 0x1.c71c72p-3f, 0x1.24924ap-2f);   // 2/9, 2/7
+  R = __builtin_fmaf(z, R, 0x1.99999ap-2f);                       // 2/5
+  R = __builtin_fmaf(z, R, 0x1.555556p-1f);                       // 2/3
+  R = z * R;
+  const float hfsq = (0.5f * f) * f;
+  const float kf = (float)k;
+  return kf * 0x1.62e4p-1f - ((hfsq - (s * (hfsq + R) + kf * 0x1.7f7d1cp-20f)) - f);
+}
+
+// --- the tree ----------------------------------------------------------------
+// T of the tree over n leaves: the largest power of two <= 8 dividing n.
+__host__ __device__ __forceinline__ int tree_T(int64_t n) {
+  int T = 8;
+  while (T > 1 && (n % T) != 0) T >>= 1;
+  return T;
+}
+
+// Streaming evaluation of one PAIR reduction over n leaves that arrive in
+// order (index cnt = 0, 1, ...), R values per lane at once (a register tile).
+// s[j] holds the finished subtree of 2^j leaves at level j.  The merge of a
+// new leaf is a binary-counter carry (levels below the trailing-ones count
+// of cnt); the last leaf folds the remaining subtrees in from the lowest to
+// the highest level.  That is PAIR's structure: a left-to-right sequence of
+// power-of-two blocks, block j+1 added to the fold of the smaller blocks.
+// D must be at least the bit length of n-1.  cnt and n are wave-uniform, so
+// every branch below is a scalar branch and every index is static.
+// Returns true on the last leaf; the PAIR value is then in `node`.
+template <int R, int D>
+__device__ __forceinline__ bool pair_push(float (&s)[D > 0 ? D : 1][R], float (&node)[R], int cnt,
+                                          int n) {
+  const int t = __builtin_ctz(~(unsigned)cnt);
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (j < t) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) node[r] = s[j][r] + node[r];
+    }
+  }
+  if (cnt + 1 == n) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      if (j > t && ((cnt >> j) & 1)) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) node[r] = s[j][r] + node[r];
+      }
+    }
+    return true;
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    if (j == t) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) s[j][r] = node[r];
+    }
+  }
+  return false;
+}
+
+// Bit length of v (0 for v == 0).
+__host__ __device__ __forceinline__ int bit_length(int64_t v) {
+  int b = 0;
+  while (v > 0) { ++b; v >>= 1; }
+  return b;
+}
+
+}  // namespace tbik

@@ -1,0 +1,42 @@
+// tbik_internal.h -- launchers shared between the kernel files and the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tbik {
+
+// One GEMM launch: C[bat][part] = tree node over the groups of `part`.
+struct GemmCall {
+  const uint16_t *A; int64_t lda; int64_t strideA;
+  const uint16_t *W; int64_t ldw; int64_t strideW;
+  float *C; uint16_t *Cb; int64_t ldc; int64_t strideC;
+  int64_t part_stride;   // element offset between the outputs of two parts
+  int M, N, K, batch;
+  int parts;             // K split into `parts` tree nodes (1 = the root)
+  int leaf_mode;         // 0 MFMA, 1 scalar
+};
+
+// Returns 0 or a TBIK_ERR_* code.
+int launch_gemm(const GemmCall &c, hipStream_t s);
+int launch_tree_combine(const float *ws, int tp, float *C, int64_t ldc, uint16_t *Cb, int M,
+                        int N, hipStream_t s);
+int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+                            uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
+                            float eps, hipStream_t s);
+int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
+                const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+                int max_pos, hipStream_t s);
+int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
+                  int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s);
+int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out,
+                      int M, int V, int tp, float *ws, hipStream_t s);
+int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P,
+                          int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
+                          float scale, hipStream_t s);
+int launch_primitive(int op, const float *x, float *y, int64_t n, hipStream_t s);
+
+// Maximum leaves per tree group supported by the kernels.
+constexpr int kMaxGroupLeaves = 512;
+
+}  // namespace tbik
