@@ -1,0 +1,376 @@
+#!/usr/bin/env python3
+"""Benchmark of the tree-based invariant kernels on one MI355X.
+
+Headline step (the row-parallel down-projection workload): one pass of the
+simulated tensor-parallel GEMM over a batch of M=256 tokens,
+A [256, 14336] bf16 ~N(0,1), W [4096, 14336] bf16 ~N(0,0.02), K split into
+tp=8 shards: the shard-partials kernel (64-wide K-block MFMA leaves + the
+in-register tree) writes 8 fp32 partials, the combine kernel runs the top
+of the tree.  value = 2*M*N*K / step time (TFLOP/s).  Inputs are resident in
+HBM; W rotates over several copies so every step streams W from HBM rather
+than from the 256 MB last-level cache.
+
+Also reported: the same GEMM at tp=1 for M in {1,32,256} against torch's
+bf16 GEMM (hipBLASLt) -- the non-invariant baseline and overhead; a
+compute-bound M=4096 prefill and the LM-head GEMM (M=512, K=4096,
+N=151936) as % of the bf16 MFMA peak; the row kernels as % of HBM
+bandwidth; the bitwise mismatch count across tp and M; and the CPU oracle
+timed on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+METRIC = "invariant GEMM TFLOP/s (% MFMA peak, overhead vs hipBLASLt); 0 bit mismatches"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--M", type=int, default=256)
+    ap.add_argument("--tp", type=int, default=8)
+    ap.add_argument("--no-extra", action="store_true", help="headline step only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--pmc-calib", action="store_true",
+                    help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--only", default="", help="run only one extra workload (profiling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the tensor-parallel shards are simulated on a "
+              "single MI355X (no collectives); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    root = os.path.dirname(os.path.abspath(__file__))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import tp_invariant_numerics_amd as tb
+    from tp_invariant_numerics_amd import inputs
+
+    if not os.path.exists(tb._build.LIB):
+        import __graft_entry__
+        __graft_entry__.build()
+    tb.lib()
+    dev = "cuda"
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    if args.pmc_calib:
+        # plain copy kernel of known size for FETCH_SIZE / WRITE_SIZE scaling
+        nbytes = 1 << 30
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("pmc-calib: copied %d bytes x5" % nbytes)
+        return
+
+    def timed(fn, iters, warm=3):
+        """Average ms per call of fn() over iters calls, HIP events on the stream."""
+        for _ in range(warm):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(iters):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / iters
+
+    # ------------------------------------------------------------------ headline
+    M, K, N, tp = args.M, 14336, 4096, args.tp
+    w_bytes = N * K * 2
+    n_rot = max(2, -(-600_000_000 // w_bytes))       # > 2x the 256 MB last-level cache
+    log("inputs: A [%d,%d], W [%d,%d] x%d rotating copies, tp=%d" % (M, K, N, K, n_rot, tp))
+    A = inputs.normal_bf16((M, K), 1001, device=dev)
+    Ws = [inputs.normal_bf16((N, K), 2001 + i, std=0.02, device=dev) for i in range(n_rot)]
+    ws = torch.empty((tp, M, N), dtype=torch.float32, device=dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    flops = 2.0 * M * N * K
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+
+    def step(i, rec=None):
+        W = Ws[i % n_rot]
+        if rec:
+            rec[0].record(stream)
+        tb.tbik_gemm_tp_partials(A, W, tp, ws=ws)
+        if rec:
+            rec[1].record(stream)
+        tb.tbik_tree_combine(ws, out=C)
+        if rec:
+            rec[2].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = sum(a.elapsed_time(b) for a, b, c in ev) / args.steps
+    comb_ms = sum(b.elapsed_time(c) for a, b, c in ev) / args.steps
+    step_ms = sum(a.elapsed_time(c) for a, b, c in ev) / args.steps
+    ms_per_step = max(step_ms, wall * 1e3 / args.steps)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    log("step %.4f ms (partials %.4f ms, combine %.4f ms), wall %.4f ms/step"
+        % (step_ms, part_ms, comb_ms, wall * 1e3 / args.steps))
+
+    # roofline of the dominant kernel (the shard-partials GEMM): HBM-bound
+    # (arithmetic intensity 2MNK / bytes < 2500e12/8e12 = 312 FLOP/B)
+    part_bytes = M * K * 2 + N * K * 2 + tp * M * N * 4
+    achieved_gbs = part_bytes / (part_ms * 1e-3) / 1e9
+    roofline = {"kernel": "k_gemm_mfma (tp shard partials)", "bound": "hbm",
+                "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "algorithmic_bytes_per_launch": part_bytes,
+                "avg_launch_ms": round(part_ms, 5),
+                "arith_intensity_flop_per_byte": round(flops / part_bytes, 1),
+                "mfma_frac": round(flops / (part_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+    # bitwise invariance over tp and batch size on this workload
+    mismatches = 0
+    W0 = Ws[0]
+    ref = tb.tbik_gemm(A, W0)[0]
+    for t in (1, 2, 4, 8):
+        Ct = tb.tbik_gemm_tpsim(A, W0, t)[0]
+        mismatches += int((Ct.view(torch.int32) != ref.view(torch.int32)).sum().item())
+    for m in (1, 32, 255):
+        Cm = tb.tbik_gemm(A[:m], W0)[0]
+        mismatches += int((Cm.view(torch.int32) != ref[:m].view(torch.int32)).sum().item())
+    log("bit mismatches across tp {1,2,4,8} and M {1,32,255,256}: %d" % mismatches)
+
+    # non-invariant baseline: torch bf16 GEMM (hipBLASLt), same shape
+    rot = {"i": 0}
+
+    def blas_rot():
+        rot["i"] += 1
+        return torch.matmul(A, Ws[rot["i"] % n_rot].t())
+
+    t_blas = timed(blas_rot, args.steps)
+
+    def tbik_tp1_rot():
+        rot["i"] += 1
+        return tb.tbik_gemm(A, Ws[rot["i"] % n_rot], out=C)
+
+    t_tp1 = timed(tbik_tp1_rot, args.steps)
+    hipblaslt = {"what": "torch.matmul bf16 (hipBLASLt), same shape, not tp-invariant",
+                 "ms": round(t_blas, 5), "tflops": round(flops / t_blas / 1e9, 1),
+                 "tbik_tp1_ms": round(t_tp1, 5),
+                 "overhead_tp1_pct": round((t_tp1 / t_blas - 1) * 100, 1),
+                 "overhead_tpsim_pct": round((ms_per_step / t_blas - 1) * 100, 1)}
+    log("hipBLASLt %.4f ms; tbik tp=1 %.4f ms; tpsim step %.4f ms" % (t_blas, t_tp1, ms_per_step))
+
+    extra = {}
+    if not args.no_extra:
+        extra = run_extra(tb, inputs, torch, np, dev, timed, log, args)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(inputs, np, log, A, Ws[0], tp)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "row-parallel down-proj GEMM, M=%d K=%d N=%d, simulated TP=%d "
+                               "(shard partials + tree combine)" % (M, K, N, tp),
+                   "M": M, "K": K, "N": N, "tp": tp, "rotating_W_copies": n_rot,
+                   "A": "bf16 ~N(0,1)", "W": "bf16 ~N(0,0.02)", "accumulate": "fp32 tree"},
+        "pct_mfma_peak": round(value / PEAK_BF16_TFLOPS * 100, 2),
+        "bit_mismatches": mismatches,
+        "roofline": roofline,
+        "hipblaslt": hipblaslt,
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def run_extra(tb, inputs, torch, np, dev, timed, log, args):
+    res = {}
+    only = args.only
+
+    def want(name):
+        return not only or only == name
+
+    # --- tp=1 GEMM at the other batch sizes vs hipBLASLt
+    if want("gemm_m"):
+        K, N = 14336, 4096
+        Ws = [inputs.normal_bf16((N, K), 3001 + i, std=0.02, device=dev) for i in range(5)]
+        for M in (1, 32, 256):
+            A = inputs.normal_bf16((M, K), 3100 + M, device=dev)
+            C = torch.empty((M, N), dtype=torch.float32, device=dev)
+            k = {"i": 0}
+
+            def ours():
+                k["i"] += 1
+                tb.tbik_gemm(A, Ws[k["i"] % 5], out=C)
+
+            def blas():
+                k["i"] += 1
+                torch.matmul(A, Ws[k["i"] % 5].t())
+
+            t1, t2 = timed(ours, 30), timed(blas, 30)
+            byt = M * K * 2 + N * K * 2 + M * N * 4
+            res["downproj_tp1_M%d" % M] = {
+                "ms": round(t1, 5), "tflops": round(2 * M * N * K / t1 / 1e9, 1),
+                "hbm_gbs": round(byt / t1 / 1e6, 1), "hbm_frac": round(byt / t1 / 1e6 / 8000, 4),
+                "hipblaslt_ms": round(t2, 5), "overhead_pct": round((t1 / t2 - 1) * 100, 1)}
+            log("downproj M=%d: %.4f ms (hipBLASLt %.4f)" % (M, t1, t2))
+        del Ws
+
+    # --- compute-bound shapes: M=4096 prefill and the LM head
+    if want("prefill"):
+        M, K, N = 4096, 14336, 4096
+        A = inputs.normal_bf16((M, K), 3200, device=dev)
+        W = inputs.normal_bf16((N, K), 3201, std=0.02, device=dev)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        t1 = timed(lambda: tb.tbik_gemm(A, W, out=C), 10)
+        t2 = timed(lambda: torch.matmul(A, W.t()), 10)
+        fl = 2.0 * M * N * K
+        res["prefill_M4096_K14336_N4096"] = {
+            "ms": round(t1, 4), "tflops": round(fl / t1 / 1e9, 1),
+            "mfma_frac": round(fl / t1 / 1e9 / 2500, 4), "hipblaslt_ms": round(t2, 4),
+            "hipblaslt_tflops": round(fl / t2 / 1e9, 1),
+            "overhead_pct": round((t1 / t2 - 1) * 100, 1)}
+        log("prefill: %.3f ms = %.1f TFLOP/s (hipBLASLt %.3f ms)" % (t1, fl / t1 / 1e9, t2))
+        del A, W, C
+
+    logits = None
+    if want("lmhead") or want("logsoftmax"):
+        M, K, V = 512, 4096, 151936
+        A = inputs.normal_bf16((M, K), 3300, device=dev)
+        W = inputs.normal_bf16((V, K), 3301, std=0.02, device=dev)
+        logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+        if want("lmhead"):
+            t1 = timed(lambda: tb.tbik_gemm(A, W, out=logits), 5, warm=2)
+            t2 = timed(lambda: torch.matmul(A, W.t()), 5, warm=2)
+            fl = 2.0 * M * V * K
+            res["lmhead_M512_K4096_N151936"] = {
+                "ms": round(t1, 4), "tflops": round(fl / t1 / 1e9, 1),
+                "mfma_frac": round(fl / t1 / 1e9 / 2500, 4), "hipblaslt_ms": round(t2, 4),
+                "hipblaslt_tflops": round(fl / t2 / 1e9, 1),
+                "overhead_pct": round((t1 / t2 - 1) * 100, 1)}
+            log("lmhead: %.3f ms = %.1f TFLOP/s (hipBLASLt %.3f ms)" % (t1, fl / t1 / 1e9, t2))
+        else:
+            tb.tbik_gemm(A, W, out=logits)
+        tgt = inputs.uniform_int(M, V, 3302, device=dev)
+        nbytes = M * V * 4
+        for tpv in (1, 4):
+            ws = torch.empty((tb.tbik_logsoftmax_workspace_bytes(M, V, tpv) // 4,),
+                             dtype=torch.float32, device=dev)
+            out = torch.empty((M,), dtype=torch.float32, device=dev)
+            t = timed(lambda: tb.tbik_logsoftmax_gather(logits, tgt, tpv, ws=ws, out=out), 20)
+            res["logsoftmax_M512_V151936_tp%d" % tpv] = {
+                "ms": round(t, 5), "gbs": round(nbytes / t / 1e6, 1),
+                "hbm_frac": round(nbytes / t / 1e6 / 8000, 4),
+                "note": "algorithmic bytes = one read of the fp32 logits"}
+            log("logsoftmax tp=%d: %.4f ms = %.0f GB/s" % (tpv, t, nbytes / t / 1e6))
+        del A, W, logits
+
+    if want("rmsnorm"):
+        rows, H = 4096, 4096
+        xs = [inputs.outlier_bf16((rows, H), 3400 + i, device=dev) for i in range(4)]
+        rs = [inputs.outlier_bf16((rows, H), 3410 + i, device=dev) for i in range(4)]
+        w = inputs.normal_bf16((H,), 3420, std=0.1, mean=1.0, device=dev)
+        y = torch.empty_like(xs[0]); ro = torch.empty_like(xs[0])
+        k = {"i": 0}
+
+        def f():
+            k["i"] += 1
+            tb.tbik_rmsnorm_residual(xs[k["i"] % 4], rs[k["i"] % 4], w, 1e-6, y=y, r_out=ro)
+
+        t = timed(f, 30)
+        nbytes = 4 * rows * H * 2 + H * 2
+        res["rmsnorm_4096x4096"] = {"ms": round(t, 5), "gbs": round(nbytes / t / 1e6, 1),
+                                    "hbm_frac": round(nbytes / t / 1e6 / 8000, 4)}
+        log("rmsnorm: %.4f ms = %.0f GB/s" % (t, nbytes / t / 1e6))
+        del xs, rs
+
+    if want("rope"):
+        T, heads, d = 32768, 16, 128
+        x = inputs.normal_bf16((T, heads, d), 3500, device=dev)
+        pos = inputs.positions(T, 32768, seed=3501).to(dev)
+        c, s = tb.tbik_rope_table(1e6, d, 32768)
+        c, s = c.to(dev), s.to(dev)
+        y = torch.empty_like(x)
+        t = timed(lambda: tb.tbik_rope(x, pos, c, s, y=y), 30)
+        nbytes = 2 * T * heads * d * 2 + T * (d // 2) * 4 * 2 + T * 4
+        res["rope_32768x16x128"] = {"ms": round(t, 5), "gbs": round(nbytes / t / 1e6, 1),
+                                    "hbm_frac": round(nbytes / t / 1e6 / 8000, 4)}
+        log("rope: %.4f ms = %.0f GB/s" % (t, nbytes / t / 1e6))
+        del x, y
+
+    if want("swiglu"):
+        rows, cols = 4096, 14336
+        g = inputs.normal_bf16((rows, cols), 3600, std=3.0, device=dev)
+        u = inputs.normal_bf16((rows, cols), 3601, device=dev)
+        o = torch.empty_like(g)
+        t = timed(lambda: tb.tbik_swiglu(g, u, out=o), 30)
+        nbytes = 3 * rows * cols * 2
+        res["swiglu_4096x14336"] = {"ms": round(t, 5), "gbs": round(nbytes / t / 1e6, 1),
+                                    "hbm_frac": round(nbytes / t / 1e6 / 8000, 4)}
+        log("swiglu: %.4f ms = %.0f GB/s" % (t, nbytes / t / 1e6))
+        del g, u, o
+    return res
+
+
+def cpu_baseline(inputs, np, log, A, W, tp):
+    """The CPU oracle (scalar C, as it stands) on a bounded sample of the
+    headline workload: all M rows x a block of output columns, simulated tp."""
+    import oracle
+    nth = min(16, os.cpu_count() or 1)
+    Ab = inputs.bits(A)
+    M, K = Ab.shape
+    cols = 8
+    while True:
+        Wb = inputs.bits(W[:cols])
+        t0 = time.perf_counter()
+        oracle.gemm_tpsim(Ab, Wb, tp, nthreads=nth)
+        dt = time.perf_counter() - t0
+        if dt >= 5.0 or cols >= W.shape[0]:
+            break
+        cols = min(W.shape[0], cols * max(2, int(8.0 / max(dt, 1e-3))))
+    fl = 2.0 * M * cols * K
+    log("cpu oracle: %d x %d outputs, K=%d, tp=%d, %d threads: %.2f s" % (M, cols, K, tp, nth, dt))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": "oracle tpsim GEMM (scalar leaves, same tree) on A[%d,%d] x W[:%d] "
+                      "(all rows, first %d output columns), tp=%d" % (M, K, cols, cols, tp)}
+
+
+if __name__ == "__main__":
+    main()

@@ -41,8 +41,12 @@
  *    stream).  Outputs are valid once the stream reaches the call.
  *  - Arguments are validated on the host before any launch; an invalid
  *    call returns a negative TBIK_ERR_* code and launches nothing.
- *  - Data pointers must be 16-byte aligned; leading dimensions (in
- *    elements) must be multiples of 8.  Violations return TBIK_ERR_ALIGN.
+ *  - Pointers must be aligned to their element size.  GEMM operands A and
+ *    W (and RoPE's tensors and tables) must also be 16-byte aligned with
+ *    leading dimensions (in elements) that are multiples of 8; violations
+ *    return TBIK_ERR_ALIGN.  Other arrays take any leading dimension >= the
+ *    row length; wider memory accesses are used when alignment permits,
+ *    which never changes a result bit.
  *  - Outputs must not overlap inputs unless stated otherwise.
  *  - Inputs must be finite; non-finite inputs give unspecified values (but
  *    never out-of-bounds accesses).
@@ -131,6 +135,26 @@ size_t tbik_gemm_tpsim_workspace_bytes(int M, int N, int K, int tp);
 int tbik_gemm_tpsim(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
                     float *C, int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int tp,
                     int leaf_mode, float *ws, size_t ws_bytes, void *stream);
+
+/* Only the partial step of tbik_gemm_tpsim: all tp shard partials in one
+ * launch, ws[t] = ws + t*M*N (dense [M,N] fp32).  Same validation as
+ * tbik_gemm_tpsim (ws must hold tp*M*N floats). */
+int tbik_gemm_tp_partials(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
+                          float *ws, size_t ws_bytes, int M, int N, int K, int tp, int leaf_mode,
+                          void *stream);
+
+/* One rank's share of real tensor parallelism ([DT] 2.1.1; [TBIK]
+ * "technical framework": reduce locally, then combine across GPUs).
+ *  A_t  [M, K_total/tp] bf16: this rank's K slice of the activations
+ *  W_t  [N, K_total/tp] bf16: this rank's K slice of the weight rows
+ *  P    [M, N] fp32 (row stride ldp): this shard's node of the tree over
+ *       the K_total/64 leaves -- bit-identical to ws[t] of tbik_gemm_tpsim
+ *       for the shard whose columns are given.  tp | T of the full tree.
+ * Combining the tp ranks' P (gathered into a dense [tp][M][N] buffer) with
+ * tbik_tree_combine reproduces tbik_gemm bit for bit. */
+int tbik_gemm_shard(const tbik_bf16 *A_t, int64_t lda, const tbik_bf16 *W_t, int64_t ldw,
+                    float *P, int64_t ldp, int M, int N, int K_total, int tp, int leaf_mode,
+                    void *stream);
 
 /* Only the combine step of tbik_gemm_tpsim: C = top tree over ws[0..tp-1]
  * (dense [tp][M][N] fp32 partials).  Lets a caller that produced the

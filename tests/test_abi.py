@@ -19,7 +19,7 @@ OK, E_NULL, E_SHAPE, E_TP, E_ALIGN, E_WS, E_LAUNCH, E_ARG = 0, -1, -2, -3, -4, -
 FAKE = C.c_void_p(1 << 20)        # aligned, never dereferenced (validation fails first)
 FAKE2 = C.c_void_p(2 << 20)
 FAKE3 = C.c_void_p(3 << 20)
-MISAL = C.c_void_p((1 << 20) + 4)
+MISAL = C.c_void_p((1 << 20) + 1)     # violates every element alignment
 
 
 @pytest.fixture(scope="module")
@@ -73,7 +73,8 @@ def test_gemm_validation(L):
     # alignment: misaligned pointer, leading dimension not a multiple of 8
     assert g(MISAL, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_ALIGN
     assert g(FAKE, 68, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_ALIGN
-    assert g(FAKE, 64, FAKE2, 64, FAKE3, 12, None, 4, 4, 64, 0, None) == E_ALIGN
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 3, None, 4, 4, 64, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, MISAL, 64, None, 4, 4, 64, 0, None) == E_ALIGN
     # leaf mode
     assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 7, None) == E_ARG
     # tree groups beyond the supported depth (K = 64 * 1031, a prime leaf count)

@@ -323,3 +323,58 @@ def test_softmax_causal_bitexact(orc, B, Lq, Lk, offset):
     P = tb.tbik_softmax_causal(torch.from_numpy(S).to(DEV), offset, float(scale))
     for b in range(B):
         assert np.array_equal(bits(P[b]), orc.softmax_causal(S[b], offset, scale))
+
+
+# ------------------------------------------------------------------ real-TP building blocks
+@pytest.mark.parametrize("leaf", [tb.LEAF_MFMA, tb.LEAF_SCALAR])
+def test_gemm_shard_and_partials_match_tpsim(orc, leaf):
+    M, N, K = 24, 96, 14336
+    A = inputs.normal_bf16((M, K), 7200, device=DEV)
+    W = inputs.normal_bf16((N, K), 7201, std=0.02, device=DEV)
+    ref = f32_bits_t(tb.tbik_gemm(A, W, leaf_mode=leaf)[0])
+    for tp in (1, 2, 4, 8):
+        _, _, ws = tb.tbik_gemm_tpsim(A, W, tp, leaf_mode=leaf)
+        parts = tb.tbik_gemm_tp_partials(A, W, tp, leaf_mode=leaf)
+        assert np.array_equal(f32_bits_t(parts), f32_bits_t(ws)), tp
+        ks = K // tp
+        shards = torch.stack([tb.tbik_gemm_shard(A[:, t * ks:(t + 1) * ks].contiguous(),
+                                                 W[:, t * ks:(t + 1) * ks].contiguous(),
+                                                 K, tp, leaf_mode=leaf) for t in range(tp)])
+        assert np.array_equal(f32_bits_t(shards), f32_bits_t(ws)), tp
+        assert np.array_equal(f32_bits_t(tb.tbik_tree_combine(shards)), ref), tp
+    if leaf == tb.LEAF_SCALAR:
+        _, refws = orc.gemm_tpsim(bits(A.cpu()), bits(W.cpu()), 8)
+        assert same_bits(parts.cpu().numpy(), refws)
+
+
+# ------------------------------------------------------------------ unaligned strides
+def test_rowops_unaligned_strides(orc):
+    rows, H = 6, 4096
+    x = inputs.outlier_bf16((rows, H), 7300)
+    r = inputs.outlier_bf16((rows, H), 7301)
+    w = inputs.normal_bf16((H,), 7302, std=0.1, mean=1.0)
+    ry, rr = orc.rmsnorm_residual(bits(x), bits(r), bits(w), 1e-6)
+    for pad in (1, 3, 4):
+        xd = torch.zeros((rows, H + pad), dtype=torch.bfloat16, device=DEV)
+        rd = torch.zeros_like(xd)
+        xd[:, :H] = x.to(DEV)
+        rd[:, :H] = r.to(DEV)
+        yd = torch.zeros_like(xd)
+        rod = torch.zeros_like(xd)
+        tb.tbik_rmsnorm_residual(xd[:, :H], rd[:, :H], w.to(DEV), 1e-6, y=yd[:, :H],
+                                 r_out=rod[:, :H])
+        assert np.array_equal(bits(yd[:, :H]), ry), pad
+        assert np.array_equal(bits(rod[:, :H]), rr), pad
+    g = inputs.normal_bf16((5, 64), 7303, std=3.0)
+    u = inputs.normal_bf16((5, 64), 7304)
+    gd = torch.zeros((5, 67), dtype=torch.bfloat16, device=DEV)
+    gd[:, :64] = g.to(DEV)
+    out = tb.tbik_swiglu(gd[:, :64], u.to(DEV))
+    assert np.array_equal(bits(out), orc.swiglu(bits(g), bits(u)))
+    rng = np.random.default_rng(7305)
+    logits = (rng.standard_normal((4, 32000)) * 3).astype(np.float32)
+    tgt = rng.integers(0, 32000, 4).astype(np.int32)
+    ld = torch.zeros((4, 32003), dtype=torch.float32, device=DEV)
+    ld[:, :32000] = torch.from_numpy(logits).to(DEV)
+    lp, _ = tb.tbik_logsoftmax_gather(ld[:, :32000], torch.from_numpy(tgt).to(DEV), 4)
+    assert same_bits(lp.cpu().numpy(), orc.logsoftmax_gather(logits, tgt, 4)[0])

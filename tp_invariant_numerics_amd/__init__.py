@@ -18,7 +18,7 @@ from . import build as _build
 __all__ = [
     "TbikError", "lib", "tbik_version", "tbik_strerror", "tbik_tree_groups", "tbik_gemm",
     "tbik_gemm_strided_batched", "tbik_gemm_tpsim", "tbik_gemm_tpsim_workspace_bytes",
-    "tbik_tree_combine", "tbik_rmsnorm_residual", "tbik_rope", "tbik_rope_table",
+    "tbik_tree_combine", "tbik_gemm_tp_partials", "tbik_gemm_shard", "tbik_rmsnorm_residual", "tbik_rope", "tbik_rope_table",
     "tbik_swiglu", "tbik_logsoftmax_gather", "tbik_logsoftmax_workspace_bytes",
     "tbik_softmax_causal", "tbik_primitive", "LEAF_MFMA", "LEAF_SCALAR",
 ]
@@ -58,6 +58,8 @@ def _sigs():
         "tbik_gemm_tpsim_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "tbik_gemm_tpsim": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, i32, p, sz, p]),
         "tbik_tree_combine": (i32, [p, i32, p, i64, p, i32, i32, p]),
+        "tbik_gemm_tp_partials": (i32, [p, i64, p, i64, p, sz, i32, i32, i32, i32, i32, p]),
+        "tbik_gemm_shard": (i32, [p, i64, p, i64, p, i64, i32, i32, i32, i32, i32, p]),
         "tbik_rmsnorm_residual": (i32, [p, p, p, p, p, i32, i32, i64, f32, p]),
         "tbik_rope": (i32, [p, p, p, p, p, i32, i32, i32, i64, i32, p]),
         "tbik_rope_table": (i32, [f64, i32, i32, p, p]),
@@ -193,6 +195,33 @@ def tbik_gemm_tpsim(A, W, tp, leaf_mode=LEAF_MFMA, ws=None, out=None, out_bf16=N
                                ws.numel() * ws.element_size(), _stream())
     _chk(rc, "tbik_gemm_tpsim")
     return out, out_bf16, ws
+
+
+def tbik_gemm_tp_partials(A, W, tp, leaf_mode=LEAF_MFMA, ws=None):
+    """All tp shard partials of the simulated K split -> ws [tp, M, N] fp32."""
+    _bits(A); _bits(W); _need_gpu(A, W)
+    M, K = A.shape
+    N = W.shape[0]
+    if ws is None:
+        ws = torch.empty((tp, M, N), dtype=torch.float32, device=A.device)
+    rc = lib().tbik_gemm_tp_partials(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(ws),
+                                     ws.numel() * ws.element_size(), M, N, K, tp, leaf_mode,
+                                     _stream())
+    _chk(rc, "tbik_gemm_tp_partials")
+    return ws
+
+
+def tbik_gemm_shard(A_t, W_t, K_total, tp, leaf_mode=LEAF_MFMA, out=None):
+    """One rank's shard node from its own K slice: A_t [M, K_total/tp], W_t [N, K_total/tp]."""
+    _bits(A_t); _bits(W_t); _need_gpu(A_t, W_t)
+    M = A_t.shape[0]
+    N = W_t.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A_t.device)
+    rc = lib().tbik_gemm_shard(_ptr(A_t), _ld(A_t), _ptr(W_t), _ld(W_t), _ptr(out), _ld(out), M,
+                               N, K_total, tp, leaf_mode, _stream())
+    _chk(rc, "tbik_gemm_shard")
+    return out
 
 
 def tbik_tree_combine(ws, out=None, out_bf16=None):

@@ -289,7 +289,7 @@ static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
 }
 
 int launch_gemm(const GemmCall &c, hipStream_t s) {
-  const int nb = c.K / 64;
+  const int nb = c.shard_of > 0 ? c.tree_leaves : c.K / 64;
   const int T = tree_T(nb);
   GemmArgs a;
   a.A = c.A; a.lda = c.lda; a.strideA = c.strideA;
@@ -298,8 +298,11 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
   a.M = c.M; a.N = c.N;
   a.G = nb / T;
   a.parts = c.parts;
-  a.gpp = T / c.parts;
+  a.gpp = T / (c.shard_of > 0 ? c.shard_of : c.parts);
   if (a.G > kMaxGroupLeaves) return TBIK_ERR_SHAPE;
+  if ((int64_t)c.batch * c.parts > 65535) return TBIK_ERR_SHAPE;
+  if (c.leaf_mode == TBIK_LEAF_SCALAR && c.M > 65535) return TBIK_ERR_SHAPE;
+  if ((c.M + 15) / 16 > 65535) return TBIK_ERR_SHAPE;
   if (c.leaf_mode == TBIK_LEAF_SCALAR) {
     dim3 grid((unsigned)((c.N + 63) / 64), (unsigned)c.M, (unsigned)(c.batch * c.parts));
     hipLaunchKernelGGL(k_gemm_scalar, grid, dim3(64), 0, s, a);

@@ -131,6 +131,31 @@ static int chunk_for(int64_t G) {
   return ch;
 }
 
+// Largest power of two <= 16 (in elements of `elem` bytes) that divides the
+// element offset of p and the row stride ld: the alignment of every row start.
+static int elem_align(const void *p, int64_t ld, int elem) {
+  int a = 16;
+  const uintptr_t off = (uintptr_t)p / (uintptr_t)elem;
+  while (a > 1 && (((off % a) != 0) || (ld % a) != 0)) a >>= 1;
+  if ((uintptr_t)p % elem) a = 1;
+  return a;
+}
+
+// Chunk width for bf16 rows: 16/8-wide chunks use 16-byte accesses (row
+// starts 8-element aligned), 4-wide use 8-byte accesses.  The tree does not
+// depend on the chunk width, only on which chunk sizes divide the group.
+static int cap_bf16(int ch, int align) {
+  if (ch >= 8 && align < 8) ch = align >= 4 ? 4 : 2;
+  if (ch == 4 && align < 4) ch = 2;
+  return ch;
+}
+
+// Chunk width for fp32 rows: >= 4 uses 16-byte accesses.
+static int cap_f32(int ch, int align) {
+  if (ch >= 4 && align < 4) ch = 2;
+  return ch;
+}
+
 // =============================================================================
 // residual-add + RMSNorm: one workgroup per row.
 // =============================================================================
@@ -177,7 +202,12 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
                             uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
                             float eps, hipStream_t s) {
   const int T = tree_T(H);
-  const int ch = chunk_for(H / T);
+  int al = elem_align(x, ld, 2);
+  al = al < elem_align(r, ld, 2) ? al : elem_align(r, ld, 2);
+  al = al < elem_align(y, ld, 2) ? al : elem_align(y, ld, 2);
+  al = al < elem_align(w, 16, 2) ? al : elem_align(w, 16, 2);
+  if (r_out) al = al < elem_align(r_out, ld, 2) ? al : elem_align(r_out, ld, 2);
+  const int ch = cap_bf16(chunk_for(H / T), al);
   const int nch = H / ch;
   if (nch > 8192) return TBIK_ERR_SHAPE;
   const size_t lds = 2 * (size_t)nch * sizeof(float);
@@ -283,7 +313,8 @@ k_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols, 
 
 int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
                   int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s) {
-  const bool vec = (cols % 8) == 0;
+  const bool vec = (cols % 8) == 0 && elem_align(g, ldg, 2) >= 8 && elem_align(u, ldu, 2) >= 8 &&
+                   elem_align(o, ldo, 2) >= 8;
   const int64_t total = (int64_t)rows * (vec ? cols / 8 : cols);
   int64_t blocks = (total + 255) / 256;
   if (blocks > 262144) blocks = 262144;
@@ -387,7 +418,7 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
                       int V, int tp, float *ws, hipStream_t s) {
   const int T = tree_T(V);
   const int G = V / T;
-  const int ch = chunk_for(G);
+  const int ch = cap_f32(chunk_for(G), elem_align(logits, ld, 4));
   const int gc = G / ch;
   if (gc > 8192) return TBIK_ERR_SHAPE;
   float *gmax = ws;
@@ -478,7 +509,14 @@ int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16
                           float scale, hipStream_t s) {
   const int T = tree_T(Lk);
   int ch = chunk_for(Lk / T);
-  if (ch > 8) ch = 8;       // keep bf16 stores 16-byte aligned or scalar
+  if (ch > 8) ch = 8;
+  ch = cap_f32(ch, elem_align(S, ld_s, 4) < elem_align(S, stride_s, 4) ? elem_align(S, ld_s, 4)
+                                                                       : elem_align(S, stride_s, 4));
+  {
+    const int ap = elem_align(P, ld_p, 2) < elem_align(P, stride_p, 2) ? elem_align(P, ld_p, 2)
+                                                                       : elem_align(P, stride_p, 2);
+    ch = cap_bf16(ch, ap);
+  }
   const int nch = Lk / ch;
   if (nch > 8192) return TBIK_ERR_SHAPE;
   const size_t lds = 2 * (size_t)nch * sizeof(float);

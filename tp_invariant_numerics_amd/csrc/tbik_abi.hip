@@ -15,6 +15,7 @@ using tbik::GemmCall;
 namespace {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned(const void *p, unsigned a) { return ((uintptr_t)p & (a - 1u)) == 0; }
 bool ld_ok(int64_t ld) { return ld > 0 && (ld % 8) == 0; }
 hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
 bool tp_ok(int tp) { return tp == 1 || tp == 2 || tp == 4 || tp == 8; }
@@ -25,8 +26,8 @@ int check_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
   if (!A || !W || (!C && !Cb)) return TBIK_ERR_NULL;
   if (M < 0 || N < 0 || K <= 0 || (K % 64) != 0) return TBIK_ERR_SHAPE;
   if (lda < K || ldw < K || ldc < N) return TBIK_ERR_SHAPE;
-  if (!ld_ok(lda) || !ld_ok(ldw) || !ld_ok(ldc)) return TBIK_ERR_ALIGN;
-  if (!aligned16(A) || !aligned16(W) || (C && !aligned16(C)) || (Cb && !aligned16(Cb)))
+  if (!ld_ok(lda) || !ld_ok(ldw)) return TBIK_ERR_ALIGN;
+  if (!aligned16(A) || !aligned16(W) || (C && !aligned(C, 4)) || (Cb && !aligned(Cb, 2)))
     return TBIK_ERR_ALIGN;
   if (leaf_mode != TBIK_LEAF_MFMA && leaf_mode != TBIK_LEAF_SCALAR) return TBIK_ERR_ARG;
   const int nb = K / 64;
@@ -71,7 +72,7 @@ int tbik_gemm_strided_batched(const tbik_bf16 *A, int64_t lda, int64_t strideA,
   if (rc) return rc;
   if (batch < 0 || batch > 65535) return TBIK_ERR_SHAPE;
   if (strideA < 0 || strideW < 0 || strideC < 0) return TBIK_ERR_SHAPE;
-  if ((strideA % 8) || (strideW % 8) || (strideC % 8)) return TBIK_ERR_ALIGN;
+  if ((strideA % 8) || (strideW % 8)) return TBIK_ERR_ALIGN;
   if (M == 0 || N == 0 || batch == 0) return TBIK_OK;
   GemmCall c{};
   c.A = A; c.lda = lda; c.strideA = strideA;
@@ -97,7 +98,7 @@ int tbik_gemm_tpsim(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t
   if (M == 0 || N == 0) return TBIK_OK;
   if (!ws) return TBIK_ERR_WORKSPACE;
   if (ws_bytes < tbik_gemm_tpsim_workspace_bytes(M, N, K, tp)) return TBIK_ERR_WORKSPACE;
-  if (!aligned16(ws)) return TBIK_ERR_ALIGN;
+  if (!aligned(ws, 4)) return TBIK_ERR_ALIGN;
   GemmCall c{};
   c.A = A; c.lda = lda; c.strideA = 0;
   c.W = W; c.ldw = ldw; c.strideW = 0;
@@ -108,13 +109,51 @@ int tbik_gemm_tpsim(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t
   return tbik::launch_tree_combine(ws, tp, C, ldc, C_bf16, M, N, as_stream(stream));
 }
 
+int tbik_gemm_tp_partials(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
+                          float *ws, size_t ws_bytes, int M, int N, int K, int tp, int leaf_mode,
+                          void *stream) {
+  int rc = check_gemm(A, lda, W, ldw, ws, N, nullptr, M, N, K, leaf_mode);
+  if (rc) return rc;
+  const int T = tbik::tree_T(K / 64);
+  if (!tp_ok(tp) || (T % tp) != 0) return TBIK_ERR_TP;
+  if (M == 0 || N == 0) return TBIK_OK;
+  if (ws_bytes < tbik_gemm_tpsim_workspace_bytes(M, N, K, tp)) return TBIK_ERR_WORKSPACE;
+  GemmCall c{};
+  c.A = A; c.lda = lda; c.strideA = 0;
+  c.W = W; c.ldw = ldw; c.strideW = 0;
+  c.C = ws; c.Cb = nullptr; c.ldc = N; c.strideC = 0; c.part_stride = (int64_t)M * N;
+  c.M = M; c.N = N; c.K = K; c.batch = 1; c.parts = tp; c.leaf_mode = leaf_mode;
+  return tbik::launch_gemm(c, as_stream(stream));
+}
+
+int tbik_gemm_shard(const tbik_bf16 *A_t, int64_t lda, const tbik_bf16 *W_t, int64_t ldw,
+                    float *P, int64_t ldp, int M, int N, int K_total, int tp, int leaf_mode,
+                    void *stream) {
+  if (!tp_ok(tp) || K_total <= 0 || (K_total % 64) != 0) return !tp_ok(tp) ? TBIK_ERR_TP
+                                                                           : TBIK_ERR_SHAPE;
+  const int T = tbik::tree_T(K_total / 64);
+  if ((T % tp) != 0) return TBIK_ERR_TP;
+  const int K = K_total / tp;
+  int rc = check_gemm(A_t, lda, W_t, ldw, P, ldp, nullptr, M, N, K, leaf_mode);
+  if (rc) return rc;
+  const int nb = K_total / 64;
+  if (nb / T > tbik::kMaxGroupLeaves) return TBIK_ERR_SHAPE;
+  if (M == 0 || N == 0) return TBIK_OK;
+  GemmCall c{};
+  c.A = A_t; c.lda = lda; c.strideA = 0;
+  c.W = W_t; c.ldw = ldw; c.strideW = 0;
+  c.C = P; c.Cb = nullptr; c.ldc = ldp; c.strideC = 0; c.part_stride = 0;
+  c.M = M; c.N = N; c.K = K; c.batch = 1; c.parts = 1; c.leaf_mode = leaf_mode;
+  c.tree_leaves = nb; c.shard_of = tp;
+  return tbik::launch_gemm(c, as_stream(stream));
+}
+
 int tbik_tree_combine(const float *ws, int tp, float *C, int64_t ldc, tbik_bf16 *C_bf16, int M,
                       int N, void *stream) {
   if (!ws || (!C && !C_bf16)) return TBIK_ERR_NULL;
   if (!tp_ok(tp)) return TBIK_ERR_TP;
   if (M < 0 || N < 0 || ldc < N) return TBIK_ERR_SHAPE;
-  if (!ld_ok(ldc)) return TBIK_ERR_ALIGN;
-  if (!aligned16(ws) || (C && !aligned16(C)) || (C_bf16 && !aligned16(C_bf16)))
+  if (!aligned(ws, 4) || (C && !aligned(C, 4)) || (C_bf16 && !aligned(C_bf16, 2)))
     return TBIK_ERR_ALIGN;
   if (M == 0 || N == 0) return TBIK_OK;
   return tbik::launch_tree_combine(ws, tp, C, ldc, C_bf16, M, N, as_stream(stream));
@@ -126,9 +165,8 @@ int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf1
   if (!x || !r || !w || !y) return TBIK_ERR_NULL;
   if (rows < 0 || H < 1 || H > 65536 || ld < H) return TBIK_ERR_SHAPE;
   if (!(eps >= 0.0f) || isinf(eps)) return TBIK_ERR_ARG;
-  if (!ld_ok(ld)) return TBIK_ERR_ALIGN;
-  if (!aligned16(x) || !aligned16(r) || !aligned16(w) || !aligned16(y) ||
-      (r_out && !aligned16(r_out)))
+  if (!aligned(x, 2) || !aligned(r, 2) || !aligned(w, 2) || !aligned(y, 2) ||
+      (r_out && !aligned(r_out, 2)))
     return TBIK_ERR_ALIGN;
   if (rows == 0) return TBIK_OK;
   return tbik::launch_rmsnorm_residual(x, r, w, y, r_out, rows, H, ld, eps, as_stream(stream));
@@ -171,8 +209,7 @@ int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int 
   if (!gate || !up || !out) return TBIK_ERR_NULL;
   if (rows < 0 || cols < 0 || ld_gate < cols || ld_up < cols || ld_out < cols)
     return TBIK_ERR_SHAPE;
-  if (!ld_ok(ld_gate) || !ld_ok(ld_up) || !ld_ok(ld_out)) return TBIK_ERR_ALIGN;
-  if (!aligned16(gate) || !aligned16(up) || !aligned16(out)) return TBIK_ERR_ALIGN;
+  if (!aligned(gate, 2) || !aligned(up, 2) || !aligned(out, 2)) return TBIK_ERR_ALIGN;
   if (rows == 0 || cols == 0) return TBIK_OK;
   return tbik::launch_swiglu(gate, up, out, rows, cols, ld_gate, ld_up, ld_out,
                              as_stream(stream));
@@ -189,9 +226,7 @@ int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targe
   if (!logits || !targets || !out_lp) return TBIK_ERR_NULL;
   if (M < 0 || V < 1 || ld < V) return TBIK_ERR_SHAPE;
   if (!tp_ok(tp) || (tbik::tree_T(V) % tp) != 0) return TBIK_ERR_TP;
-  if (!ld_ok(ld)) return TBIK_ERR_ALIGN;
-  if (!aligned16(logits) || ((uintptr_t)targets & 3u) || ((uintptr_t)out_lp & 3u))
-    return TBIK_ERR_ALIGN;
+  if (!aligned(logits, 4) || !aligned(targets, 4) || !aligned(out_lp, 4)) return TBIK_ERR_ALIGN;
   if (M == 0) return TBIK_OK;
   if (M > 65535) return TBIK_ERR_SHAPE;
   if (!ws || ws_bytes < tbik_logsoftmax_workspace_bytes(M, V, tp)) return TBIK_ERR_WORKSPACE;
@@ -206,8 +241,7 @@ int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf1
   if (Lq < 0 || Lk < 1 || Lk > 65536 || batch < 0 || batch > 65535 || offset < 0)
     return TBIK_ERR_SHAPE;
   if (ld_s < Lk || ld_p < Lk || stride_s < 0 || stride_p < 0) return TBIK_ERR_SHAPE;
-  if (!ld_ok(ld_s) || !ld_ok(ld_p) || (stride_s % 8) || (stride_p % 8)) return TBIK_ERR_ALIGN;
-  if (!aligned16(S) || !aligned16(P)) return TBIK_ERR_ALIGN;
+  if (!aligned(S, 4) || !aligned(P, 2)) return TBIK_ERR_ALIGN;
   if (!isfinite(scale)) return TBIK_ERR_ARG;
   if (Lq == 0 || batch == 0) return TBIK_OK;
   return tbik::launch_softmax_causal(S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, batch, offset,

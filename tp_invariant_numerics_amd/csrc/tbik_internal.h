@@ -15,6 +15,11 @@ struct GemmCall {
   int M, N, K, batch;
   int parts;             // K split into `parts` tree nodes (1 = the root)
   int leaf_mode;         // 0 MFMA, 1 scalar
+  // When shard_of > 0 the K columns given are one shard of a tree over
+  // tree_leaves leaves split into shard_of shards: the launch computes that
+  // shard's node (its T/shard_of groups) and parts must be 1.
+  int tree_leaves;
+  int shard_of;
 };
 
 // Returns 0 or a TBIK_ERR_* code.
