@@ -190,6 +190,196 @@ k_gemm_mfma(GemmArgs p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-tile kernel: LDS ring fed by direct global->LDS loads.
+//
+// A workgroup of WAVES_M x WAVES_N waves owns an MT x NT output tile
+// (MT = 16*WM*WAVES_M, NT = 16*WN*WAVES_N) and the whole K range of its part.
+// Each 64-wide K block of A and W ("stage", (MT+NT)*128 bytes) is fetched once
+// per workgroup with global_load_lds_dwordx4 into a ring of S LDS slots, S-1
+// stages ahead of the MFMAs.  Inside a slot, row r's eight 16-byte chunks
+// are stored XOR-swizzled (chunk c at position c ^ (r & 7)), so both the
+// copy (one 8-row, 1 KB segment per wave instruction) and the MFMA fragment
+// reads are free of bank conflicts.  Synchronisation is a wave-local wait on
+// the vector-memory counter for the slot's own loads plus one s_barrier per
+// K block; no fence is needed because the loads write LDS directly.
+//
+// The tree is the same as in k_gemm_mfma.  Leaves are taken in unrolled
+// blocks of U (U | G): inside a block every merge is resolved at compile time
+// and the merge of leaf j-1 is issued after the MFMAs of leaf j (two leaf
+// accumulators), letting the VALU adds overlap the matrix unit.
+//
+// Tiles are numbered so that each XCD (workgroups are dealt to the 8 XCDs
+// round-robin) receives a contiguous range, walked in groups of GROUP_M row
+// tiles so that concurrently running tiles share A and W in that XCD's L2.
+// ---------------------------------------------------------------------------
+struct TileMap {
+  int tiles_m, tiles_n, parts, group_m;
+};
+
+__device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
+  const int q = nblocks >> 3, r = nblocks & 7;
+  const int x = bid & 7, j = bid >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
+}
+
+typedef const void __attribute__((address_space(1))) *gptr_t;
+typedef void __attribute__((address_space(3))) *lptr_t;
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] = 7, lgkmcnt [11:8] = 15).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int U, int GD, int TD>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+k_gemm_ring(GemmArgs p, TileMap tm) {
+  constexpr int WAVES = WAVES_M * WAVES_N;
+  constexpr int MT = 16 * WM * WAVES_M;
+  constexpr int NT = 16 * WN * WAVES_N;
+  constexpr int R = 4 * WM * WN;
+  constexpr int SEGA = MT / 8, SEGB = NT / 8;      // 1 KB segments per stage
+  constexpr int SEG = SEGA + SEGB;
+  static_assert(SEG % WAVES == 0, "segments must split evenly over waves");
+  constexpr int DPW = SEG / WAVES;                  // loads per wave per stage
+  constexpr int SLOT = SEG * 64;                    // 16-byte units per slot
+  __shared__ u32x4 ring[S * SLOT];
+
+  // ---- tile of this workgroup
+  const int nblocks = tm.tiles_m * tm.tiles_n * tm.parts;
+  int id = xcd_logical(blockIdx.x, nblocks);
+  const int per_part = tm.tiles_m * tm.tiles_n;
+  const int part = id / per_part;
+  id -= part * per_part;
+  const int span = tm.group_m * tm.tiles_n;
+  const int grp = id / span;
+  const int first_m = grp * tm.group_m;
+  const int gsz = min(tm.tiles_m - first_m, tm.group_m);
+  const int tile_m = first_m + (id - grp * span) % gsz;
+  const int tile_n = (id - grp * span) / gsz;
+  const int m0 = tile_m * MT, n0 = tile_n * NT;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
+  const int G = p.G;
+  const int gpp = p.gpp;
+  const int nleaf = gpp * G;
+  const int64_t kbase = (int64_t)part * gpp * G * 64;
+
+  // ---- this lane's source for each of its wave's DPW segments
+  const uint16_t *src[DPW];
+  int dst[DPW];
+#pragma unroll
+  for (int i = 0; i < DPW; ++i) {
+    const int seg = wave + WAVES * i;
+    const int rin = lane >> 3;                       // row inside the segment
+    const int c = (lane & 7) ^ rin;                  // logical chunk at this position
+    if (seg < SEGA) {
+      int row = m0 + seg * 8 + rin;
+      row = row < p.M ? row : p.M - 1;
+      src[i] = p.A + (int64_t)row * p.lda + kbase + 8 * c;
+    } else {
+      int row = n0 + (seg - SEGA) * 8 + rin;
+      row = row < p.N ? row : p.N - 1;
+      src[i] = p.W + (int64_t)row * p.ldw + kbase + 8 * c;
+    }
+    dst[i] = seg * 64;                               // segment base (16-byte units)
+  }
+  // ---- fragment offsets inside a slot (16-byte units)
+  int fa[WM][2], fb[WN][2];
+#pragma unroll
+  for (int b = 0; b < WM; ++b) {
+    const int row = wm * 16 * WM + 16 * b + (lane & 15);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fa[b][h] = row * 8 + ((4 * h + (lane >> 4)) ^ (row & 7));
+  }
+#pragma unroll
+  for (int b = 0; b < WN; ++b) {
+    const int row = MT + wn * 16 * WN + 16 * b + (lane & 15);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) fb[b][h] = row * 8 + ((4 * h + (lane >> 4)) ^ (row & 7));
+  }
+
+  // issue the loads of stage `st` (clamped to the last stage: the surplus
+  // loads at the end refill a slot that is never read again)
+  auto issue = [&](int st) {
+    const int sc = st < nleaf ? st : nleaf - 1;
+    const int slot = st % S;
+#pragma unroll
+    for (int i = 0; i < DPW; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + (int64_t)sc * 64),
+                                       (lptr_t)(ring + slot * SLOT + dst[i]), 16, 0, 0);
+  };
+  auto mfma_leaf = [&](float (&acc)[R], int st) {
+    const u32x4 *sl = ring + (st % S) * SLOT;
+    u32x4 a[WM][2], b[WN][2];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) { a[i][0] = sl[fa[i][0]]; a[i][1] = sl[fa[i][1]]; }
+#pragma unroll
+    for (int i = 0; i < WN; ++i) { b[i][0] = sl[fb[i][0]]; b[i][1] = sl[fb[i][1]]; }
+    leaf_mfma<WM, WN>(acc, a, b);
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; ++st) issue(st);
+
+  // Leaves are processed in blocks of U (U divides G, so the lowest log2(U)
+  // levels of PAIR inside a group are perfect trees over exactly these
+  // blocks).  Inside a block every merge is static and the merge of leaf
+  // j-1 follows the MFMAs of leaf j; block sums go through the runtime
+  // stack `s` (PAIR over the G/U blocks of a group), group sums through `top`.
+  constexpr int LU = U >= 8 ? 3 : U >= 4 ? 2 : U >= 2 ? 1 : 0;
+  float s[GD > 0 ? GD : 1][R];
+  float top[TD > 0 ? TD : 1][R];
+  float node[R];
+  const int nblk = G / U;
+  int l = 0;
+  for (int gi = 0; gi < gpp; ++gi) {
+    for (int cb = 0; cb < nblk; ++cb) {
+      float acc[2][R];
+      float q[LU > 0 ? LU : 1][R];
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        wait_vmcnt<DPW * (S - 2)>();
+        __builtin_amdgcn_s_barrier();
+        issue(l + S - 1);
+        mfma_leaf(acc[j & 1], l);
+        if (j > 0) pair_push<R, LU>(q, acc[(j - 1) & 1], j - 1, U);
+        ++l;
+      }
+      pair_push<R, LU>(q, acc[(U - 1) & 1], U - 1, U);
+#pragma unroll
+      for (int r = 0; r < R; ++r) node[r] = acc[(U - 1) & 1][r];
+      if (pair_push<R, GD>(s, node, cb, nblk)) pair_push<R, TD>(top, node, gi, gpp);
+    }
+  }
+  wait_vmcnt<0>();     // no load into LDS may outlive the workgroup
+
+  float *Cp = p.C ? p.C + (int64_t)part * p.part_stride : nullptr;
+  uint16_t *Cbp = p.Cb;
+  const int orow = 4 * (lane >> 4);
+#pragma unroll
+  for (int bm = 0; bm < WM; ++bm) {
+#pragma unroll
+    for (int bn = 0; bn < WN; ++bn) {
+      const int col = n0 + wn * 16 * WN + 16 * bn + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = m0 + wm * 16 * WM + 16 * bm + orow + i;
+        if (row < p.M && col < p.N) {
+          const float v = node[(bm * WN + bn) * 4 + i];
+          const int64_t o = (int64_t)row * p.ldc + col;
+          if (Cp) Cp[o] = v;
+          if (Cbp) Cbp[o] = f2bf(v);
+        }
+      }
+    }
+  }
+}
+
 // Scalar leaves: one thread per output, 64 sequential fma per leaf in
 // increasing k; the same tree.  Bit-exact with the CPU oracle.
 __global__ void __launch_bounds__(64) k_gemm_scalar(GemmArgs p) {
@@ -276,6 +466,58 @@ static int launch_big(const GemmArgs &a, int batch, hipStream_t s) {
   return TBIK_ERR_ARG;
 }
 
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int U, int GD, int TD>
+static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
+  constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
+  TileMap tm;
+  tm.tiles_m = (a.M + MT - 1) / MT;
+  tm.tiles_n = (a.N + NT - 1) / NT;
+  tm.parts = a.parts;
+  tm.group_m = 8;
+  const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * tm.parts;
+  if (nb > 0x7fffffff) return TBIK_ERR_SHAPE;
+  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, U, GD, TD>), dim3((unsigned)nb),
+                     dim3(64 * WAVES_M * WAVES_N), 0, s, a, tm);
+  return check_launch();
+}
+
+// 128 x 64 tiles: 4 waves of 32 x 64 stacked along M; 4-stage ring (96 KB).
+template <int U, int GD>
+static int launch_ring_u(const GemmArgs &a, hipStream_t s) {
+  switch (a.gpp) {
+    case 1: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 0>(a, s);
+    case 2: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 1>(a, s);
+    case 4: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 2>(a, s);
+    case 8: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 3>(a, s);
+  }
+  return TBIK_ERR_ARG;
+}
+
+// Block size U: the largest of 8, 4, 1 dividing G.  Stack depth for the
+// PAIR over the G/U blocks: bit length of G/U - 1.
+static bool ring_supported(int G) {
+  const int U = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : 1;
+  return bit_length(G / U - 1) <= (U == 1 ? 5 : 3);
+}
+
+static int launch_ring(const GemmArgs &a, hipStream_t s) {
+  const int G = a.G;
+  if (G % 8 == 0) {
+    const int need = bit_length(G / 8 - 1);
+    if (need == 0) return launch_ring_u<8, 0>(a, s);
+    if (need <= 3) return launch_ring_u<8, 3>(a, s);
+  }
+  if (G % 4 == 0) {
+    const int need = bit_length(G / 4 - 1);
+    if (need == 0) return launch_ring_u<4, 0>(a, s);
+    if (need <= 3) return launch_ring_u<4, 3>(a, s);
+  }
+  const int need = bit_length(G - 1);
+  if (need <= 3) return launch_ring_u<1, 3>(a, s);
+  if (need <= 5) return launch_ring_u<1, 5>(a, s);
+  return TBIK_ERR_ARG;
+}
+
 // Small M: one wave per group of the part, combined in LDS.
 template <int WM, int GD>
 static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
@@ -309,6 +551,7 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
     return check_launch();
   }
   const int need = bit_length(a.G - 1);
+  if (c.M > 32 && c.batch == 1 && ring_supported(a.G)) return launch_ring(a, s);
   if (c.M > 32 && need <= 5) {
     return need <= 3 ? launch_big<4, 3>(a, c.batch, s) : launch_big<2, 5>(a, c.batch, s);
   }
