@@ -55,6 +55,12 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
+    # every kernel launched from host code must have its stub in the library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [ln.split()[-1] for ln in nm.stdout.splitlines() if "_ZN4tbik" in ln]
+    if missing:
+        os.unlink(tmp)
+        raise RuntimeError("libtbik.so has undefined kernel symbols: %s" % missing[:4])
     os.replace(tmp, LIB)
     return LIB
 

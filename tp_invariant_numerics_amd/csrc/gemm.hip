@@ -24,6 +24,40 @@
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
 
+// Ring geometry: RING_WM x RING_WN 16x16 blocks per wave, 4 waves stacked
+// along M, RING_S stages.
+#ifndef TBIK_RING_WM
+#define TBIK_RING_WM 2
+#endif
+#ifndef TBIK_RING_WN
+#define TBIK_RING_WN 4
+#endif
+#ifndef TBIK_RING_S
+#define TBIK_RING_S 4
+#endif
+#ifndef TBIK_RING_WAVES_M
+#define TBIK_RING_WAVES_M 4
+#endif
+#ifndef TBIK_RING_WAVES_N
+#define TBIK_RING_WAVES_N 1
+#endif
+// wide (128 x 128) tiles where the tree state fits
+#ifndef TBIK_RING_WIDE
+#define TBIK_RING_WIDE 1
+#endif
+// leaf accumulators per wave: 3 lets a leaf's merge overlap the next leaf's
+// MFMAs, 2 saves one register tile
+#ifndef TBIK_RING_NX
+#define TBIK_RING_NX 3
+#endif
+// cache-policy bits of the ring's loads of A and of W (2 = non-temporal)
+#ifndef TBIK_RING_AUX_A
+#define TBIK_RING_AUX_A 0
+#endif
+#ifndef TBIK_RING_AUX_B
+#define TBIK_RING_AUX_B 0
+#endif
+
 namespace tbik {
 
 struct GemmArgs {
@@ -223,6 +257,15 @@ __device__ __forceinline__ int xcd_logical(int bid, int nblocks) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + j;
 }
 
+// Barrier for the LDS ring: this wave's LDS reads are complete
+// (lgkmcnt(0)) before it arrives, and the memory clobber keeps the compiler
+// from moving LDS reads of a slot past the barrier after which that slot is
+// refilled.  Unlike __syncthreads() it does not wait for outstanding global
+// loads, so the ring's prefetches stay in flight.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 typedef const void __attribute__((address_space(1))) *gptr_t;
 typedef void __attribute__((address_space(3))) *lptr_t;
 
@@ -234,19 +277,198 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int U, int GD, int TD>
+// Static merge schedule of one block of U leaves (U in {2,4,8}), leaf j in
+// accumulator X[j % 3].  merge_leaf<j>() runs after the MFMAs of leaf j+1
+// were issued (for j < U-1), so its adds can overlap them; every add writes
+// its final destination (pair level P1, quad level P2), so no copies are
+// needed.  The value returned by the merge of leaf U-1 is the block's PAIR
+// (a perfect tree over the U leaves).
+template <int R, int NX>
+struct BlockTree {
+  float X[NX][R];
+  float P1[R];
+  float P2[R];
+};
+
+template <int U, int J, int R, int NX>
+__device__ __forceinline__ void merge_leaf(BlockTree<R, NX> &t, float (&out)[R]) {
+  static_assert(U == 2 || U == 4 || U == 8, "block size");
+  if constexpr ((J & 1) == 0) {
+    return;                                     // waits for its sibling leaf
+  } else {
+    float(&a)[R] = t.X[(J - 1) % NX];
+    float(&b)[R] = t.X[J % NX];
+    constexpr int pairs = (J + 1) / 2;          // pairs completed so far
+    if constexpr (U == 2) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) out[r] = a[r] + b[r];
+    } else if constexpr (pairs & 1) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) t.P1[r] = a[r] + b[r];
+    } else {
+      float q[R];
+#pragma unroll
+      for (int r = 0; r < R; ++r) q[r] = t.P1[r] + (a[r] + b[r]);
+      if constexpr (U == 4) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) out[r] = q[r];
+      } else if constexpr ((pairs / 2) & 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) t.P2[r] = q[r];
+      } else {
+#pragma unroll
+        for (int r = 0; r < R; ++r) out[r] = t.P2[r] + q[r];
+      }
+    }
+  }
+}
+
+constexpr int cbit_length(int v) { return v > 0 ? 1 + cbit_length(v >> 1) : 0; }
+
+// Everything one wave of k_gemm_ring needs to stream leaves through the ring
+// and merge them, plus the compile-time schedules of the tree.
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX>
+struct Ring {
+  static constexpr int WAVES = WAVES_M * WAVES_N;
+  static constexpr int MT = 16 * WM * WAVES_M;
+  static constexpr int NT = 16 * WN * WAVES_N;
+  static constexpr int R = 4 * WM * WN;
+  static constexpr int SEGA = MT / 8, SEGB = NT / 8;     // 1 KB segments per stage
+  static constexpr int SEG = SEGA + SEGB;
+  static_assert(SEGA % WAVES == 0 && SEGB % WAVES == 0, "segments must split evenly");
+  static constexpr int DPW = SEG / WAVES;                 // loads per wave per stage
+  static constexpr int DPA = SEGA / WAVES;                // of which from A
+  static constexpr int SLOT = SEG * 64;                   // 16-byte units per slot
+
+  u32x4 *ring;
+  __amdgpu_buffer_rsrc_t rsa, rsb;
+  unsigned voff[DPW];
+  int fa0[2], fb0[2];
+  int wave, nleaf, l;
+  int64_t kbase;
+
+  __device__ __forceinline__ void issue(int st, int slot) {
+    const int sc = st < nleaf ? st : nleaf - 1;
+    const int soff = (int)((kbase + (int64_t)sc * 64) * 2);
+#pragma unroll
+    for (int i = 0; i < DPA; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsa, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
+          TBIK_RING_AUX_A);
+#pragma unroll
+    for (int i = DPA; i < DPW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rsb, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
+          TBIK_RING_AUX_B);
+  }
+
+  __device__ __forceinline__ void mfma_leaf(float (&acc)[R], int slot) {
+    const u32x4 *sl = ring + slot * SLOT;
+    u32x4 a[WM][2], b[WN][2];
+#pragma unroll
+    for (int i = 0; i < WM; ++i) {
+      a[i][0] = sl[fa0[0] + 128 * i];
+      a[i][1] = sl[fa0[1] + 128 * i];
+    }
+#pragma unroll
+    for (int i = 0; i < WN; ++i) {
+      b[i][0] = sl[fb0[0] + 128 * i];
+      b[i][1] = sl[fb0[1] + 128 * i];
+    }
+    leaf_mfma<WM, WN>(acc, a, b);
+  }
+
+  // One leaf: wait for its stage, refill the slot freed by the previous
+  // leaf, then the MFMAs.  `slot_static` >= 0 when the slot is known at
+  // compile time (the block started at a multiple of S).
+  __device__ __forceinline__ void step(float (&acc)[R], int j, bool static_slot) {
+    // keep the scheduler inside one leaf: unbounded interleaving across a
+    // fully unrolled group raises register pressure into spills
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<DPW * (S - 2)>();
+    ring_barrier();
+    if (static_slot) {
+      issue(l + j + S - 1, (j + S - 1) % S);
+      mfma_leaf(acc, j % S);
+    } else {
+      issue(l + j + S - 1, (unsigned)(l + j + S - 1) % S);
+      mfma_leaf(acc, (unsigned)(l + j) % S);
+    }
+  }
+
+  // Perfect tree over the next U leaves (U in {1,2,4,8}), merges resolved at
+  // compile time; with NX == 3 the merge of leaf j-1 follows the MFMAs of
+  // leaf j.  Advances l by U.
+  template <int U>
+  __device__ __forceinline__ void block(float (&out)[R]) {
+    if constexpr (U == 1) {
+      step(out, 0, false);
+      l += 1;
+    } else {
+      constexpr bool SS = (U % S) == 0;
+      BlockTree<R, NX> bt;
+#define TBIK_LEAF_STEP(J)                                                    \
+  if constexpr ((J) < U) {                                                   \
+    if constexpr (NX == 2 && (J) > 0) merge_leaf<U, (J) - 1, R, NX>(bt, out); \
+    step(bt.X[(J) % NX], (J), SS);                                           \
+    if constexpr (NX == 3 && (J) > 0) merge_leaf<U, (J) - 1, R, NX>(bt, out); \
+  }
+      TBIK_LEAF_STEP(0) TBIK_LEAF_STEP(1) TBIK_LEAF_STEP(2) TBIK_LEAF_STEP(3)
+      TBIK_LEAF_STEP(4) TBIK_LEAF_STEP(5) TBIK_LEAF_STEP(6) TBIK_LEAF_STEP(7)
+#undef TBIK_LEAF_STEP
+      merge_leaf<U, U - 1, R, NX>(bt, out);
+      l += U;
+    }
+  }
+
+  // Perfect tree over N leaves (N a power of two): halves recursively,
+  // blocks of at most 8 leaves at the bottom.
+  template <int N>
+  __device__ __forceinline__ void perfect(float (&out)[R]) {
+    if constexpr (N <= 8) {
+      block<N>(out);
+    } else {
+      float left[R];
+      perfect<N / 2>(left);
+      perfect<N / 2>(out);
+#pragma unroll
+      for (int r = 0; r < R; ++r) out[r] = left[r] + out[r];
+    }
+  }
+
+  // PAIR over N leaves: the perfect tree over the largest power-of-two
+  // prefix, added to PAIR over the rest (an odd tail moves up unchanged, so
+  // PAIR is this right fold of its binary decomposition).
+  template <int N>
+  __device__ __forceinline__ void pair(float (&out)[R]) {
+    constexpr int H = (N >= 256) ? 256 : (N >= 128) ? 128 : (N >= 64) ? 64 : (N >= 32) ? 32
+                    : (N >= 16) ? 16 : (N >= 8) ? 8 : (N >= 4) ? 4 : (N >= 2) ? 2 : 1;
+    if constexpr (H == N) {
+      perfect<N>(out);
+    } else {
+      float left[R];
+      perfect<H>(left);
+      pair<N - H>(out);
+#pragma unroll
+      for (int r = 0; r < R; ++r) out[r] = left[r] + out[r];
+    }
+  }
+};
+
+// GS > 0: the group size G is the compile-time constant GS and each group
+// is evaluated by Ring::pair<GS>.  GS == 0: runtime G, blocks of U leaves
+// pushed through a binary-counter stack of depth GD.  TD: stack depth over
+// the groups of one part.
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, int GS, int U, int GD, int TD>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 k_gemm_ring(GemmArgs p, TileMap tm) {
-  constexpr int WAVES = WAVES_M * WAVES_N;
-  constexpr int MT = 16 * WM * WAVES_M;
-  constexpr int NT = 16 * WN * WAVES_N;
-  constexpr int R = 4 * WM * WN;
-  constexpr int SEGA = MT / 8, SEGB = NT / 8;      // 1 KB segments per stage
-  constexpr int SEG = SEGA + SEGB;
-  static_assert(SEG % WAVES == 0, "segments must split evenly over waves");
-  constexpr int DPW = SEG / WAVES;                  // loads per wave per stage
-  constexpr int SLOT = SEG * 64;                    // 16-byte units per slot
-  __shared__ u32x4 ring[S * SLOT];
+  // The body uses buffer-resource builtins that only exist for the device;
+  // the host compilation pass only needs the launch stub.
+#if defined(__HIP_DEVICE_COMPILE__)
+  using RG = Ring<WM, WN, WAVES_M, WAVES_N, S, NX>;
+  constexpr int MT = RG::MT, NT = RG::NT, R = RG::R, WAVES = RG::WAVES;
+  constexpr int DPW = RG::DPW, DPA = RG::DPA, SEGA = RG::SEGA;
+  __shared__ u32x4 ring[S * RG::SLOT];
 
   // ---- tile of this workgroup
   const int nblocks = tm.tiles_m * tm.tiles_n * tm.parts;
@@ -262,99 +484,79 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   const int tile_n = (id - grp * span) / gsz;
   const int m0 = tile_m * MT, n0 = tile_n * NT;
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  RG rg;
+  rg.ring = ring;
+  rg.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = rg.wave;
   const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
-  const int G = p.G;
+  const int G = GS > 0 ? GS : p.G;
   const int gpp = p.gpp;
-  const int nleaf = gpp * G;
-  const int64_t kbase = (int64_t)part * gpp * G * 64;
+  rg.nleaf = gpp * G;
+  rg.kbase = (int64_t)part * gpp * G * 64;
+  rg.l = 0;
 
-  // ---- this lane's source for each of its wave's DPW segments
-  const uint16_t *src[DPW];
-  int dst[DPW];
+  // ---- buffer resources over this tile's rows (rows past the end are
+  //      clamped to the last row, so every access stays inside)
+  const int arows = min(MT, p.M - m0), brows = min(NT, p.N - n0);
+  rg.rsa = __builtin_amdgcn_make_buffer_rsrc((void *)(p.A + (int64_t)m0 * p.lda), (short)0,
+                                             (int)((int64_t)arows * p.lda * 2), 0x00020000);
+  rg.rsb = __builtin_amdgcn_make_buffer_rsrc((void *)(p.W + (int64_t)n0 * p.ldw), (short)0,
+                                             (int)((int64_t)brows * p.ldw * 2), 0x00020000);
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int seg = wave + WAVES * i;
-    const int rin = lane >> 3;                       // row inside the segment
+    const int rin = lane >> 3;
     const int c = (lane & 7) ^ rin;                  // logical chunk at this position
-    if (seg < SEGA) {
-      int row = m0 + seg * 8 + rin;
-      row = row < p.M ? row : p.M - 1;
-      src[i] = p.A + (int64_t)row * p.lda + kbase + 8 * c;
+    if (i < DPA) {
+      const int row = min(seg * 8 + rin, arows - 1);
+      rg.voff[i] = (unsigned)(((int64_t)row * p.lda + 8 * c) * 2);
     } else {
-      int row = n0 + (seg - SEGA) * 8 + rin;
-      row = row < p.N ? row : p.N - 1;
-      src[i] = p.W + (int64_t)row * p.ldw + kbase + 8 * c;
+      const int row = min((seg - SEGA) * 8 + rin, brows - 1);
+      rg.voff[i] = (unsigned)(((int64_t)row * p.ldw + 8 * c) * 2);
     }
-    dst[i] = seg * 64;                               // segment base (16-byte units)
   }
-  // ---- fragment offsets inside a slot (16-byte units)
-  int fa[WM][2], fb[WN][2];
+  // ---- fragment bases (16-byte units) inside slot 0; the row's low three
+  //      bits equal lane & 7, so the swizzle only depends on the lane
+  const int lr = lane & 15, lg = lane >> 4;
 #pragma unroll
-  for (int b = 0; b < WM; ++b) {
-    const int row = wm * 16 * WM + 16 * b + (lane & 15);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) fa[b][h] = row * 8 + ((4 * h + (lane >> 4)) ^ (row & 7));
-  }
-#pragma unroll
-  for (int b = 0; b < WN; ++b) {
-    const int row = MT + wn * 16 * WN + 16 * b + (lane & 15);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) fb[b][h] = row * 8 + ((4 * h + (lane >> 4)) ^ (row & 7));
+  for (int h = 0; h < 2; ++h) {
+    rg.fa0[h] = (wm * 16 * WM + lr) * 8 + ((4 * h + lg) ^ (lr & 7));
+    rg.fb0[h] = (MT + wn * 16 * WN + lr) * 8 + ((4 * h + lg) ^ (lr & 7));
   }
 
-  // issue the loads of stage `st` (clamped to the last stage: the surplus
-  // loads at the end refill a slot that is never read again)
-  auto issue = [&](int st) {
-    const int sc = st < nleaf ? st : nleaf - 1;
-    const int slot = st % S;
 #pragma unroll
-    for (int i = 0; i < DPW; ++i)
-      __builtin_amdgcn_global_load_lds((gptr_t)(src[i] + (int64_t)sc * 64),
-                                       (lptr_t)(ring + slot * SLOT + dst[i]), 16, 0, 0);
-  };
-  auto mfma_leaf = [&](float (&acc)[R], int st) {
-    const u32x4 *sl = ring + (st % S) * SLOT;
-    u32x4 a[WM][2], b[WN][2];
-#pragma unroll
-    for (int i = 0; i < WM; ++i) { a[i][0] = sl[fa[i][0]]; a[i][1] = sl[fa[i][1]]; }
-#pragma unroll
-    for (int i = 0; i < WN; ++i) { b[i][0] = sl[fb[i][0]]; b[i][1] = sl[fb[i][1]]; }
-    leaf_mfma<WM, WN>(acc, a, b);
-  };
+  for (int st = 0; st < S - 1; ++st) rg.issue(st, st);
 
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st) issue(st);
-
-  // Leaves are processed in blocks of U (U divides G, so the lowest log2(U)
-  // levels of PAIR inside a group are perfect trees over exactly these
-  // blocks).  Inside a block every merge is static and the merge of leaf
-  // j-1 follows the MFMAs of leaf j; block sums go through the runtime
-  // stack `s` (PAIR over the G/U blocks of a group), group sums through `top`.
-  constexpr int LU = U >= 8 ? 3 : U >= 4 ? 2 : U >= 2 ? 1 : 0;
-  float s[GD > 0 ? GD : 1][R];
   float top[TD > 0 ? TD : 1][R];
   float node[R];
-  const int nblk = G / U;
-  int l = 0;
-  for (int gi = 0; gi < gpp; ++gi) {
-    for (int cb = 0; cb < nblk; ++cb) {
-      float acc[2][R];
-      float q[LU > 0 ? LU : 1][R];
-#pragma unroll
-      for (int j = 0; j < U; ++j) {
-        wait_vmcnt<DPW * (S - 2)>();
-        __builtin_amdgcn_s_barrier();
-        issue(l + S - 1);
-        mfma_leaf(acc[j & 1], l);
-        if (j > 0) pair_push<R, LU>(q, acc[(j - 1) & 1], j - 1, U);
-        ++l;
+  const int ngroups = gpp;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    if constexpr (GS > 0) {
+      // Full 8-leaf blocks (perfect subtrees, aligned in the group) in a
+      // loop, then the static tail of GS % 8 leaves; PAIR over the group is
+      // PAIR over these block values, the tail's PAIR being the last item.
+      constexpr int NB = GS / 8, TAIL = GS % 8, NI = NB + (TAIL ? 1 : 0);
+      constexpr int ID = cbit_length(NI - 1);
+      float st[ID > 0 ? ID : 1][R];
+#pragma clang loop unroll(disable)
+      for (int b = 0; b < NB; ++b) {
+        rg.template block<8>(node);
+        pair_push<R, ID>(st, node, b, NI);
       }
-      pair_push<R, LU>(q, acc[(U - 1) & 1], U - 1, U);
-#pragma unroll
-      for (int r = 0; r < R; ++r) node[r] = acc[(U - 1) & 1][r];
-      if (pair_push<R, GD>(s, node, cb, nblk)) pair_push<R, TD>(top, node, gi, gpp);
+      if constexpr (TAIL > 0) {
+        rg.template pair<TAIL>(node);
+        pair_push<R, ID>(st, node, NB, NI);
+      }
+    } else {
+      float s[GD > 0 ? GD : 1][R];
+      const int nblk = G / U;
+      for (int cb = 0; cb < nblk; ++cb) {
+        rg.template block<U>(node);
+        pair_push<R, GD>(s, node, cb, nblk);
+      }
     }
+    pair_push<R, TD>(top, node, gi, gpp);
   }
   wait_vmcnt<0>();     // no load into LDS may outlive the workgroup
 
@@ -378,6 +580,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
       }
     }
   }
+#endif
 }
 
 // Scalar leaves: one thread per output, 64 sequential fma per leaf in
@@ -466,7 +669,7 @@ static int launch_big(const GemmArgs &a, int batch, hipStream_t s) {
   return TBIK_ERR_ARG;
 }
 
-template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int U, int GD, int TD>
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, int GS, int U, int GD, int TD>
 static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
   TileMap tm;
@@ -476,45 +679,71 @@ static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   tm.group_m = 8;
   const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * tm.parts;
   if (nb > 0x7fffffff) return TBIK_ERR_SHAPE;
-  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, U, GD, TD>), dim3((unsigned)nb),
-                     dim3(64 * WAVES_M * WAVES_N), 0, s, a, tm);
+  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, GS, U, GD, TD>),
+                     dim3((unsigned)nb), dim3(64 * WAVES_M * WAVES_N), 0, s, a, tm);
   return check_launch();
 }
 
-// 128 x 64 tiles: 4 waves of 32 x 64 stacked along M; 4-stage ring (96 KB).
-template <int U, int GD>
-static int launch_ring_u(const GemmArgs &a, hipStream_t s) {
+// Tile geometries: "narrow" 128 x 64 (4 waves of 32 x 64 along M, three
+// leaf accumulators) and "wide" 128 x 128 (2 x 2 waves of 64 x 64, two leaf
+// accumulators) -- the wide tile moves a third less data per MFMA but only
+// fits when the tree's live state is small.
+template <int GS, int U, int GD, int TD>
+static int launch_narrow(const GemmArgs &a, hipStream_t s) {
+  return launch_ring_cfg<TBIK_RING_WM, TBIK_RING_WN, TBIK_RING_WAVES_M, TBIK_RING_WAVES_N,
+                         TBIK_RING_S, TBIK_RING_NX, GS, U, GD, TD>(a, s);
+}
+template <int GS, int TD>
+static int launch_wide(const GemmArgs &a, hipStream_t s) {
+  return launch_ring_cfg<4, 4, 2, 2, 4, 2, GS, 1, 0, TD>(a, s);
+}
+
+template <int GS, int U, int GD>
+static int launch_narrow_td(const GemmArgs &a, hipStream_t s) {
   switch (a.gpp) {
-    case 1: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 0>(a, s);
-    case 2: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 1>(a, s);
-    case 4: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 2>(a, s);
-    case 8: return launch_ring_cfg<2, 4, 4, 1, 4, U, GD, 3>(a, s);
+    case 1:
+    case 2: return launch_narrow<GS, U, GD, 1>(a, s);
+    case 4: return launch_narrow<GS, U, GD, 2>(a, s);
+    case 8: return launch_narrow<GS, U, GD, 3>(a, s);
   }
   return TBIK_ERR_ARG;
 }
 
-// Block size U: the largest of 8, 4, 1 dividing G.  Stack depth for the
-// PAIR over the G/U blocks: bit length of G/U - 1.
-static bool ring_supported(int G) {
+static bool ring_supported_g(int G) {
+  if (G == 28 || G == 8 || G == 4) return true;
   const int U = (G % 8 == 0) ? 8 : (G % 4 == 0) ? 4 : 1;
   return bit_length(G / U - 1) <= (U == 1 ? 5 : 3);
 }
 
 static int launch_ring(const GemmArgs &a, hipStream_t s) {
   const int G = a.G;
-  if (G % 8 == 0) {
-    const int need = bit_length(G / 8 - 1);
-    if (need == 0) return launch_ring_u<8, 0>(a, s);
-    if (need <= 3) return launch_ring_u<8, 3>(a, s);
+#if TBIK_RING_WIDE
+  // wide tiles where the live tree state fits (G = 28 with at most two
+  // groups per part, G = 8 with any number) and there are enough of them to
+  // occupy every CU at least twice
+  const int64_t wide_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.parts;
+  if (wide_tiles >= 512) {
+  // (a stack depth TD >= log2(groups) is valid; TD = 1 for a single group
+  //  allocates registers better than TD = 0)
+  if (G == 28 && a.gpp <= 2) return launch_wide<28, 1>(a, s);
+  if (G == 8) {
+    switch (a.gpp) {
+      case 1:
+      case 2: return launch_wide<8, 1>(a, s);
+      case 4: return launch_wide<8, 2>(a, s);
+      case 8: return launch_wide<8, 3>(a, s);
+    }
   }
-  if (G % 4 == 0) {
-    const int need = bit_length(G / 4 - 1);
-    if (need == 0) return launch_ring_u<4, 0>(a, s);
-    if (need <= 3) return launch_ring_u<4, 3>(a, s);
   }
+#endif
+  if (G == 28) return launch_narrow_td<28, 1, 0>(a, s);
+  if (G == 8) return launch_narrow_td<8, 1, 0>(a, s);
+  if (G == 4) return launch_narrow_td<4, 1, 0>(a, s);
+  if (G % 8 == 0 && bit_length(G / 8 - 1) <= 3) return launch_narrow_td<0, 8, 3>(a, s);
+  if (G % 4 == 0 && bit_length(G / 4 - 1) <= 3) return launch_narrow_td<0, 4, 3>(a, s);
   const int need = bit_length(G - 1);
-  if (need <= 3) return launch_ring_u<1, 3>(a, s);
-  if (need <= 5) return launch_ring_u<1, 5>(a, s);
+  if (need <= 3) return launch_narrow_td<0, 1, 3>(a, s);
+  if (need <= 5) return launch_narrow_td<0, 1, 5>(a, s);
   return TBIK_ERR_ARG;
 }
 
@@ -551,7 +780,9 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
     return check_launch();
   }
   const int need = bit_length(a.G - 1);
-  if (c.M > 32 && c.batch == 1 && ring_supported(a.G)) return launch_ring(a, s);
+  if (c.M > 32 && c.batch == 1 && ring_supported_g(a.G) &&
+      (int64_t)128 * c.lda * 2 < ((int64_t)1 << 31) && (int64_t)128 * c.ldw * 2 < ((int64_t)1 << 31))
+    return launch_ring(a, s);
   if (c.M > 32 && need <= 5) {
     return need <= 3 ? launch_big<4, 3>(a, c.batch, s) : launch_big<2, 5>(a, c.batch, s);
   }
