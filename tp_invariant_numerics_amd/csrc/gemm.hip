@@ -41,6 +41,13 @@
 #ifndef TBIK_RING_WAVES_N
 #define TBIK_RING_WAVES_N 1
 #endif
+// fragment reads one leaf ahead of the MFMAs (narrow / wide tiles)
+#ifndef TBIK_RING_PIPE
+#define TBIK_RING_PIPE 1
+#endif
+#ifndef TBIK_RING_WIDE_PIPE
+#define TBIK_RING_WIDE_PIPE 0
+#endif
 // wide (128 x 128) tiles where the tree state fits
 #ifndef TBIK_RING_WIDE
 #define TBIK_RING_WIDE 1
@@ -327,7 +334,7 @@ constexpr int cbit_length(int v) { return v > 0 ? 1 + cbit_length(v >> 1) : 0; }
 
 // Everything one wave of k_gemm_ring needs to stream leaves through the ring
 // and merge them, plus the compile-time schedules of the tree.
-template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX>
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE>
 struct Ring {
   static constexpr int WAVES = WAVES_M * WAVES_N;
   static constexpr int MT = 16 * WM * WAVES_M;
@@ -362,9 +369,11 @@ struct Ring {
           TBIK_RING_AUX_B);
   }
 
-  __device__ __forceinline__ void mfma_leaf(float (&acc)[R], int slot) {
+  // fragments of the next leaf (PIPE): read one leaf ahead of their MFMAs
+  u32x4 ca[WM][2], cb[WN][2];
+
+  __device__ __forceinline__ void read_frags(u32x4 (&a)[WM][2], u32x4 (&b)[WN][2], int slot) {
     const u32x4 *sl = ring + slot * SLOT;
-    u32x4 a[WM][2], b[WN][2];
 #pragma unroll
     for (int i = 0; i < WM; ++i) {
       a[i][0] = sl[fa0[0] + 128 * i];
@@ -375,7 +384,24 @@ struct Ring {
       b[i][0] = sl[fb0[0] + 128 * i];
       b[i][1] = sl[fb0[1] + 128 * i];
     }
+  }
+
+  __device__ __forceinline__ void mfma_leaf(float (&acc)[R], int slot) {
+    u32x4 a[WM][2], b[WN][2];
+    read_frags(a, b, slot);
     leaf_mfma<WM, WN>(acc, a, b);
+  }
+
+  // Prologue: the first S stages in flight (PIPE) or S-1 (otherwise); with
+  // PIPE, also the first leaf's fragments.
+  __device__ __forceinline__ void prologue() {
+#pragma unroll
+    for (int st = 0; st < (PIPE ? S : S - 1); ++st) issue(st, st);
+    if constexpr (PIPE) {
+      wait_vmcnt<DPW * (S - 1)>();
+      ring_barrier();
+      read_frags(ca, cb, 0);
+    }
   }
 
   // One leaf: wait for its stage, refill the slot freed by the previous
@@ -387,7 +413,24 @@ struct Ring {
     __builtin_amdgcn_sched_barrier(0);
     wait_vmcnt<DPW * (S - 2)>();
     ring_barrier();
-    if (static_slot) {
+    if constexpr (PIPE) {
+      // stage l+j+1 has landed; leaf l+j's slot is free (its fragments are
+      // in ca/cb): refill it with stage l+j+S, read the next leaf's
+      // fragments, then the MFMAs of leaf l+j
+      u32x4 na[WM][2], nb[WN][2];
+      if (static_slot) {
+        issue(l + j + S, j % S);
+        read_frags(na, nb, (j + 1) % S);
+      } else {
+        issue(l + j + S, (unsigned)(l + j) % S);
+        read_frags(na, nb, (unsigned)(l + j + 1) % S);
+      }
+      leaf_mfma<WM, WN>(acc, ca, cb);
+#pragma unroll
+      for (int i = 0; i < WM; ++i) { ca[i][0] = na[i][0]; ca[i][1] = na[i][1]; }
+#pragma unroll
+      for (int i = 0; i < WN; ++i) { cb[i][0] = nb[i][0]; cb[i][1] = nb[i][1]; }
+    } else if (static_slot) {
       issue(l + j + S - 1, (j + S - 1) % S);
       mfma_leaf(acc, j % S);
     } else {
@@ -459,13 +502,14 @@ struct Ring {
 // is evaluated by Ring::pair<GS>.  GS == 0: runtime G, blocks of U leaves
 // pushed through a binary-counter stack of depth GD.  TD: stack depth over
 // the groups of one part.
-template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, int GS, int U, int GD, int TD>
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
+          int TD>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
 k_gemm_ring(GemmArgs p, TileMap tm) {
   // The body uses buffer-resource builtins that only exist for the device;
   // the host compilation pass only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
-  using RG = Ring<WM, WN, WAVES_M, WAVES_N, S, NX>;
+  using RG = Ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE>;
   constexpr int MT = RG::MT, NT = RG::NT, R = RG::R, WAVES = RG::WAVES;
   constexpr int DPW = RG::DPW, DPA = RG::DPA, SEGA = RG::SEGA;
   __shared__ u32x4 ring[S * RG::SLOT];
@@ -525,8 +569,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
     rg.fb0[h] = (MT + wn * 16 * WN + lr) * 8 + ((4 * h + lg) ^ (lr & 7));
   }
 
-#pragma unroll
-  for (int st = 0; st < S - 1; ++st) rg.issue(st, st);
+  rg.prologue();
 
   float top[TD > 0 ? TD : 1][R];
   float node[R];
@@ -669,7 +712,8 @@ static int launch_big(const GemmArgs &a, int batch, hipStream_t s) {
   return TBIK_ERR_ARG;
 }
 
-template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, int GS, int U, int GD, int TD>
+template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
+          int TD>
 static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
   TileMap tm;
@@ -679,7 +723,7 @@ static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   tm.group_m = 8;
   const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * tm.parts;
   if (nb > 0x7fffffff) return TBIK_ERR_SHAPE;
-  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, GS, U, GD, TD>),
+  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE, GS, U, GD, TD>),
                      dim3((unsigned)nb), dim3(64 * WAVES_M * WAVES_N), 0, s, a, tm);
   return check_launch();
 }
@@ -690,12 +734,15 @@ static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
 // fits when the tree's live state is small.
 template <int GS, int U, int GD, int TD>
 static int launch_narrow(const GemmArgs &a, hipStream_t s) {
+  // fragment pipelining only with the compile-time schedules, whose live
+  // state leaves room for the second fragment set
   return launch_ring_cfg<TBIK_RING_WM, TBIK_RING_WN, TBIK_RING_WAVES_M, TBIK_RING_WAVES_N,
-                         TBIK_RING_S, TBIK_RING_NX, GS, U, GD, TD>(a, s);
+                         TBIK_RING_S, TBIK_RING_NX, (TBIK_RING_PIPE != 0 && GS > 0), GS, U, GD, TD>(
+      a, s);
 }
 template <int GS, int TD>
 static int launch_wide(const GemmArgs &a, hipStream_t s) {
-  return launch_ring_cfg<4, 4, 2, 2, 4, 2, GS, 1, 0, TD>(a, s);
+  return launch_ring_cfg<4, 4, 2, 2, 4, 2, TBIK_RING_WIDE_PIPE != 0, GS, 1, 0, TD>(a, s);
 }
 
 template <int GS, int U, int GD>
