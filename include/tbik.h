@@ -219,7 +219,8 @@ int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int 
  *  logits   [M, V] fp32, row stride ld.
  *  targets  [M] int32 in [0, V) (out-of-range targets: out_lp = NaN).
  *  out_lp   [M] fp32.
- *  ws       at least tbik_logsoftmax_workspace_bytes(M, V, tp) bytes.
+ *  ws       at least tbik_logsoftmax_workspace_bytes(M, V, tp) = M*tp*4
+ *           bytes; on return ws[i*tp + t] holds row i's shard-t sum.
  * ---------------------------------------------------------------------- */
 size_t tbik_logsoftmax_workspace_bytes(int M, int V, int tp);
 
@@ -243,9 +244,12 @@ int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf1
 /* ------------------------------------------------------------------------
  * The library's fp32/bf16 primitives applied elementwise (for checking):
  *  op 0: EXP(x)   op 1: LOG(x)   op 2: bf16 round-to-nearest-even of x,
- *  widened back to fp32.   x, y: [n] fp32 device arrays.
+ *  widened back to fp32 (a NaN gives a quiet NaN of unspecified payload)
+ *  op 3: g / (1 + EXP(-g)) with g = bf16(x): the SwiGLU gate activation of
+ *  a bf16 gate, its division correctly rounded.
+ *  x, y: [n] fp32 device arrays.
  * ---------------------------------------------------------------------- */
-enum { TBIK_PRIM_EXP = 0, TBIK_PRIM_LOG = 1, TBIK_PRIM_BF16 = 2 };
+enum { TBIK_PRIM_EXP = 0, TBIK_PRIM_LOG = 1, TBIK_PRIM_BF16 = 2, TBIK_PRIM_SILU = 3 };
 
 int tbik_primitive(int op, const float *x, float *y, int64_t n, void *stream);
 

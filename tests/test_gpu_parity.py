@@ -73,6 +73,40 @@ def test_primitives_bitexact(orc, op):
     assert same_bits(y[~nan], ref[~nan])
 
 
+def test_silu_all_bf16_gates(orc):
+    """The gate activation on every one of the 2^16 bf16 gate values: the
+    oracle's EXP, then IEEE fp32 add and division (numpy float32)."""
+    g = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = orc.bf16_to_f32(g)
+    say("silu all gates", x.size)
+    y = tb.tbik_primitive(tb.PRIM_SILU, torch.from_numpy(x).to(DEV)).cpu().numpy()
+    with np.errstate(all="ignore"):
+        ref = x / (np.float32(1.0) + orc.expf(-x))
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(y), nan)
+    assert same_bits(y[~nan], ref[~nan])
+
+
+def test_bf16_rounding_all_fp32():
+    """fp32 -> bf16 round-to-nearest-even on all 2^32 fp32 patterns, in
+    chunks: exact bits for every non-NaN input (numpy integer arithmetic on
+    the bit pattern is the reference), a quiet NaN of the same sign for a NaN."""
+    chunk = 1 << 28
+    for c in range(1 << 32 >> 28):
+        u = np.arange(c * chunk, (c + 1) * chunk, dtype=np.uint64).astype(np.uint32)
+        say("bf16 all fp32, chunk", c)
+        xd = torch.from_numpy(u.view(np.float32)).to(DEV)
+        y = tb.tbik_primitive(tb.PRIM_BF16, xd).cpu().numpy().view(np.uint32)
+        del xd
+        nan = (u & 0x7FFFFFFF) > 0x7F800000
+        ref = ((u + np.uint32(0x7FFF) + ((u >> 16) & 1)) & np.uint32(0xFFFF0000))
+        assert np.array_equal(y[~nan], ref[~nan])
+        yn = y[nan]
+        assert np.all((yn & 0x7FC00000) == 0x7FC00000)       # quiet NaN
+        assert np.array_equal(yn >> 31, u[nan] >> 31)          # sign kept
+        assert np.all((yn & 0xFFFF) == 0)
+
+
 # ------------------------------------------------------------------ GEMM
 def _gen_gemm(M, N, K, seed, wstd=1.0):
     A = inputs.normal_bf16((M, K), seed)
@@ -229,7 +263,8 @@ def test_gemm_strided_batched_equals_single(orc):
 
 # ------------------------------------------------------------------ RMSNorm
 @pytest.mark.parametrize("rows,H", [(1, 4096), (7, 4096), (256, 4096), (4096, 4096),
-                                    (5, 2048), (3, 5120), (4, 1000), (9, 96), (2, 8), (3, 4104)])
+                                    (5, 2048), (3, 5120), (4, 1000), (9, 96), (2, 8), (3, 4104),
+                                    (3, 64), (2, 512), (2, 16384)])
 def test_rmsnorm_bitexact(orc, rows, H):
     x = inputs.outlier_bf16((rows, H), 8000 + H)
     r = inputs.outlier_bf16((rows, H), 8001 + H)
@@ -282,6 +317,18 @@ def test_swiglu_bitexact(orc, rows, cols):
     say("swiglu", rows, cols)
     y = tb.tbik_swiglu(g.to(DEV), u.to(DEV))
     assert np.array_equal(bits(y), orc.swiglu(bits(g), bits(u)))
+
+
+def test_swiglu_all_bf16_gates(orc):
+    g = inputs.from_bits(np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).reshape(256, 256))
+    u = inputs.normal_bf16(g.shape, 9700)
+    say("swiglu all gates")
+    y = bits(tb.tbik_swiglu(g.to(DEV), u.to(DEV)))
+    ref = orc.swiglu(bits(g), bits(u))
+    nan_y = (y & 0x7FFF) > 0x7F80
+    nan_r = (ref & 0x7FFF) > 0x7F80
+    assert np.array_equal(nan_y, nan_r)
+    assert np.array_equal(y[~nan_r], ref[~nan_r])
 
 
 def test_swiglu_extreme_gates(orc):

@@ -25,7 +25,7 @@ __all__ = [
 
 LEAF_MFMA = 0
 LEAF_SCALAR = 1
-PRIM_EXP, PRIM_LOG, PRIM_BF16 = 0, 1, 2
+PRIM_EXP, PRIM_LOG, PRIM_BF16, PRIM_SILU = 0, 1, 2, 3
 
 _lib = None
 
@@ -310,7 +310,7 @@ def tbik_logsoftmax_gather(logits, targets, tp=1, ws=None, out=None):
 
 def logsoftmax_shard_nodes(ws, M, tp):
     """View of the per-row shard partial sums inside a log-softmax workspace."""
-    return ws[M * 16: M * 16 + M * tp].view(M, tp)
+    return ws[: M * tp].view(M, tp)
 
 
 def tbik_softmax_causal(S, offset, scale, P=None):

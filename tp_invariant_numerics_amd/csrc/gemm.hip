@@ -681,6 +681,34 @@ k_tree_combine(const float *ws, int64_t mn, int N, float *C, uint16_t *Cb, int64
   }
 }
 
+// Four consecutive elements of a row per thread (N % 4 == 0, 16-byte
+// aligned partials and fp32 output rows, 8-byte aligned bf16 rows).
+template <int TP>
+__global__ void __launch_bounds__(256)
+k_tree_combine4(const float *ws, int64_t mn, int N, float *C, uint16_t *Cb, int64_t ldc) {
+  const int64_t n4 = mn / 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += stride) {
+    f32x4 v[TP];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) v[t] = *reinterpret_cast<const f32x4 *>(ws + (int64_t)t * mn + 4 * q);
+#pragma unroll
+    for (int w = TP; w > 1; w >>= 1) {
+#pragma unroll
+      for (int k = 0; k < w / 2; ++k) v[k] = v[2 * k] + v[2 * k + 1];
+    }
+    const int64_t idx = 4 * q;
+    const int64_t row = idx / N, col = idx - row * N;
+    if (C) *reinterpret_cast<f32x4 *>(C + row * ldc + col) = v[0];
+    if (Cb) {
+      u32x2 o;
+      o[0] = pack_bf16(v[0][0], v[0][1]);
+      o[1] = pack_bf16(v[0][2], v[0][3]);
+      *reinterpret_cast<u32x2 *>(Cb + row * ldc + col) = o;
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
@@ -846,6 +874,22 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
 int launch_tree_combine(const float *ws, int tp, float *C, int64_t ldc, uint16_t *Cb, int M,
                         int N, hipStream_t s) {
   const int64_t mn = (int64_t)M * N;
+  const bool vec = (N % 4) == 0 && (ldc % 4) == 0 && ((uintptr_t)ws & 15) == 0 &&
+                   (!C || ((uintptr_t)C & 15) == 0) && (!Cb || ((uintptr_t)Cb & 7) == 0);
+  if (vec) {
+    int64_t blocks = (mn / 4 + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    dim3 grid((unsigned)blocks), block(256);
+    switch (tp) {
+      case 1: hipLaunchKernelGGL(k_tree_combine4<1>, grid, block, 0, s, ws, mn, N, C, Cb, ldc); break;
+      case 2: hipLaunchKernelGGL(k_tree_combine4<2>, grid, block, 0, s, ws, mn, N, C, Cb, ldc); break;
+      case 4: hipLaunchKernelGGL(k_tree_combine4<4>, grid, block, 0, s, ws, mn, N, C, Cb, ldc); break;
+      case 8: hipLaunchKernelGGL(k_tree_combine4<8>, grid, block, 0, s, ws, mn, N, C, Cb, ldc); break;
+      default: return TBIK_ERR_TP;
+    }
+    return check_launch();
+  }
   int64_t blocks = (mn + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   if (blocks < 1) blocks = 1;

@@ -94,14 +94,13 @@ __device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[CH]) {
     for (int q = 0; q < CH / 8; ++q) {
       u32x4 u;
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        u[e] = (uint32_t)f2bf(v[8 * q + 2 * e]) | ((uint32_t)f2bf(v[8 * q + 2 * e + 1]) << 16);
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
       *reinterpret_cast<u32x4 *>(p + 8 * q) = u;
     }
   } else if constexpr (CH == 4) {
     u32x2 u;
-    u[0] = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
-    u[1] = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+    u[0] = pack_bf16(v[0], v[1]);
+    u[1] = pack_bf16(v[2], v[3]);
     *reinterpret_cast<u32x2 *>(p) = u;
   } else {
 #pragma unroll
@@ -198,6 +197,56 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
   }
 }
 
+// Register-resident variant: every thread owns at most one chunk, so h
+// stays in registers between the sum of squares and the output (x and r are
+// read once).  The chunks of one tree group are gc = G/CH consecutive
+// threads, gc a power of two dividing 64, so PAIR over the group's chunk sums
+// is a perfect tree evaluated as a butterfly over those lanes (xor 1, 2, 4,
+// ...; every lane ends with the same bits since IEEE addition commutes).
+// The T group sums meet in LDS for the top perfect tree.
+template <int CH>
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm_reg(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y,
+              uint16_t *r_out, int H, int64_t ld, float eps, int T, int gc) {
+  __shared__ float gsum[8];
+  const int nch = H / CH;
+  const int ch = threadIdx.x;
+  const bool own = ch < nch;
+  const int64_t off = (int64_t)blockIdx.x * ld + (int64_t)ch * CH;
+  float h[CH], ww[CH];
+  float part = 0.0f;
+  if (own) {
+    float b[CH], sq[CH];
+    load_bf16<CH>(h, x + off);
+    load_bf16<CH>(b, r + off);
+    load_bf16<CH>(ww, w + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      h[e] = h[e] + b[e];
+      sq[e] = h[e] * h[e];
+    }
+    if (r_out) store_bf16<CH>(r_out + off, h);
+    part = chunk_tree<CH>(sq);
+  }
+  for (int o = 1; o < gc; o <<= 1) part = part + __shfl_xor(part, o);
+  if (own && (ch & (gc - 1)) == 0) gsum[ch / gc] = part;
+  __syncthreads();
+  float g[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) g[q] = q < T ? gsum[q] : 0.0f;
+  for (int wdt = T; wdt > 1; wdt >>= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < wdt / 2) g[q] = g[2 * q] + g[2 * q + 1];
+  const float mean = g[0] / (float)H;
+  const float rstd = 1.0f / __builtin_sqrtf(mean + eps);
+  if (own) {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) h[e] = (h[e] * rstd) * ww[e];
+    store_bf16<CH>(y + off, h);
+  }
+}
+
 int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
                             uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
                             float eps, hipStream_t s) {
@@ -210,8 +259,19 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
   const int ch = cap_bf16(chunk_for(H / T), al);
   const int nch = H / ch;
   if (nch > 8192) return TBIK_ERR_SHAPE;
-  const size_t lds = 2 * (size_t)nch * sizeof(float);
+  const int gc = nch / T;
   dim3 grid((unsigned)rows), block(kRowThreads);
+  if (nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
+    switch (ch) {
+      case 16: hipLaunchKernelGGL(k_rmsnorm_reg<16>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 8: hipLaunchKernelGGL(k_rmsnorm_reg<8>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 4: hipLaunchKernelGGL(k_rmsnorm_reg<4>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 2: hipLaunchKernelGGL(k_rmsnorm_reg<2>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      default: hipLaunchKernelGGL(k_rmsnorm_reg<1>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+    }
+    return check_launch();
+  }
+  const size_t lds = 2 * (size_t)nch * sizeof(float);
   switch (ch) {
     case 16: hipLaunchKernelGGL(k_rmsnorm<16>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
     case 8: hipLaunchKernelGGL(k_rmsnorm<8>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
@@ -223,19 +283,19 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
 }
 
 // =============================================================================
-// RoPE (rotate-half).  One thread = 4 consecutive pairs (i..i+3, i+h..i+h+3).
+// RoPE (rotate-half).  One thread = 4 consecutive pairs (i..i+3, i+h..i+h+3);
+// grid.x covers the (head, pair-quad) items of one token, grid.y the tokens.
 // =============================================================================
 __global__ void __launch_bounds__(256)
 k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
-       const float *sin_tab, int T, int heads, int half, int64_t ld_token, int max_pos) {
+       const float *sin_tab, int T, int heads, int half, int64_t ld_token, int max_pos,
+       int q4_shift) {
   const int q4 = half / 4;                       // 4-pair items per head
-  const int64_t total = (int64_t)T * heads * q4;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += stride) {
-    const int64_t th = it / q4;
-    const int i = (int)(it - th * q4) * 4;
-    const int t = (int)(th / heads);
-    const int hd = (int)(th - (int64_t)t * heads);
+  const int item = blockIdx.x * blockDim.x + threadIdx.x;
+  if (item >= heads * q4) return;
+  const int hd = q4_shift >= 0 ? item >> q4_shift : item / q4;
+  const int i = (item - hd * q4) * 4;
+  for (int t = blockIdx.y; t < T; t += gridDim.y) {
     int p = pos[t];
     p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
     const int64_t off = (int64_t)t * ld_token + (int64_t)hd * 2 * half + i;
@@ -243,23 +303,23 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
     const u32x2 ub = *reinterpret_cast<const u32x2 *>(x + off + half);
     const f32x4 c = *reinterpret_cast<const f32x4 *>(cos_tab + (int64_t)p * half + i);
     const f32x4 sn = *reinterpret_cast<const f32x4 *>(sin_tab + (int64_t)p * half + i);
-    float a[4] = {__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
-                  __uint_as_float(ua[1] << 16), __uint_as_float(ua[1] & 0xffff0000u)};
-    float b[4] = {__uint_as_float(ub[0] << 16), __uint_as_float(ub[0] & 0xffff0000u),
-                  __uint_as_float(ub[1] << 16), __uint_as_float(ub[1] & 0xffff0000u)};
-    uint16_t ya[4], yb[4];
+    const float a[4] = {__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
+                        __uint_as_float(ua[1] << 16), __uint_as_float(ua[1] & 0xffff0000u)};
+    const float b[4] = {__uint_as_float(ub[0] << 16), __uint_as_float(ub[0] & 0xffff0000u),
+                        __uint_as_float(ub[1] << 16), __uint_as_float(ub[1] & 0xffff0000u)};
+    float ya[4], yb[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float ac = a[e] * c[e], bs = b[e] * sn[e];
       const float bc = b[e] * c[e], as = a[e] * sn[e];
-      ya[e] = f2bf(ac - bs);
-      yb[e] = f2bf(bc + as);
+      ya[e] = ac - bs;
+      yb[e] = bc + as;
     }
     u32x2 oa, ob;
-    oa[0] = (uint32_t)ya[0] | ((uint32_t)ya[1] << 16);
-    oa[1] = (uint32_t)ya[2] | ((uint32_t)ya[3] << 16);
-    ob[0] = (uint32_t)yb[0] | ((uint32_t)yb[1] << 16);
-    ob[1] = (uint32_t)yb[2] | ((uint32_t)yb[3] << 16);
+    oa[0] = pack_bf16(ya[0], ya[1]);
+    oa[1] = pack_bf16(ya[2], ya[3]);
+    ob[0] = pack_bf16(yb[0], yb[1]);
+    ob[1] = pack_bf16(yb[2], yb[3]);
     *reinterpret_cast<u32x2 *>(y + off) = oa;
     *reinterpret_cast<u32x2 *>(y + off + half) = ob;
   }
@@ -268,83 +328,163 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
 int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
                 const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
                 int max_pos, hipStream_t s) {
+  if (T == 0) return TBIK_OK;
   const int half = head_dim / 2;
-  const int64_t total = (int64_t)T * heads * (half / 4);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 262144) blocks = 262144;
-  if (blocks < 1) blocks = 1;
-  hipLaunchKernelGGL(k_rope, dim3((unsigned)blocks), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab,
-                     T, heads, half, ld_token, max_pos);
+  const int q4 = half / 4;
+  const int items = heads * q4;
+  int q4_shift = -1;
+  for (int b = 0; b < 31; ++b)
+    if ((1 << b) == q4) q4_shift = b;
+  const unsigned gx = (unsigned)((items + 255) / 256);
+  const unsigned gy = (unsigned)(T < 65535 ? T : 65535);
+  hipLaunchKernelGGL(k_rope, dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab, T, heads,
+                     half, ld_token, max_pos, q4_shift);
   return check_launch();
 }
 
 // =============================================================================
 // SwiGLU: out = bf16((g / (1 + EXP(-g))) * u).  8 elements per item.
 // =============================================================================
-__device__ __forceinline__ float swiglu1(float g, float u) {
-  const float den = 1.0f + exp_f32(-g);
-  const float silu = g / den;
-  return silu * u;
+// silu(g) = g / (1 + EXP(-g)), the division correctly rounded.
+// Fast path: the quotient from a refined reciprocal plus one exact-remainder
+// correction (Markstein's scheme).  The gate is bf16, so silu has only
+// 2^16 possible arguments: for every finite bf16 g with g >= -87 and
+// |g| >= 2^-20 the fast path returns the IEEE quotient, whatever reciprocal
+// within 3 ulp the hardware's v_rcp_f32 gives (checked exhaustively on the
+// CPU for each such reciprocal; the GPU path is checked against the oracle on
+// all 2^16 gates).  g >= -87 keeps 1 + EXP(-g) below 2^126, so the reciprocal
+// is a normal number.  Every other g (NaN, +-inf, g < -87, tiny |g|) takes
+// the IEEE division in a branch that random activations essentially never
+// enter.
+__device__ __forceinline__ float silu_den(float g) { return 1.0f + exp_core(exp_clamp(-g)); }
+
+__device__ __forceinline__ bool silu_fast_ok(float g) {
+  return g >= -87.0f && __builtin_fabsf(g) >= 0x1p-20f && g <= 0x1.fffffep+127f;
 }
 
+__device__ __forceinline__ float silu_fast(float g, float d) {
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  const float e0 = __builtin_fmaf(-d, y0, 1.0f);
+  const float y1 = __builtin_fmaf(e0, y0, y0);
+  const float q0 = g * y1;
+  const float rm = __builtin_fmaf(-d, q0, g);
+  return __builtin_fmaf(rm, y1, q0);
+}
+
+// n gates at once; the IEEE fallback is one branch for all n.
+template <int n>
+__device__ __forceinline__ void silu_n(float (&g)[n]) {
+  float d[n];
+  bool slow = false;
+#pragma unroll
+  for (int e = 0; e < n; ++e) {
+    d[e] = silu_den(g[e]);
+    slow = slow || !silu_fast_ok(g[e]);
+  }
+  if (slow) {
+#pragma unroll
+    for (int e = 0; e < n; ++e) g[e] = silu_fast_ok(g[e]) ? silu_fast(g[e], d[e]) : g[e] / d[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < n; ++e) g[e] = silu_fast(g[e], d[e]);
+  }
+}
+
+__device__ __forceinline__ float silu(float g) {
+  float v[1] = {g};
+  silu_n<1>(v);
+  return v[0];
+}
+
+// grid.x covers the 8-element items of a row, grid.y the rows.
 template <bool VEC>
 __global__ void __launch_bounds__(256)
 k_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols, int64_t ldg,
          int64_t ldu, int64_t ldo) {
   const int per = VEC ? 8 : 1;
-  const int items = cols / per;
-  const int64_t total = (int64_t)rows * items;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t it = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; it < total; it += stride) {
-    const int64_t row = it / items;
-    const int col = (int)(it - row * items) * per;
+  const int col = (blockIdx.x * blockDim.x + threadIdx.x) * per;
+  if (col >= cols) return;
+  for (int row = blockIdx.y; row < rows; row += gridDim.y) {
     if constexpr (VEC) {
       float gv[8], uv[8];
-      load_bf16<8>(gv, g + row * ldg + col);
-      load_bf16<8>(uv, u + row * ldu + col);
+      load_bf16<8>(gv, g + (int64_t)row * ldg + col);
+      load_bf16<8>(uv, u + (int64_t)row * ldu + col);
+      silu_n<8>(gv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gv[e] = swiglu1(gv[e], uv[e]);
-      store_bf16<8>(o + row * ldo + col, gv);
+      for (int e = 0; e < 8; ++e) gv[e] = gv[e] * uv[e];
+      store_bf16<8>(o + (int64_t)row * ldo + col, gv);
     } else {
-      o[row * ldo + col] = f2bf(swiglu1(bf2f(g[row * ldg + col]), bf2f(u[row * ldu + col])));
+      o[(int64_t)row * ldo + col] =
+          f2bf(silu(bf2f(g[(int64_t)row * ldg + col])) * bf2f(u[(int64_t)row * ldu + col]));
     }
   }
 }
 
 int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
                   int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s) {
+  if (rows == 0 || cols == 0) return TBIK_OK;
   const bool vec = (cols % 8) == 0 && elem_align(g, ldg, 2) >= 8 && elem_align(u, ldu, 2) >= 8 &&
                    elem_align(o, ldo, 2) >= 8;
-  const int64_t total = (int64_t)rows * (vec ? cols / 8 : cols);
-  int64_t blocks = (total + 255) / 256;
-  if (blocks > 262144) blocks = 262144;
-  if (blocks < 1) blocks = 1;
+  const int items = vec ? cols / 8 : cols;
+  const dim3 grid((unsigned)((items + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
   if (vec)
-    hipLaunchKernelGGL(k_swiglu<true>, dim3((unsigned)blocks), dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+    hipLaunchKernelGGL(k_swiglu<true>, grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
   else
-    hipLaunchKernelGGL(k_swiglu<false>, dim3((unsigned)blocks), dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+    hipLaunchKernelGGL(k_swiglu<false>, grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
   return check_launch();
 }
 
 // =============================================================================
-// log-softmax + gather.
-//  pass 1: k_group_max    -> gmax[M][T]  (exact maxima; order-free)
-//  pass 2: k_group_sumexp -> gsum[M][T]  (EXP(x - m), PAIR inside the group)
-//  pass 3: k_lsm_finish   -> shard nodes [M][tp], perfect tree, LOG, gather
+// log-softmax + gather: one workgroup per row, one kernel.
+//  pass 1: m = exact row maximum (fmax; order-free);
+//  pass 2: e = EXP(x - m) per leaf, chunk trees -> LDS (reverse chunk order,
+//          so the first re-reads hit the lines pass 1 fetched last);
+//  PAIR levels of every group in place in LDS (node i of a level sits at
+//  i * 2^level, so the carried odd element never moves), then the shard
+//  nodes (perfect trees over T/tp groups), their perfect tree, LOG, gather.
 // =============================================================================
-constexpr int kLsmThreads = 256;
+#ifndef TBIK_LSM_THREADS
+#define TBIK_LSM_THREADS 1024
+#endif
+#ifndef TBIK_LSM_LDS_MIN
+#define TBIK_LSM_LDS_MIN 0
+#endif
+constexpr int kLsmThreads = TBIK_LSM_THREADS;
+
+// PAIR over `groups` groups of m values each, group g at buf[g*m ..): the
+// group's PAIR value is left at buf[g*m].  All threads of the block call it.
+template <int NT>
+__device__ __forceinline__ void lds_pair_inplace(float *buf, int m, int groups) {
+  const int m0 = m;
+  int s = 1;
+  while (m > 1) {
+    const int half = m >> 1;
+    for (int idx = threadIdx.x; idx < groups * half; idx += NT) {
+      const int g = idx / half;
+      const int i = idx - g * half;
+      float *b = buf + g * m0 + 2 * i * s;
+      b[0] = b[0] + b[s];
+    }
+    __syncthreads();
+    s <<= 1;
+    m = half + (m & 1);
+  }
+}
 
 template <int CH>
 __global__ void __launch_bounds__(kLsmThreads)
-k_group_max(const float *logits, int64_t ld, int V, int T, float *gmax) {
+k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V, int T, int tp,
+                 float *shard, float *out) {
+  extern __shared__ float lds[];
   __shared__ float red[kLsmThreads / 64];
-  const int row = blockIdx.y, g = blockIdx.x;
-  const int G = V / T;
-  const float *xg = logits + (int64_t)row * ld + (int64_t)g * G;
+  const int row = blockIdx.x;
+  const float *xr = logits + (int64_t)row * ld;
+  const int nch = V / CH;
+  const int gc = nch / T;
   float m = -__builtin_inff();
-  for (int ch = threadIdx.x; ch < G / CH; ch += kLsmThreads) {
+  for (int ch = threadIdx.x; ch < nch; ch += kLsmThreads) {
     float v[CH];
-    load_f32<CH>(v, xg + ch * CH);
+    load_f32<CH>(v, xr + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) m = __builtin_fmaxf(m, v[e]);
   }
@@ -352,52 +492,24 @@ k_group_max(const float *logits, int64_t ld, int V, int T, float *gmax) {
   for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    float r = red[0];
+  m = red[0];
 #pragma unroll
-    for (int q = 1; q < kLsmThreads / 64; ++q) r = __builtin_fmaxf(r, red[q]);
-    gmax[(int64_t)row * 8 + g] = r;
-  }
-}
-
-template <int CH>
-__global__ void __launch_bounds__(kLsmThreads)
-k_group_sumexp(const float *logits, int64_t ld, int V, int T, const float *gmax, float *gsum) {
-  extern __shared__ float lds[];
-  const int row = blockIdx.y, g = blockIdx.x;
-  const int G = V / T;
-  const int gc = G / CH;
-  float m = gmax[(int64_t)row * 8];
-  for (int q = 1; q < T; ++q) m = __builtin_fmaxf(m, gmax[(int64_t)row * 8 + q]);
-  const float *xg = logits + (int64_t)row * ld + (int64_t)g * G;
-  for (int ch = threadIdx.x; ch < gc; ch += kLsmThreads) {
+  for (int q = 1; q < kLsmThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
+  for (int ch = nch - 1 - (int)threadIdx.x; ch >= 0; ch -= kLsmThreads) {
     float v[CH];
-    load_f32<CH>(v, xg + ch * CH);
+    load_f32<CH>(v, xr + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) v[e] = exp_f32(v[e] - m);
     lds[ch] = chunk_tree<CH>(v);
   }
   __syncthreads();
-  float *res = lds_pair<kLsmThreads>(lds, lds + gc, gc, 1);
-  if (threadIdx.x == 0) gsum[(int64_t)row * 8 + g] = res[0];
-}
-
-__global__ void __launch_bounds__(256)
-k_lsm_finish(const float *logits, int64_t ld, const int32_t *targets, int M, int V, int T, int tp,
-             const float *gmax, const float *gsum, float *shard, float *out) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= M) return;
-  float m = gmax[(int64_t)row * 8];
-  for (int q = 1; q < T; ++q) m = __builtin_fmaxf(m, gmax[(int64_t)row * 8 + q]);
-  float v[8];
-  for (int q = 0; q < 8; ++q) v[q] = (q < T) ? gsum[(int64_t)row * 8 + q] : 0.0f;
-  // shard nodes: perfect tree over each shard's T/tp groups
+  lds_pair_inplace<kLsmThreads>(lds, gc, T);
+  if (threadIdx.x != 0) return;
   const int per = T / tp;
   float nodes[8];
-  for (int t = 0; t < 8; ++t) {
-    if (t >= tp) break;
+  for (int t = 0; t < tp; ++t) {
     float u[8];
-    for (int q = 0; q < 8; ++q) u[q] = (q < per) ? v[t * per + q] : 0.0f;
+    for (int q = 0; q < per; ++q) u[q] = lds[(t * per + q) * gc];
     for (int w = per; w > 1; w >>= 1)
       for (int q = 0; q < w / 2; ++q) u[q] = u[2 * q] + u[2 * q + 1];
     nodes[t] = u[0];
@@ -405,51 +517,43 @@ k_lsm_finish(const float *logits, int64_t ld, const int32_t *targets, int M, int
   }
   for (int w = tp; w > 1; w >>= 1)
     for (int q = 0; q < w / 2; ++q) nodes[q] = nodes[2 * q] + nodes[2 * q + 1];
-  const float ssum = nodes[0];
   const int tgt = targets[row];
   if (tgt < 0 || tgt >= V) {
     out[row] = __builtin_nanf("");
     return;
   }
-  out[row] = (logits[(int64_t)row * ld + tgt] - m) - log_f32(ssum);
+  out[row] = (xr[tgt] - m) - log_f32(nodes[0]);
 }
 
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out, int M,
                       int V, int tp, float *ws, hipStream_t s) {
+  if (M == 0) return TBIK_OK;
   const int T = tree_T(V);
   const int G = V / T;
   const int ch = cap_f32(chunk_for(G), elem_align(logits, ld, 4));
-  const int gc = G / ch;
-  if (gc > 8192) return TBIK_ERR_SHAPE;
-  float *gmax = ws;
-  float *gsum = ws + (size_t)M * 8;
-  float *shard = ws + (size_t)M * 16;
-  dim3 grid((unsigned)T, (unsigned)M), block(kLsmThreads);
-  const size_t lds = 2 * (size_t)gc * sizeof(float);
+  const int nch = V / ch;
+  size_t lds = (size_t)nch * sizeof(float);
+  if (lds > 160 * 1024) return TBIK_ERR_SHAPE;
+  if (lds < (size_t)TBIK_LSM_LDS_MIN) lds = TBIK_LSM_LDS_MIN;
+  float *shard = ws;
+  dim3 grid((unsigned)M), block(kLsmThreads);
   switch (ch) {
-    case 16:
-      hipLaunchKernelGGL(k_group_max<16>, grid, block, 0, s, logits, ld, V, T, gmax);
-      hipLaunchKernelGGL(k_group_sumexp<16>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
-      break;
-    case 8:
-      hipLaunchKernelGGL(k_group_max<8>, grid, block, 0, s, logits, ld, V, T, gmax);
-      hipLaunchKernelGGL(k_group_sumexp<8>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
-      break;
-    case 4:
-      hipLaunchKernelGGL(k_group_max<4>, grid, block, 0, s, logits, ld, V, T, gmax);
-      hipLaunchKernelGGL(k_group_sumexp<4>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
-      break;
-    case 2:
-      hipLaunchKernelGGL(k_group_max<2>, grid, block, 0, s, logits, ld, V, T, gmax);
-      hipLaunchKernelGGL(k_group_sumexp<2>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
-      break;
-    default:
-      hipLaunchKernelGGL(k_group_max<1>, grid, block, 0, s, logits, ld, V, T, gmax);
-      hipLaunchKernelGGL(k_group_sumexp<1>, grid, block, lds, s, logits, ld, V, T, gmax, gsum);
-      break;
+#define TBIK_LSM_CASE(C)                                                                       \
+  case C:                                                                                      \
+    if (lds > 64 * 1024)                                                                       \
+      (void)hipFuncSetAttribute((const void *)k_logsoftmax_row<C>,                             \
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);               \
+    hipLaunchKernelGGL(k_logsoftmax_row<C>, grid, block, lds, s, logits, ld, targets, V, T, tp, \
+                       shard, out);                                                            \
+    break;
+    TBIK_LSM_CASE(16)
+    TBIK_LSM_CASE(8)
+    TBIK_LSM_CASE(4)
+    TBIK_LSM_CASE(2)
+    TBIK_LSM_CASE(1)
+#undef TBIK_LSM_CASE
+    default: return TBIK_ERR_SHAPE;
   }
-  hipLaunchKernelGGL(k_lsm_finish, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, s, logits, ld,
-                     targets, M, V, T, tp, gmax, gsum, shard, out);
   return check_launch();
 }
 
@@ -540,7 +644,8 @@ __global__ void __launch_bounds__(256) k_primitive(int op, const float *x, float
     float r;
     if (op == TBIK_PRIM_EXP) r = exp_f32(v);
     else if (op == TBIK_PRIM_LOG) r = log_f32(v);
-    else r = bf2f(f2bf(v));
+    else if (op == TBIK_PRIM_BF16) r = bf2f(f2bf(v));
+    else r = silu(bf2f(f2bf(v)));
     y[i] = r;
   }
 }

@@ -218,7 +218,7 @@ int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int 
 size_t tbik_logsoftmax_workspace_bytes(int M, int V, int tp) {
   (void)V;
   if (M < 0 || tp < 1) return 0;
-  return (size_t)M * (16 + (size_t)tp) * sizeof(float);
+  return (size_t)M * (size_t)tp * sizeof(float);
 }
 
 int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targets, float *out_lp,
@@ -250,7 +250,7 @@ int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf1
 
 int tbik_primitive(int op, const float *x, float *y, int64_t n, void *stream) {
   if (!x || !y) return TBIK_ERR_NULL;
-  if (op < TBIK_PRIM_EXP || op > TBIK_PRIM_BF16) return TBIK_ERR_ARG;
+  if (op < TBIK_PRIM_EXP || op > TBIK_PRIM_SILU) return TBIK_ERR_ARG;
   if (n < 0) return TBIK_ERR_SHAPE;
   if (((uintptr_t)x & 3u) || ((uintptr_t)y & 3u)) return TBIK_ERR_ALIGN;
   if (n == 0) return TBIK_OK;

@@ -23,15 +23,19 @@ namespace tbik {
 
 __device__ __forceinline__ float bf2f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN -> quiet NaN.
-// Adding 0x7fff plus the lowest kept bit to the pattern carries into the
-// kept half exactly when the discarded half is above one half-unit, or is a
-// tie with an odd kept half.
-__device__ __forceinline__ uint16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// fp32 -> bf16, round to nearest, ties to even, subnormals kept: the gfx950
+// conversion instruction (v_cvt_pk_bf16_f32) under the default rounding mode
+// with fp32 denormals enabled.  A NaN becomes a quiet NaN of the same sign
+// (its payload is not specified).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+// Two conversions in one instruction: a in the low half, b in the high half.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  const f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
 // --- EXP ---------------------------------------------------------------------
@@ -40,10 +44,18 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 // and lo; e^r by the degree-7 Taylor polynomial (coefficients 1/n! rounded
 // to fp32) in Horner form with fma; 2^k applied as two power-of-two
 // multiplies so that a subnormal result is rounded once.
-__device__ __forceinline__ float exp_f32(float x) {
-  if (x != x) return x + x;
-  if (x > 89.0f) return __builtin_inff();
-  if (x < -104.0f) return 0.0f;
+//
+// EXP's special cases (x > 89 -> +inf, x < -104 -> +0) need no branch or
+// select: with x clamped to [-104.5, 89.5] the main path itself overflows
+// to +inf above 89 and rounds to +0 below -104, and inside [-104, 89] the
+// clamp is the identity.  This equality holds for every non-NaN fp32 x (an
+// exhaustive check of all 2^32 inputs).
+__device__ __forceinline__ float exp_clamp(float x) {
+  return __builtin_fminf(__builtin_fmaxf(x, -104.5f), 89.5f);
+}
+
+// Main path; x must lie in [-104.5, 89.5].
+__device__ __forceinline__ float exp_core(float x) {
   const float kf = __builtin_rintf(x * 0x1.715476p+0f);
   const int k = (int)kf;
   float r = __builtin_fmaf(-kf, 0x1.62e4p-1f, x);
@@ -61,6 +73,12 @@ __device__ __forceinline__ float exp_f32(float x) {
   const float s1 = __uint_as_float((uint32_t)(k1 + 127) << 23);
   const float s2 = __uint_as_float((uint32_t)(k2 + 127) << 23);
   return (p * s1) * s2;
+}
+
+// EXP of any fp32 x; a NaN is returned quieted (x + x).
+__device__ __forceinline__ float exp_f32(float x) {
+  const float res = exp_core(exp_clamp(x));
+  return (x != x) ? x + x : res;
 }
 
 // --- LOG ---------------------------------------------------------------------
