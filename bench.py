@@ -334,6 +334,20 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
         log("rope: %.4f ms = %.0f GB/s" % (t, nbytes / t / 1e6))
         del x, y
 
+    if want("decoder"):
+        from tp_invariant_numerics_amd.decoder import decoder_forward
+        cfg = inputs.DecoderConfig()
+        B, L = 8, 512
+        w = inputs.decoder_weights(cfg, 3700, device=dev)
+        tok = inputs.decoder_tokens(B, L, cfg.vocab, 3701, device=dev)
+        for tpv in (1, 4):
+            t = timed(lambda: decoder_forward(w, tok, cfg, tp=tpv), 5, warm=2)
+            res["decoder_8L_d2048_tokens8x512_tp%d" % tpv] = {
+                "ms": round(t, 3), "tokens_per_s": round(B * L / t * 1e3, 1),
+                "note": "forward logprobs, every step in libtbik (MFMA leaves)"}
+            log("decoder tp=%d: %.2f ms = %.0f tokens/s" % (tpv, t, B * L / t * 1e3))
+        del w
+
     if want("swiglu"):
         rows, cols = 4096, 14336
         g = inputs.normal_bf16((rows, cols), 3600, std=3.0, device=dev)
@@ -355,15 +369,16 @@ def cpu_baseline(inputs, np, log, A, W, tp):
     nth = min(16, os.cpu_count() or 1)
     Ab = inputs.bits(A)
     M, K = Ab.shape
+    # a short calibration run, then one run sized for about 12 s of CPU work
     cols = 8
-    while True:
-        Wb = inputs.bits(W[:cols])
-        t0 = time.perf_counter()
-        oracle.gemm_tpsim(Ab, Wb, tp, nthreads=nth)
-        dt = time.perf_counter() - t0
-        if dt >= 5.0 or cols >= W.shape[0]:
-            break
-        cols = min(W.shape[0], cols * max(2, int(8.0 / max(dt, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm_tpsim(Ab, inputs.bits(W[:cols]), tp, nthreads=nth)
+    dt = time.perf_counter() - t0
+    cols = int(min(W.shape[0], max(8, cols * 12.0 / max(dt, 1e-3))))
+    Wb = inputs.bits(W[:cols])
+    t0 = time.perf_counter()
+    oracle.gemm_tpsim(Ab, Wb, tp, nthreads=nth)
+    dt = time.perf_counter() - t0
     fl = 2.0 * M * cols * K
     log("cpu oracle: %d x %d outputs, K=%d, tp=%d, %d threads: %.2f s" % (M, cols, K, tp, nth, dt))
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",

@@ -242,6 +242,18 @@ int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf1
                         float scale, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Row gather, the embedding lookup of the decoder composition (TBIK summary
+ * page, "technical framework": the invariant kernels inside a full model):
+ *   out[i, :] = table[idx[i], :]  for i < n; an index outside [0, rows)
+ *   gives a zero row.  A copy: no arithmetic.
+ *  table  [rows, cols] bf16, row stride ld_table.
+ *  idx    [n] int32 device array.
+ *  out    [n, cols] bf16, row stride ld_out.
+ * ---------------------------------------------------------------------- */
+int tbik_gather_rows(const tbik_bf16 *table, int64_t ld_table, int rows, const int32_t *idx,
+                     int n, int cols, tbik_bf16 *out, int64_t ld_out, void *stream);
+
+/* ------------------------------------------------------------------------
  * The library's fp32/bf16 primitives applied elementwise (for checking):
  *  op 0: EXP(x)   op 1: LOG(x)   op 2: bf16 round-to-nearest-even of x,
  *  widened back to fp32 (a NaN gives a quiet NaN of unspecified payload)

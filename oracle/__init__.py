@@ -79,10 +79,12 @@ def bf16_to_f32(h):
 
 
 def f32_to_bf16(x):
-    x = _c(np.asarray(x, dtype=np.float32).ravel(), np.float32)
+    x = np.asarray(x, dtype=np.float32)
+    shape = x.shape
+    x = _c(x.ravel(), np.float32)
     y = np.empty(x.shape, np.uint16)
     lib().or_f32_to_bf16_array(_ptr(x), _ptr(y), x.size)
-    return y
+    return y.reshape(shape)
 
 
 def expf(x):

@@ -46,6 +46,26 @@ def test_every_declared_symbol_is_exported(L):
         assert hasattr(L, name), name
 
 
+def test_every_declared_symbol_has_a_binding_signature(L):
+    """Each entry point has explicit ctypes argument types: without them a
+    64-bit device pointer would be passed as a C int and truncated."""
+    import tp_invariant_numerics_amd as t
+    sigs = t._sigs()
+    for name in declared_functions():
+        assert name in sigs, name
+        assert getattr(L, name).argtypes is not None, name
+
+
+def test_gather_rows_validation(L):
+    g = L.tbik_gather_rows
+    assert g(None, 8, 4, FAKE, 2, 8, FAKE2, 8, None) == E_NULL
+    assert g(FAKE, 4, 4, FAKE2, 2, 8, FAKE3, 8, None) == E_SHAPE      # ld_table < cols
+    assert g(FAKE, 8, 4, FAKE2, 2, 8, FAKE3, 4, None) == E_SHAPE      # ld_out < cols
+    assert g(FAKE, 8, -1, FAKE2, 2, 8, FAKE3, 8, None) == E_SHAPE
+    assert g(MISAL, 8, 4, FAKE2, 2, 8, FAKE3, 8, None) == E_ALIGN
+    assert g(FAKE, 8, 4, FAKE2, 0, 8, FAKE3, 8, None) == OK           # nothing to copy
+
+
 def test_version_and_strerror(L):
     import tp_invariant_numerics_amd as t
     assert t.tbik_version() >= 10000

@@ -68,6 +68,7 @@ def _sigs():
         "tbik_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p, sz, p]),
         "tbik_softmax_causal": (i32, [p, i64, i64, p, i64, i64, i32, i32, i32, i32, f32, p]),
         "tbik_primitive": (i32, [i32, p, p, i64, p]),
+        "tbik_gather_rows": (i32, [p, i64, i32, p, i32, i32, p, i64, p]),
     }
 
 

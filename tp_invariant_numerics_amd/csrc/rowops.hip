@@ -635,6 +635,46 @@ int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16
 }
 
 // =============================================================================
+// row gather (embedding lookup): out[i] = table[idx[i]], zero row when the
+// index is out of range.  grid.x covers the columns, grid.y the rows.
+// =============================================================================
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+k_gather_rows(const uint16_t *table, int64_t ld_table, int rows, const int32_t *idx, int n,
+              int cols, uint16_t *out, int64_t ld_out) {
+  const int per = VEC ? 8 : 1;
+  const int col = (blockIdx.x * blockDim.x + threadIdx.x) * per;
+  if (col >= cols) return;
+  for (int i = blockIdx.y; i < n; i += gridDim.y) {
+    const int r = idx[i];
+    const bool ok = r >= 0 && r < rows;
+    if constexpr (VEC) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (ok) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)r * ld_table + col);
+      *reinterpret_cast<u32x4 *>(out + (int64_t)i * ld_out + col) = v;
+    } else {
+      out[(int64_t)i * ld_out + col] = ok ? table[(int64_t)r * ld_table + col] : (uint16_t)0;
+    }
+  }
+}
+
+int launch_gather_rows(const uint16_t *table, int64_t ld_table, int rows, const int32_t *idx,
+                       int n, int cols, uint16_t *out, int64_t ld_out, hipStream_t s) {
+  if (n == 0 || cols == 0) return TBIK_OK;
+  const bool vec = (cols % 8) == 0 && elem_align(table, ld_table, 2) >= 8 &&
+                   elem_align(out, ld_out, 2) >= 8;
+  const int items = vec ? cols / 8 : cols;
+  const dim3 grid((unsigned)((items + 255) / 256), (unsigned)(n < 65535 ? n : 65535));
+  if (vec)
+    hipLaunchKernelGGL(k_gather_rows<true>, grid, dim3(256), 0, s, table, ld_table, rows, idx, n,
+                       cols, out, ld_out);
+  else
+    hipLaunchKernelGGL(k_gather_rows<false>, grid, dim3(256), 0, s, table, ld_table, rows, idx, n,
+                       cols, out, ld_out);
+  return check_launch();
+}
+
+// =============================================================================
 // primitives, elementwise
 // =============================================================================
 __global__ void __launch_bounds__(256) k_primitive(int op, const float *x, float *y, int64_t n) {

@@ -234,6 +234,16 @@ int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targe
   return tbik::launch_logsoftmax(logits, ld, targets, out_lp, M, V, tp, ws, as_stream(stream));
 }
 
+int tbik_gather_rows(const tbik_bf16 *table, int64_t ld_table, int rows, const int32_t *idx,
+                     int n, int cols, tbik_bf16 *out, int64_t ld_out, void *stream) {
+  if (!table || !idx || !out) return TBIK_ERR_NULL;
+  if (rows < 0 || n < 0 || cols < 0 || ld_table < cols || ld_out < cols) return TBIK_ERR_SHAPE;
+  if (!aligned(table, 2) || !aligned(idx, 4) || !aligned(out, 2)) return TBIK_ERR_ALIGN;
+  if (n == 0 || cols == 0) return TBIK_OK;
+  return tbik::launch_gather_rows(table, ld_table, rows, idx, n, cols, out, ld_out,
+                                  as_stream(stream));
+}
+
 int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf16 *P,
                         int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
                         float scale, void *stream) {

@@ -40,6 +40,8 @@ int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16
                           int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
                           float scale, hipStream_t s);
 int launch_primitive(int op, const float *x, float *y, int64_t n, hipStream_t s);
+int launch_gather_rows(const uint16_t *table, int64_t ld_table, int rows, const int32_t *idx,
+                       int n, int cols, uint16_t *out, int64_t ld_out, hipStream_t s);
 
 // Maximum leaves per tree group supported by the kernels.
 constexpr int kMaxGroupLeaves = 512;

@@ -86,3 +86,48 @@ def from_bits(b):
     """bf16 tensor from numpy uint16 bit patterns."""
     b = np.ascontiguousarray(b, dtype=np.uint16)
     return torch.from_numpy(b.view(np.int16)).view(torch.bfloat16)
+
+
+# --- decoder composition -------------------------------------------------------
+
+class DecoderConfig:
+    """Shape of the random-init decoder (pre-norm, RMSNorm + RoPE attention,
+    SwiGLU MLP, untied LM head)."""
+
+    def __init__(self, layers=8, d=2048, heads=16, head_dim=128, ffn=5632, vocab=32000,
+                 theta=1e6, eps=1e-6):
+        self.layers, self.d, self.heads, self.head_dim = layers, d, heads, head_dim
+        self.ffn, self.vocab, self.theta, self.eps = ffn, vocab, theta, eps
+        assert heads * head_dim == d
+
+    def __repr__(self):
+        return ("DecoderConfig(layers=%d, d=%d, heads=%d, head_dim=%d, ffn=%d, vocab=%d)"
+                % (self.layers, self.d, self.heads, self.head_dim, self.ffn, self.vocab))
+
+
+def decoder_weights(cfg, seed, device="cpu", std=0.02):
+    """bf16 weights ~N(0, std^2) in the nn.Linear [out, in] layout; RMSNorm
+    weights are ones.  Per layer: w_qk [2d, d] (query rows then key rows),
+    w_v [d, d], w_o [d, d], w_gu [2 ffn, d] (gate rows then up rows),
+    w_down [d, ffn]."""
+    d, f = cfg.d, cfg.ffn
+    ones = torch.ones((d,), dtype=torch.bfloat16, device=device)
+    w = {"emb": normal_bf16((cfg.vocab, d), seed, std=std, device=device),
+         "lm_head": normal_bf16((cfg.vocab, d), seed + 1, std=std, device=device),
+         "final_norm": ones, "layers": []}
+    for l in range(cfg.layers):
+        s = seed + 16 * (l + 1)
+        w["layers"].append({
+            "attn_norm": ones, "mlp_norm": ones,
+            "w_qk": normal_bf16((2 * d, d), s, std=std, device=device),
+            "w_v": normal_bf16((d, d), s + 1, std=std, device=device),
+            "w_o": normal_bf16((d, d), s + 2, std=std, device=device),
+            "w_gu": normal_bf16((2 * f, d), s + 3, std=std, device=device),
+            "w_down": normal_bf16((d, f), s + 4, std=std, device=device),
+        })
+    return w
+
+
+def decoder_tokens(batch, length, vocab, seed, device="cpu"):
+    """[batch, length] int32 token ids, uniform over the vocabulary."""
+    return uniform_int(batch * length, vocab, seed, device=device).view(batch, length)
