@@ -29,6 +29,25 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "invariant GEMM TFLOP/s (% MFMA peak, overhead vs hipBLASLt); 0 bit mismatches"
 
+# The headline's shard-partials kernel, as named in a rocprofv3 kernel trace.
+HEAD_KERNEL = "k_gemm_ring<4, 4, 2, 2, 4, 2, false, 28, 1, 0, 1>"
+# HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs (profiles/
+# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64870 KiB x 2.000
+# + WRITE_SIZE 32768 KiB x 1.000, the factors being what a plain 1 GiB device
+# copy reads on the same counters (524303 KiB fetched, 1048576 KiB written).
+# Valid only for the GEMM sources the counters were taken on (hash below).
+HEAD_TRAFFIC_BYTES = (64870 * 2 + 32768) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "a174ee68e79d2393e0c84f00cef368c2f675c57dd88dfde1ec4ca95700e46371"
+
+
+def gemm_source_sha256(root):
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "tbik_device.h", "tbik_internal.h"):
+        with open(os.path.join(root, "tp_invariant_numerics_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -139,17 +158,32 @@ def main():
     log("step %.4f ms (partials %.4f ms, combine %.4f ms), wall %.4f ms/step"
         % (step_ms, part_ms, comb_ms, wall * 1e3 / args.steps))
 
-    # roofline of the dominant kernel (the shard-partials GEMM): HBM-bound
-    # (arithmetic intensity 2MNK / bytes < 2500e12/8e12 = 312 FLOP/B)
+    # Average duration of the shard-partials kernel: back-to-back launches on
+    # the launch stream between two HIP events (per-kernel events inside a
+    # step add their own dispatch overhead to the interval).
+    nb2b = max(10, args.steps)
+
+    def part_only(i=[0]):
+        i[0] += 1
+        tb.tbik_gemm_tp_partials(A, Ws[i[0] % n_rot], tp, ws=ws)
+
+    kern_ms = timed(part_only, nb2b)
+    log("partials kernel back-to-back: %.4f ms per launch" % kern_ms)
+
+    # roofline of the dominant kernel (the shard-partials GEMM): by arithmetic
+    # intensity 2MNK / bytes = 190 FLOP/B < 2500e12/8e12 = 312 FLOP/B it is
+    # HBM-bound; its MFMA fraction is reported beside it
     part_bytes = M * K * 2 + N * K * 2 + tp * M * N * 4
-    achieved_gbs = part_bytes / (part_ms * 1e-3) / 1e9
-    roofline = {"kernel": "k_gemm_mfma (tp shard partials)", "bound": "hbm",
+    achieved_gbs = part_bytes / (kern_ms * 1e-3) / 1e9
+    traffic = HEAD_TRAFFIC_BYTES if gemm_source_sha256(root) == HEAD_TRAFFIC_SRC_SHA256 else None
+    roofline = {"kernel": HEAD_KERNEL + " (tp shard partials)", "bound": "hbm",
                 "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": part_bytes,
-                "avg_launch_ms": round(part_ms, 5),
+                "avg_launch_ms": round(kern_ms, 5),
+                "in_step_event_ms": round(part_ms, 5),
                 "arith_intensity_flop_per_byte": round(flops / part_bytes, 1),
-                "mfma_frac": round(flops / (part_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+                "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
     # bitwise invariance over tp and batch size on this workload
     mismatches = 0
