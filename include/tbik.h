@@ -106,10 +106,21 @@ int tbik_tree_groups(int64_t n);
  *                      on the row's position in the batch or on tp.
  *    TBIK_LEAF_SCALAR  a leaf is 64 sequential fp32 fma in increasing k;
  *                      bit-exact with the CPU oracle.  Slow; for checking.
+ *  ws, ws_bytes
+ *          optional device workspace (NULL / 0: none; 16-byte aligned).
+ *          When it holds tbik_gemm_workspace_bytes(M, N, K) bytes and that
+ *          is non-zero, K is split into 2, 4 or 8 aligned nodes of the tree
+ *          computed by separate workgroups into ws and combined by the top
+ *          of the tree (the same bits as without: the split is at tree
+ *          nodes; TBIK summary page, "technical framework").  Worth it when
+ *          M x N has too few tiles to occupy the GPU.  The contents of ws
+ *          are unspecified afterwards.
  * ---------------------------------------------------------------------- */
+size_t tbik_gemm_workspace_bytes(int M, int N, int K);
+
 int tbik_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
               float *C, int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K,
-              int leaf_mode, void *stream);
+              int leaf_mode, float *ws, size_t ws_bytes, void *stream);
 
 /* Strided-batched form: for b in [0,batch): A + b*strideA, W + b*strideW,
  * C + b*strideC, C_bf16 + b*strideC (strides in elements, multiples of 8).

@@ -81,24 +81,24 @@ def test_tree_groups(L):
 def test_gemm_validation(L):
     g = L.tbik_gemm
     # A NULL / W NULL / both outputs NULL
-    assert g(None, 64, FAKE, 64, FAKE2, 64, None, 4, 4, 64, 0, None) == E_NULL
-    assert g(FAKE, 64, None, 64, FAKE2, 64, None, 4, 4, 64, 0, None) == E_NULL
-    assert g(FAKE, 64, FAKE2, 64, None, 64, None, 4, 4, 64, 0, None) == E_NULL
+    assert g(None, 64, FAKE, 64, FAKE2, 64, None, 4, 4, 64, 0, None, 0, None) == E_NULL
+    assert g(FAKE, 64, None, 64, FAKE2, 64, None, 4, 4, 64, 0, None, 0, None) == E_NULL
+    assert g(FAKE, 64, FAKE2, 64, None, 64, None, 4, 4, 64, 0, None, 0, None) == E_NULL
     # K not a positive multiple of 64, negative sizes, small leading dims
-    assert g(FAKE, 128, FAKE2, 128, FAKE3, 64, None, 4, 4, 100, 0, None) == E_SHAPE
-    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 0, 0, None) == E_SHAPE
-    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, -1, 4, 64, 0, None) == E_SHAPE
-    assert g(FAKE, 32, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_SHAPE
-    assert g(FAKE, 64, FAKE2, 64, FAKE3, 8, None, 4, 16, 64, 0, None) == E_SHAPE
+    assert g(FAKE, 128, FAKE2, 128, FAKE3, 64, None, 4, 4, 100, 0, None, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 0, 0, None, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, -1, 4, 64, 0, None, 0, None) == E_SHAPE
+    assert g(FAKE, 32, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 8, None, 4, 16, 64, 0, None, 0, None) == E_SHAPE
     # alignment: misaligned pointer, leading dimension not a multiple of 8
-    assert g(MISAL, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_ALIGN
-    assert g(FAKE, 68, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None) == E_ALIGN
-    assert g(FAKE, 64, FAKE2, 64, FAKE3, 3, None, 4, 4, 64, 0, None) == E_SHAPE
-    assert g(FAKE, 64, FAKE2, 64, MISAL, 64, None, 4, 4, 64, 0, None) == E_ALIGN
+    assert g(MISAL, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None, 0, None) == E_ALIGN
+    assert g(FAKE, 68, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 0, None, 0, None) == E_ALIGN
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 3, None, 4, 4, 64, 0, None, 0, None) == E_SHAPE
+    assert g(FAKE, 64, FAKE2, 64, MISAL, 64, None, 4, 4, 64, 0, None, 0, None) == E_ALIGN
     # leaf mode
-    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 7, None) == E_ARG
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 4, 4, 64, 7, None, 0, None) == E_ARG
     # tree groups beyond the supported depth (K = 64 * 1031, a prime leaf count)
-    assert g(FAKE, 66000, FAKE2, 66000, FAKE3, 64, None, 1, 1, 64 * 1031, 0, None) == E_SHAPE
+    assert g(FAKE, 66000, FAKE2, 66000, FAKE3, 64, None, 1, 1, 64 * 1031, 0, None, 0, None) == E_SHAPE
 
 
 def test_gemm_tpsim_validation(L):
@@ -151,7 +151,7 @@ def test_rowop_validation(L):
 
 def test_empty_shapes_are_no_ops(L):
     # M = 0 / rows = 0 return OK before touching any pointer or launching
-    assert L.tbik_gemm(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 0, 4, 64, 0, None) == OK
+    assert L.tbik_gemm(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 0, 4, 64, 0, None, 0, None) == OK
     assert L.tbik_rmsnorm_residual(FAKE, FAKE, FAKE, FAKE2, None, 0, 64, 64, 1e-6, None) == OK
     assert L.tbik_swiglu(FAKE, FAKE, FAKE2, 0, 8, 8, 8, 8, None) == OK
     assert L.tbik_primitive(0, FAKE, FAKE2, 0, None) == OK

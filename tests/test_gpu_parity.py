@@ -176,6 +176,25 @@ def test_gemm_mfma_tp_invariant(M, N, K, tps):
         assert np.array_equal(f32_bits_t(again), refb), tp
 
 
+@pytest.mark.parametrize("M,N,K", [(33, 4096, 14336), (256, 4096, 14336), (100, 2048, 2048),
+                                   (77, 300, 5632), (130, 520, 4096)])
+def test_gemm_split_k_workspace_same_bits(M, N, K):
+    """tbik_gemm with its split-K workspace (nodes of the tree computed by
+    separate workgroups, then the top of the tree) equals the one-launch
+    result bit for bit, fp32 and bf16 outputs."""
+    A = inputs.normal_bf16((M, K), 4300 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 4301 + N, std=0.02, device=DEV)
+    need = tb.tbik_gemm_workspace_bytes(M, N, K)
+    say("split-K", M, N, K, "workspace bytes", need)
+    assert need > 0
+    C0, Cb0 = tb.tbik_gemm(A, W, want_bf16=True, ws=None)
+    C1, Cb1 = tb.tbik_gemm(A, W, want_bf16=True)
+    assert np.array_equal(f32_bits_t(C0), f32_bits_t(C1))
+    assert torch.equal(Cb0.view(torch.int16), Cb1.view(torch.int16))
+    _, Cb2 = tb.tbik_gemm(A, W, want_fp32=False, want_bf16=True)
+    assert torch.equal(Cb0.view(torch.int16), Cb2.view(torch.int16))
+
+
 def test_gemm_mfma_batch_invariant():
     K, N = 14336, 4096
     A = inputs.normal_bf16((256, K), 4000, device=DEV)

@@ -52,7 +52,8 @@ def _sigs():
         "tbik_version": (i32, []),
         "tbik_strerror": (C.c_char_p, [i32]),
         "tbik_tree_groups": (i32, [i64]),
-        "tbik_gemm": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, p]),
+        "tbik_gemm_workspace_bytes": (sz, [i32, i32, i32]),
+        "tbik_gemm": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, p, sz, p]),
         "tbik_gemm_strided_batched": (i32, [p, i64, i64, p, i64, i64, p, i64, i64, p, i32, i32,
                                             i32, i32, i32, p]),
         "tbik_gemm_tpsim_workspace_bytes": (sz, [i32, i32, i32, i32]),
@@ -136,9 +137,15 @@ def tbik_tree_groups(n):
 
 # --- GEMM ---------------------------------------------------------------------
 
+def tbik_gemm_workspace_bytes(M, N, K):
+    return lib().tbik_gemm_workspace_bytes(M, N, K)
+
+
 def tbik_gemm(A, W, leaf_mode=LEAF_MFMA, out=None, out_bf16=None, want_fp32=True,
-              want_bf16=False):
+              want_bf16=False, ws="auto"):
     """C = A @ W^T with the tree over 64-wide K blocks.  A [M,K], W [N,K] bf16.
+    ws: "auto" allocates the split-K workspace the library asks for, None
+    passes none, or a float32 device tensor.
     Returns (C fp32 or None, C_bf16 or None)."""
     _bits(A); _bits(W); _need_gpu(A, W)
     M, K = A.shape
@@ -153,8 +160,12 @@ def tbik_gemm(A, W, leaf_mode=LEAF_MFMA, out=None, out_bf16=None, want_fp32=True
     ldc = _ld(ref) if ref is not None else N
     if out is not None and out_bf16 is not None and _ld(out_bf16) != ldc:
         raise ValueError("C and C_bf16 must share the row stride")
+    if isinstance(ws, str):
+        nb = tbik_gemm_workspace_bytes(M, N, K) if leaf_mode == LEAF_MFMA else 0
+        ws = torch.empty((nb // 4,), dtype=torch.float32, device=A.device) if nb else None
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
     rc = lib().tbik_gemm(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(out), ldc, _ptr(out_bf16),
-                         M, N, K, leaf_mode, _stream())
+                         M, N, K, leaf_mode, _ptr(ws), wsb, _stream())
     _chk(rc, "tbik_gemm")
     return out, out_bf16
 

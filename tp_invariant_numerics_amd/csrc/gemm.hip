@@ -834,6 +834,23 @@ static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
   return TBIK_ERR_ARG;
 }
 
+// Number of aligned tree nodes (1, 2, 4 or 8 parts) into which tbik_gemm
+// splits K when a workspace is given: the smallest split that gives the ring
+// kernel about one 128 x 64 workgroup per CU.  Measured on the M = 33..512,
+// K = 14336, N = 4096 projections, one workgroup per CU beats two (the extra
+// partials cost more HBM traffic than the added occupancy returns).
+// 1 = no split (small M, batched, scalar leaves, or enough tiles).
+int gemm_split_parts(int M, int N, int K, int batch, int leaf_mode) {
+  if (leaf_mode != TBIK_LEAF_MFMA || batch != 1 || M <= 32 || N <= 0 || K <= 0) return 1;
+  const int nb = K / 64;
+  const int T = tree_T(nb);
+  if (!ring_supported_g(nb / T)) return 1;
+  const int64_t narrow = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
+  for (int p = 1; p <= T; p <<= 1)
+    if (narrow * p >= 256) return p;
+  return T;
+}
+
 int launch_gemm(const GemmCall &c, hipStream_t s) {
   const int nb = c.shard_of > 0 ? c.tree_leaves : c.K / 64;
   const int T = tree_T(nb);

@@ -58,8 +58,33 @@ const char *tbik_strerror(int code) {
 
 int tbik_tree_groups(int64_t n) { return n <= 0 ? 0 : tbik::tree_T(n); }
 
+size_t tbik_gemm_workspace_bytes(int M, int N, int K) {
+  if (M <= 0 || N <= 0 || K <= 0 || (K % 64) != 0) return 0;
+  const int p = tbik::gemm_split_parts(M, N, K, 1, TBIK_LEAF_MFMA);
+  return p > 1 ? (size_t)p * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 int tbik_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, float *C,
-              int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int leaf_mode, void *stream) {
+              int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int leaf_mode, float *ws,
+              size_t ws_bytes, void *stream) {
+  int rc = check_gemm(A, lda, W, ldw, C, ldc, C_bf16, M, N, K, leaf_mode);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return TBIK_OK;
+  const int p = tbik::gemm_split_parts(M, N, K, 1, leaf_mode);
+  // Split K into p aligned tree nodes only when the caller's workspace holds
+  // them; otherwise (or when p == 1) one launch computes the whole tree.
+  // Both give the same bits: the split is at node boundaries.
+  if (p > 1 && ws && aligned(ws, 16) &&
+      ws_bytes >= (size_t)p * (size_t)M * (size_t)N * sizeof(float)) {
+    GemmCall c{};
+    c.A = A; c.lda = lda; c.strideA = 0;
+    c.W = W; c.ldw = ldw; c.strideW = 0;
+    c.C = ws; c.Cb = nullptr; c.ldc = N; c.strideC = 0; c.part_stride = (int64_t)M * N;
+    c.M = M; c.N = N; c.K = K; c.batch = 1; c.parts = p; c.leaf_mode = leaf_mode;
+    rc = tbik::launch_gemm(c, as_stream(stream));
+    if (rc) return rc;
+    return tbik::launch_tree_combine(ws, p, C, ldc, C_bf16, M, N, as_stream(stream));
+  }
   return tbik_gemm_strided_batched(A, lda, 0, W, ldw, 0, C, ldc, 0, C_bf16, M, N, K, 1, leaf_mode,
                                    stream);
 }

@@ -24,6 +24,7 @@ struct GemmCall {
 
 // Returns 0 or a TBIK_ERR_* code.
 int launch_gemm(const GemmCall &c, hipStream_t s);
+int gemm_split_parts(int M, int N, int K, int batch, int leaf_mode);
 int launch_tree_combine(const float *ws, int tp, float *C, int64_t ldc, uint16_t *Cb, int M,
                         int N, hipStream_t s);
 int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,

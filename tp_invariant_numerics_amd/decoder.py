@@ -45,7 +45,8 @@ def _p(t, off=0):
 def _gemm(A, lda, W, ldw, C, Cb, ldc, M, N, K, leaf, aoff=0, woff=0, coff=0):
     rc = lib().tbik_gemm(_p(A, aoff), lda, _p(W, woff), ldw,
                          None if C is None else _p(C, coff), ldc,
-                         None if Cb is None else _p(Cb, coff), M, N, K, leaf, _stream())
+                         None if Cb is None else _p(Cb, coff), M, N, K, leaf, None, 0,
+                         _stream())
     _chk(rc, "tbik_gemm")
 
 
