@@ -24,6 +24,11 @@
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
 
+// Small-M kernel: leaves of operand loads in flight ahead of the MFMAs.
+#ifndef TBIK_SMALL_PF
+#define TBIK_SMALL_PF 2
+#endif
+
 // Ring geometry: RING_WM x RING_WN 16x16 blocks per wave, 4 waves stacked
 // along M, RING_S stages.
 #ifndef TBIK_RING_WM
@@ -116,7 +121,8 @@ __device__ __forceinline__ void leaf_mfma(float (&out)[4 * WM * WN], const u32x4
 // KSPLIT wave groups own disjoint aligned group ranges of the same tile.
 // GD: stack depth for PAIR inside a group (>= bit length of G-1).
 // TD: stack depth over the groups of one wave group (log2 of their count).
-template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD>
+// PF: leaves whose operand loads are in flight ahead of the MFMAs.
+template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1>
 __global__ void __launch_bounds__(64 * WAVES * KSPLIT)
 k_gemm_mfma(GemmArgs p) {
   constexpr int R = 4 * WM * WN;
@@ -160,32 +166,38 @@ k_gemm_mfma(GemmArgs p) {
 
   const int nleaf = gpw * G;
   int64_t koff = (int64_t)gfirst * G * 64;
-  u32x4 fa[WM][2], fb[WN][2];
-  load_frags<WM>(fa, ap, av, koff);
-  load_frags<WN>(fb, wp, wv, koff);
+  // Slot q of fa / fb holds the leaf l with l % PF == q: the loop is unrolled
+  // by PF so that slots are named statically and no in-flight register is
+  // copied; leaf l+PF is requested into the slot right after leaf l's MFMAs.
+  u32x4 fa[PF][WM][2], fb[PF][WN][2];
+#pragma unroll
+  for (int q = 0; q < PF; ++q) {
+    if (q < nleaf) {
+      load_frags<WM>(fa[q], ap, av, koff + 64 * q);
+      load_frags<WN>(fb[q], wp, wv, koff + 64 * q);
+    }
+  }
   int c = 0, gi = 0;
-  for (int l = 0; l < nleaf; ++l) {
-    u32x4 na[WM][2], nb[WN][2];
-    const bool more = (l + 1) < nleaf;
-    if (more) {
-      load_frags<WM>(na, ap, av, koff + 64);
-      load_frags<WN>(nb, wp, wv, koff + 64);
-    }
-    leaf_mfma<WM, WN>(node, fa, fb);
-    if (pair_push<R, GD>(s, node, c, G)) {
-      pair_push<R, TD>(top, node, gi, gpw);
-      ++gi;
-      c = 0;
-    } else {
-      ++c;
-    }
-    if (more) {
+  for (int l0 = 0; l0 < nleaf; l0 += PF) {
 #pragma unroll
-      for (int b = 0; b < WM; ++b) { fa[b][0] = na[b][0]; fa[b][1] = na[b][1]; }
-#pragma unroll
-      for (int b = 0; b < WN; ++b) { fb[b][0] = nb[b][0]; fb[b][1] = nb[b][1]; }
+    for (int q = 0; q < PF; ++q) {
+      const int l = l0 + q;
+      if (l < nleaf) {
+        leaf_mfma<WM, WN>(node, fa[q], fb[q]);
+        if (l + PF < nleaf) {
+          load_frags<WM>(fa[q], ap, av, koff + 64 * (q + PF));
+          load_frags<WN>(fb[q], wp, wv, koff + 64 * (q + PF));
+        }
+        if (pair_push<R, GD>(s, node, c, G)) {
+          pair_push<R, TD>(top, node, gi, gpw);
+          ++gi;
+          c = 0;
+        } else {
+          ++c;
+        }
+      }
     }
-    koff += 64;
+    koff += 64 * PF;
   }
   // node = this wave group's node of the tree.
 
@@ -717,12 +729,12 @@ static int check_launch() {
   return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH;
 }
 
-template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD>
+template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1>
 static int launch_cfg(const GemmArgs &a, int batch, hipStream_t s) {
   dim3 grid((unsigned)((a.N + 16 * WN * WAVES - 1) / (16 * WN * WAVES)),
             (unsigned)((a.M + 16 * WM - 1) / (16 * WM)), (unsigned)(batch * a.parts));
-  hipLaunchKernelGGL((k_gemm_mfma<WM, WN, WAVES, KSPLIT, GD, TD>), grid, dim3(64 * WAVES * KSPLIT),
-                     0, s, a);
+  hipLaunchKernelGGL((k_gemm_mfma<WM, WN, WAVES, KSPLIT, GD, TD, PF>), grid,
+                     dim3(64 * WAVES * KSPLIT), 0, s, a);
   return check_launch();
 }
 
@@ -826,10 +838,10 @@ static int launch_ring(const GemmArgs &a, hipStream_t s) {
 template <int WM, int GD>
 static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
   switch (a.gpp) {
-    case 1: return launch_cfg<WM, 1, 1, 1, GD, 0>(a, batch, s);
-    case 2: return launch_cfg<WM, 1, 1, 2, GD, 0>(a, batch, s);
-    case 4: return launch_cfg<WM, 1, 1, 4, GD, 0>(a, batch, s);
-    case 8: return launch_cfg<WM, 1, 1, 8, GD, 0>(a, batch, s);
+    case 1: return launch_cfg<WM, 1, 1, 1, GD, 0, TBIK_SMALL_PF>(a, batch, s);
+    case 2: return launch_cfg<WM, 1, 1, 2, GD, 0, TBIK_SMALL_PF>(a, batch, s);
+    case 4: return launch_cfg<WM, 1, 1, 4, GD, 0, TBIK_SMALL_PF>(a, batch, s);
+    case 8: return launch_cfg<WM, 1, 1, 8, GD, 0, TBIK_SMALL_PF>(a, batch, s);
   }
   return TBIK_ERR_ARG;
 }
