@@ -323,6 +323,26 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
             tb.tbik_gemm(A, W, out=logits)
         tgt = inputs.uniform_int(M, V, 3302, device=dev)
         nbytes = M * V * 4
+        # logprob path with the row maximum fused into the LM-head GEMM
+        pm = torch.empty((M, (V + 63) // 64), dtype=torch.float32, device=dev)
+        if want("lmhead"):
+            t1 = timed(lambda: tb.tbik_gemm_logits(A, W, out=logits, pmax=pm), 5, warm=2)
+            res["lmhead_fused_rowmax_M512_K4096_N151936"] = {
+                "ms": round(t1, 4), "tflops": round(2.0 * M * V * K / t1 / 1e9, 1),
+                "note": "tbik_gemm_logits: LM-head GEMM + 64-column row maxima in its epilogue"}
+        else:
+            tb.tbik_gemm_logits(A, W, out=logits, pmax=pm)
+        for tpv in (1, 4):
+            ws = torch.empty((tb.tbik_logsoftmax_workspace_bytes(M, V, tpv) // 4,),
+                             dtype=torch.float32, device=dev)
+            out = torch.empty((M,), dtype=torch.float32, device=dev)
+            t = timed(lambda: tb.tbik_logsoftmax_gather_pmax(logits, tgt, pm, tpv, ws=ws, out=out),
+                      20)
+            res["logsoftmax_fused_max_M512_V151936_tp%d" % tpv] = {
+                "ms": round(t, 5), "gbs": round(nbytes / t / 1e6, 1),
+                "hbm_frac": round(nbytes / t / 1e6 / 8000, 4),
+                "note": "row maxima from the LM-head GEMM epilogue; one read of the fp32 logits"}
+            log("logsoftmax (fused max) tp=%d: %.4f ms = %.0f GB/s" % (tpv, t, nbytes / t / 1e6))
         for tpv in (1, 4):
             ws = torch.empty((tb.tbik_logsoftmax_workspace_bytes(M, V, tpv) // 4,),
                              dtype=torch.float32, device=dev)

@@ -240,6 +240,31 @@ int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targe
                            void *stream);
 
 /* ------------------------------------------------------------------------
+ * The logprob path with the row maximum fused into the LM-head GEMM
+ * ([TBIK] Abstract; [ISO] 叁).  The maximum is exact in any order, so
+ * per-block maxima taken in the GEMM's epilogue give the same m, and the
+ * log-softmax then reads the logits from HBM once instead of twice.
+ *
+ * tbik_gemm_logits: C = tbik_gemm(A, W) with MFMA leaves (fp32 C required)
+ * and pmax[i*ld_pmax + b] = max of C[i, 64b .. 64b+63] (clipped to N) for
+ * b < ceil(N/64).  ld_pmax >= ceil(N/64); pmax 4-byte aligned.
+ *
+ * tbik_logsoftmax_gather_pmax: tbik_logsoftmax_gather with
+ * m_i = max_b pmax[i*ld_pmax + b] over b < npmax instead of a pass over the
+ * logits.  Defined only if that maximum equals the row maximum of the
+ * logits (as tbik_gemm_logits guarantees with npmax = ceil(V/64)); the
+ * result is then bit-identical to tbik_gemm + tbik_logsoftmax_gather.
+ * ---------------------------------------------------------------------- */
+int tbik_gemm_logits(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
+                     float *C, int64_t ldc, int M, int N, int K, float *pmax, int64_t ld_pmax,
+                     void *stream);
+
+int tbik_logsoftmax_gather_pmax(const float *logits, int64_t ld, const int32_t *targets,
+                                float *out_lp, int M, int V, int tp, const float *pmax,
+                                int64_t ld_pmax, int npmax, float *ws, size_t ws_bytes,
+                                void *stream);
+
+/* ------------------------------------------------------------------------
  * Causal softmax over attention scores (decoder composition).
  *   z_j = S[i,j] * scale;  visible keys j <= i + offset;
  *   m = max of visible z;  e_j = EXP(z_j - m) if visible else +0;

@@ -66,6 +66,20 @@ def test_gather_rows_validation(L):
     assert g(FAKE, 8, 4, FAKE2, 0, 8, FAKE3, 8, None) == OK           # nothing to copy
 
 
+def test_logprob_fused_validation(L):
+    g = L.tbik_gemm_logits
+    assert g(FAKE, 64, FAKE2, 64, None, 64, 4, 4, 64, FAKE3, 1, None) == E_NULL
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, 4, 4, 64, None, 1, None) == E_NULL
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 128, 4, 128, 64, FAKE, 1, None) == E_SHAPE  # ld_pmax
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, 4, 4, 64, MISAL, 1, None) == E_ALIGN
+    assert g(FAKE, 64, FAKE2, 64, FAKE3, 64, 0, 4, 64, FAKE, 1, None) == OK
+    h = L.tbik_logsoftmax_gather_pmax
+    assert h(FAKE, 8, FAKE2, FAKE3, 4, 8, 1, None, 1, 1, FAKE, 1 << 20, None) == E_NULL
+    assert h(FAKE, 8, FAKE2, FAKE3, 4, 8, 1, FAKE, 0, 1, FAKE, 1 << 20, None) == E_SHAPE
+    assert h(FAKE, 8, FAKE2, FAKE3, 4, 8, 3, FAKE, 1, 1, FAKE, 1 << 20, None) == E_TP
+    assert h(FAKE, 8, FAKE2, FAKE3, 4, 8, 1, FAKE, 1, 1, None, 0, None) == E_WS
+
+
 def test_version_and_strerror(L):
     import tp_invariant_numerics_amd as t
     assert t.tbik_version() >= 10000

@@ -359,6 +359,47 @@ def test_swiglu_extreme_gates(orc):
     assert np.array_equal(bits(y), orc.swiglu(bits(g), bits(u)))
 
 
+# ------------------------------------------------------------------ logprob path
+def _block_max_ref(C):
+    M, N = C.shape
+    nb = (N + 63) // 64
+    pad = torch.full((M, nb * 64), -float("inf"), dtype=torch.float32, device=C.device)
+    pad[:, :N] = C
+    return pad.view(M, nb, 64).amax(dim=2)
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 151936, 4096), (100, 1000, 2048), (8, 300, 1024),
+                                   (33, 65, 64 * 28)])
+def test_gemm_logits_row_maxima(M, N, K):
+    """The LM-head GEMM with fused 64-column row maxima: C is bitwise the
+    plain GEMM's, pmax is exactly the maximum of each block of C."""
+    A = inputs.normal_bf16((M, K), 4400 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 4401 + N, std=0.02, device=DEV)
+    say("gemm_logits", M, N, K)
+    C, pmax = tb.tbik_gemm_logits(A, W)
+    ref, _ = tb.tbik_gemm(A, W)
+    assert np.array_equal(f32_bits_t(C), f32_bits_t(ref))
+    assert np.array_equal(f32_bits_t(pmax), f32_bits_t(_block_max_ref(ref)))
+
+
+@pytest.mark.parametrize("tp", [1, 4])
+def test_logprob_path_fused_max_bitexact(orc, tp):
+    """LM-head GEMM with fused maxima + one-read log-softmax = the oracle's
+    log-softmax of the same logits, bit for bit (shard sums too)."""
+    M, K, V = 512, 4096, 151936
+    A = inputs.normal_bf16((M, K), 4500, device=DEV)
+    W = inputs.normal_bf16((V, K), 4501, std=0.02, device=DEV)
+    tgt = inputs.uniform_int(M, V, 4502, device=DEV)
+    say("logprob path fused max, tp", tp)
+    logits, pmax = tb.tbik_gemm_logits(A, W)
+    lp, ws = tb.tbik_logsoftmax_gather_pmax(logits, tgt, pmax, tp)
+    ref, nodes = orc.logsoftmax_gather(logits.cpu().numpy(), tgt.cpu().numpy(), tp)
+    assert same_bits(lp.cpu().numpy(), ref)
+    assert same_bits(tb.logsoftmax_shard_nodes(ws, M, tp).cpu().numpy(), nodes)
+    lp2, _ = tb.tbik_logsoftmax_gather(logits, tgt, tp)
+    assert same_bits(lp.cpu().numpy(), lp2.cpu().numpy())
+
+
 # ------------------------------------------------------------------ log-softmax
 @pytest.mark.parametrize("M,V,tps", [(8, 151936, (1, 2, 4, 8)), (16, 32000, (1, 2, 4, 8)),
                                      (5, 1000, (1, 2, 4, 8)), (3, 12, (1, 2, 4)),

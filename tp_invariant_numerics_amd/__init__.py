@@ -69,6 +69,9 @@ def _sigs():
         "tbik_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p, sz, p]),
         "tbik_softmax_causal": (i32, [p, i64, i64, p, i64, i64, i32, i32, i32, i32, f32, p]),
         "tbik_primitive": (i32, [i32, p, p, i64, p]),
+        "tbik_gemm_logits": (i32, [p, i64, p, i64, p, i64, i32, i32, i32, p, i64, p]),
+        "tbik_logsoftmax_gather_pmax": (i32, [p, i64, p, p, i32, i32, i32, p, i64, i32, p, sz,
+                                              p]),
         "tbik_gather_rows": (i32, [p, i64, i32, p, i32, i32, p, i64, p]),
     }
 
@@ -317,6 +320,39 @@ def tbik_logsoftmax_gather(logits, targets, tp=1, ws=None, out=None):
     rc = lib().tbik_logsoftmax_gather(_ptr(logits), _ld(logits), _ptr(targets), _ptr(out), M, V,
                                       tp, _ptr(ws), ws.numel() * 4, _stream())
     _chk(rc, "tbik_logsoftmax_gather")
+    return out, ws
+
+
+def tbik_gemm_logits(A, W, out=None, pmax=None):
+    """LM-head GEMM (MFMA leaves) with the row maxima of 64-column blocks
+    fused into its epilogue -> (logits [M,N] fp32, pmax [M, ceil(N/64)])."""
+    _bits(A); _bits(W); _need_gpu(A, W)
+    M, K = A.shape
+    N = W.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    nb = (N + 63) // 64
+    if pmax is None:
+        pmax = torch.empty((M, nb), dtype=torch.float32, device=A.device)
+    rc = lib().tbik_gemm_logits(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(out), _ld(out), M, N, K,
+                                _ptr(pmax), _ld(pmax), _stream())
+    _chk(rc, "tbik_gemm_logits")
+    return out, pmax
+
+
+def tbik_logsoftmax_gather_pmax(logits, targets, pmax, tp=1, ws=None, out=None):
+    """tbik_logsoftmax_gather taking the row maxima from pmax [M, nb]."""
+    _need_gpu(logits, targets, pmax)
+    M, V = logits.shape
+    nbytes = tbik_logsoftmax_workspace_bytes(M, V, tp)
+    if ws is None:
+        ws = torch.empty((max(1, nbytes // 4),), dtype=torch.float32, device=logits.device)
+    if out is None:
+        out = torch.empty((M,), dtype=torch.float32, device=logits.device)
+    rc = lib().tbik_logsoftmax_gather_pmax(_ptr(logits), _ld(logits), _ptr(targets), _ptr(out),
+                                           M, V, tp, _ptr(pmax), _ld(pmax), pmax.shape[1],
+                                           _ptr(ws), ws.numel() * 4, _stream())
+    _chk(rc, "tbik_logsoftmax_gather_pmax")
     return out, ws
 
 

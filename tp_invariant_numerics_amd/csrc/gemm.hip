@@ -80,6 +80,9 @@ struct GemmArgs {
   int G;        // leaves per group
   int gpp;      // groups per part
   int parts;
+  // Optional (ring kernel, parts == 1): per-row maxima of C over 64-column
+  // blocks, pmax[row * ld_pmax + col / 64].
+  float *pmax; int64_t ld_pmax;
 };
 
 // Load one leaf's operand fragments for WB 16-row blocks (two MFMA halves).
@@ -635,7 +638,77 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
       }
     }
   }
+  if constexpr (WN == 4) {
+    // Exact row maxima of this wave's 64 columns (max is order-free): the
+    // logprob path's log-softmax then reads the logits only once.
+    if (p.pmax) {
+      const int cblk = (n0 + wn * 16 * WN) / 64;
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int bn = 0; bn < WN; ++bn) {
+            const int col = n0 + wn * 16 * WN + 16 * bn + (lane & 15);
+            if (col < p.N) mx = __builtin_fmaxf(mx, node[(bm * WN + bn) * 4 + i]);
+          }
+          // running maximum along each 16-lane row (DPP row_shr 1, 2, 4, 8;
+          // a lane without a source keeps its own value): lane 15 of the
+          // row ends with the maximum of all 16 lanes
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x111, 0xf, 0xf, false)));
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x112, 0xf, 0xf, false)));
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x114, 0xf, 0xf, false)));
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x118, 0xf, 0xf, false)));
+          const int row = m0 + wm * 16 * WM + 16 * bm + orow + i;
+          if ((lane & 15) == 15 && row < p.M && n0 + wn * 16 * WN < p.N)
+            p.pmax[(int64_t)row * p.ld_pmax + cblk] = mx;
+        }
+      }
+    }
+  }
 #endif
+}
+
+static int check_launch() {
+  return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH;
+}
+
+// Row maxima over 64-column blocks of an fp32 matrix (the fused epilogue's
+// result for shapes the ring kernel does not take): one thread per block.
+__global__ void __launch_bounds__(256)
+k_block_rowmax(const float *C, int64_t ldc, int M, int N, float *pmax, int64_t ld_pmax) {
+  const int nblk = (N + 63) / 64;
+  const int64_t total = (int64_t)M * nblk;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = t / nblk;
+    const int b = (int)(t - row * nblk);
+    const float *c = C + row * ldc + (int64_t)b * 64;
+    const int n = N - b * 64 < 64 ? N - b * 64 : 64;
+    float mx = -__builtin_inff();
+    for (int j = 0; j < n; ++j) mx = __builtin_fmaxf(mx, c[j]);
+    pmax[row * ld_pmax + b] = mx;
+  }
+}
+
+int launch_block_rowmax(const float *C, int64_t ldc, int M, int N, float *pmax, int64_t ld_pmax,
+                        hipStream_t s) {
+  const int64_t total = (int64_t)M * ((N + 63) / 64);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  if (blocks < 1) blocks = 1;
+  hipLaunchKernelGGL(k_block_rowmax, dim3((unsigned)blocks), dim3(256), 0, s, C, ldc, M, N, pmax,
+                     ld_pmax);
+  return check_launch();
 }
 
 // Scalar leaves: one thread per output, 64 sequential fma per leaf in
@@ -725,9 +798,6 @@ k_tree_combine4(const float *ws, int64_t mn, int N, float *C, uint16_t *Cb, int6
 // launchers
 // ---------------------------------------------------------------------------
 
-static int check_launch() {
-  return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH;
-}
 
 template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1>
 static int launch_cfg(const GemmArgs &a, int batch, hipStream_t s) {
@@ -873,11 +943,29 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
   a.M = c.M; a.N = c.N;
   a.G = nb / T;
   a.parts = c.parts;
+  a.pmax = nullptr; a.ld_pmax = 0;
   a.gpp = T / (c.shard_of > 0 ? c.shard_of : c.parts);
   if (a.G > kMaxGroupLeaves) return TBIK_ERR_SHAPE;
   if ((int64_t)c.batch * c.parts > 65535) return TBIK_ERR_SHAPE;
   if (c.leaf_mode == TBIK_LEAF_SCALAR && c.M > 65535) return TBIK_ERR_SHAPE;
   if ((c.M + 15) / 16 > 65535) return TBIK_ERR_SHAPE;
+  if (c.pmax) {
+    // row maxima: fused into the ring kernel's epilogue where it runs,
+    // otherwise a pass over C after the GEMM
+    const bool ring = c.leaf_mode == TBIK_LEAF_MFMA && c.M > 32 && c.batch == 1 &&
+                      c.parts == 1 && c.shard_of == 0 && ring_supported_g(nb / T) &&
+                      (int64_t)128 * c.lda * 2 < ((int64_t)1 << 31) &&
+                      (int64_t)128 * c.ldw * 2 < ((int64_t)1 << 31);
+    if (ring) {
+      a.pmax = c.pmax; a.ld_pmax = c.ld_pmax;
+      return launch_ring(a, s);
+    }
+    GemmCall c2 = c;
+    c2.pmax = nullptr;
+    const int rc = launch_gemm(c2, s);
+    if (rc) return rc;
+    return launch_block_rowmax(c.C, c.ldc, c.M, c.N, c.pmax, c.ld_pmax, s);
+  }
   if (c.leaf_mode == TBIK_LEAF_SCALAR) {
     dim3 grid((unsigned)((c.N + 63) / 64), (unsigned)c.M, (unsigned)(c.batch * c.parts));
     hipLaunchKernelGGL(k_gemm_scalar, grid, dim3(64), 0, s, a);

@@ -474,7 +474,7 @@ __device__ __forceinline__ void lds_pair_inplace(float *buf, int m, int groups) 
 template <int CH>
 __global__ void __launch_bounds__(kLsmThreads)
 k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V, int T, int tp,
-                 float *shard, float *out) {
+                 float *shard, float *out, const float *pmax, int64_t ld_pmax, int npmax) {
   extern __shared__ float lds[];
   __shared__ float red[kLsmThreads / 64];
   const int row = blockIdx.x;
@@ -482,11 +482,18 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   const int nch = V / CH;
   const int gc = nch / T;
   float m = -__builtin_inff();
-  for (int ch = threadIdx.x; ch < nch; ch += kLsmThreads) {
-    float v[CH];
-    load_f32<CH>(v, xr + ch * CH);
+  if (pmax) {
+    // the row maximum from partial maxima (e.g. fused into the GEMM that
+    // produced the logits): the logits are then read once
+    for (int b = threadIdx.x; b < npmax; b += kLsmThreads)
+      m = __builtin_fmaxf(m, pmax[(int64_t)row * ld_pmax + b]);
+  } else {
+    for (int ch = threadIdx.x; ch < nch; ch += kLsmThreads) {
+      float v[CH];
+      load_f32<CH>(v, xr + ch * CH);
 #pragma unroll
-    for (int e = 0; e < CH; ++e) m = __builtin_fmaxf(m, v[e]);
+      for (int e = 0; e < CH; ++e) m = __builtin_fmaxf(m, v[e]);
+    }
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
@@ -526,7 +533,8 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
 }
 
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out, int M,
-                      int V, int tp, float *ws, hipStream_t s) {
+                      int V, int tp, float *ws, const float *pmax, int64_t ld_pmax, int npmax,
+                      hipStream_t s) {
   if (M == 0) return TBIK_OK;
   const int T = tree_T(V);
   const int G = V / T;
@@ -544,7 +552,7 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
       (void)hipFuncSetAttribute((const void *)k_logsoftmax_row<C>,                             \
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);               \
     hipLaunchKernelGGL(k_logsoftmax_row<C>, grid, block, lds, s, logits, ld, targets, V, T, tp, \
-                       shard, out);                                                            \
+                       shard, out, pmax, ld_pmax, npmax);                                      \
     break;
     TBIK_LSM_CASE(16)
     TBIK_LSM_CASE(8)

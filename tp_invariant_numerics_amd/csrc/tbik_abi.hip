@@ -256,7 +256,43 @@ int tbik_logsoftmax_gather(const float *logits, int64_t ld, const int32_t *targe
   if (M > 65535) return TBIK_ERR_SHAPE;
   if (!ws || ws_bytes < tbik_logsoftmax_workspace_bytes(M, V, tp)) return TBIK_ERR_WORKSPACE;
   if ((uintptr_t)ws & 3u) return TBIK_ERR_ALIGN;
-  return tbik::launch_logsoftmax(logits, ld, targets, out_lp, M, V, tp, ws, as_stream(stream));
+  return tbik::launch_logsoftmax(logits, ld, targets, out_lp, M, V, tp, ws, nullptr, 0, 0,
+                                 as_stream(stream));
+}
+
+int tbik_logsoftmax_gather_pmax(const float *logits, int64_t ld, const int32_t *targets,
+                                float *out_lp, int M, int V, int tp, const float *pmax,
+                                int64_t ld_pmax, int npmax, float *ws, size_t ws_bytes,
+                                void *stream) {
+  if (!logits || !targets || !out_lp || !pmax) return TBIK_ERR_NULL;
+  if (M < 0 || V < 1 || ld < V || npmax < 1 || ld_pmax < npmax) return TBIK_ERR_SHAPE;
+  if (!tp_ok(tp) || (tbik::tree_T(V) % tp) != 0) return TBIK_ERR_TP;
+  if (!aligned(logits, 4) || !aligned(targets, 4) || !aligned(out_lp, 4) || !aligned(pmax, 4))
+    return TBIK_ERR_ALIGN;
+  if (M == 0) return TBIK_OK;
+  if (M > 65535) return TBIK_ERR_SHAPE;
+  if (!ws || ws_bytes < tbik_logsoftmax_workspace_bytes(M, V, tp)) return TBIK_ERR_WORKSPACE;
+  if ((uintptr_t)ws & 3u) return TBIK_ERR_ALIGN;
+  return tbik::launch_logsoftmax(logits, ld, targets, out_lp, M, V, tp, ws, pmax, ld_pmax, npmax,
+                                 as_stream(stream));
+}
+
+int tbik_gemm_logits(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, float *C,
+                     int64_t ldc, int M, int N, int K, float *pmax, int64_t ld_pmax,
+                     void *stream) {
+  int rc = check_gemm(A, lda, W, ldw, C, ldc, nullptr, M, N, K, TBIK_LEAF_MFMA);
+  if (rc) return rc;
+  if (!C || !pmax) return TBIK_ERR_NULL;
+  if (ld_pmax < (N + 63) / 64) return TBIK_ERR_SHAPE;
+  if (!aligned(pmax, 4)) return TBIK_ERR_ALIGN;
+  if (M == 0 || N == 0) return TBIK_OK;
+  GemmCall c{};
+  c.A = A; c.lda = lda; c.strideA = 0;
+  c.W = W; c.ldw = ldw; c.strideW = 0;
+  c.C = C; c.Cb = nullptr; c.ldc = ldc; c.strideC = 0; c.part_stride = 0;
+  c.M = M; c.N = N; c.K = K; c.batch = 1; c.parts = 1; c.leaf_mode = TBIK_LEAF_MFMA;
+  c.pmax = pmax; c.ld_pmax = ld_pmax;
+  return tbik::launch_gemm(c, as_stream(stream));
 }
 
 int tbik_gather_rows(const tbik_bf16 *table, int64_t ld_table, int rows, const int32_t *idx,

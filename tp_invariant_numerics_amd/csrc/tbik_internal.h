@@ -20,6 +20,9 @@ struct GemmCall {
   // shard's node (its T/shard_of groups) and parts must be 1.
   int tree_leaves;
   int shard_of;
+  // Optional: exact row maxima of C over 64-column blocks (needs C, one
+  // batch, one part): pmax[row * ld_pmax + col / 64].
+  float *pmax; int64_t ld_pmax;
 };
 
 // Returns 0 or a TBIK_ERR_* code.
@@ -36,7 +39,8 @@ int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float 
 int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
                   int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s);
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out,
-                      int M, int V, int tp, float *ws, hipStream_t s);
+                      int M, int V, int tp, float *ws, const float *pmax, int64_t ld_pmax,
+                      int npmax, hipStream_t s);
 int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P,
                           int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
                           float scale, hipStream_t s);

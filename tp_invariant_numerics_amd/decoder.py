@@ -17,8 +17,9 @@ page, Abstract and "technical framework"; rounding-alignment article,
     g | u    = h W_gu^T;  a = SwiGLU(g, u)           tbik_gemm, tbik_swiglu
     x        = a W_down^T                            row-parallel: tp K shards
 
-then RMSNorm, the LM head (fp32 logits) and the tree log-softmax with the
-next-token gather, its vocabulary split in tp shards.
+then RMSNorm, the LM head (fp32 logits, with the exact row maxima fused into
+its epilogue in MFMA mode) and the tree log-softmax with the next-token
+gather, its vocabulary split in tp shards.
 
 Simulated tensor parallelism touches exactly the reductions real tensor
 parallelism would split: the K dimension of the two row-parallel GEMMs and
@@ -144,13 +145,24 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA):
         _gemm_rowpar(a, lw["w_down"], x, tp, leaf_mode, ws)
     norm(x, weights["final_norm"])
     lm = weights["lm_head"]
-    _gemm(h, d, lm, lm.stride(0), logits, None, V, T, V, d, leaf_mode)
     targets = torch.zeros((B, L), dtype=torch.int32, device=dev)
     targets[:, :L - 1] = tokens[:, 1:]
     targets = targets.reshape(-1)
     lp = torch.empty((T,), dtype=f32, device=dev)
     lws = torch.empty((T * tp,), dtype=f32, device=dev)
-    rc = L_.tbik_logsoftmax_gather(_p(logits), V, _p(targets), _p(lp), T, V, tp, _p(lws),
-                                   lws.numel() * 4, st)
-    _chk(rc, "tbik_logsoftmax_gather")
+    if leaf_mode == LEAF_MFMA:
+        # row maxima fused into the LM-head GEMM: the log-softmax reads the
+        # logits once
+        nblk = (V + 63) // 64
+        pmax = torch.empty((T, nblk), dtype=f32, device=dev)
+        _chk(L_.tbik_gemm_logits(_p(h), d, _p(lm), lm.stride(0), _p(logits), V, T, V, d,
+                                 _p(pmax), nblk, st), "tbik_gemm_logits")
+        rc = L_.tbik_logsoftmax_gather_pmax(_p(logits), V, _p(targets), _p(lp), T, V, tp,
+                                            _p(pmax), nblk, nblk, _p(lws), lws.numel() * 4, st)
+        _chk(rc, "tbik_logsoftmax_gather_pmax")
+    else:
+        _gemm(h, d, lm, lm.stride(0), logits, None, V, T, V, d, leaf_mode)
+        rc = L_.tbik_logsoftmax_gather(_p(logits), V, _p(targets), _p(lp), T, V, tp, _p(lws),
+                                       lws.numel() * 4, st)
+        _chk(rc, "tbik_logsoftmax_gather")
     return lp.view(B, L)[:, :L - 1]
