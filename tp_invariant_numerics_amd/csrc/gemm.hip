@@ -776,7 +776,8 @@ k_tree_combine4(const float *ws, int64_t mn, int N, float *C, uint16_t *Cb, int6
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n4; q += stride) {
     f32x4 v[TP];
 #pragma unroll
-    for (int t = 0; t < TP; ++t) v[t] = *reinterpret_cast<const f32x4 *>(ws + (int64_t)t * mn + 4 * q);
+    for (int t = 0; t < TP; ++t)
+      v[t] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(ws + (int64_t)t * mn + 4 * q));
 #pragma unroll
     for (int w = TP; w > 1; w >>= 1) {
 #pragma unroll
@@ -784,7 +785,7 @@ k_tree_combine4(const float *ws, int64_t mn, int N, float *C, uint16_t *Cb, int6
     }
     const int64_t idx = 4 * q;
     const int64_t row = idx / N, col = idx - row * N;
-    if (C) *reinterpret_cast<f32x4 *>(C + row * ldc + col) = v[0];
+    if (C) __builtin_nontemporal_store(v[0], reinterpret_cast<f32x4 *>(C + row * ldc + col));
     if (Cb) {
       u32x2 o;
       o[0] = pack_bf16(v[0][0], v[0][1]);

@@ -64,13 +64,30 @@ __device__ __forceinline__ float lds_row_tree(float *buf_a, float *buf_b, int gc
   return root[0];
 }
 
-// ---- bf16 chunk loads -------------------------------------------------------
-template <int CH>
+// ---- chunk loads and stores ---------------------------------------------------
+// NT = true: non-temporal access, for data touched once by a layout in which
+// each load or store instruction covers whole cache lines (consecutive lanes,
+// consecutive addresses: SwiGLU, RoPE).  On such streams it measures 5-10%
+// faster than a cached access; layouts that split a line over several
+// instructions of one lane (the chunk-per-thread reductions) must stay
+// cached, or every instruction refetches the line.
+template <bool NT, typename V>
+__device__ __forceinline__ V vload(const V *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT, typename V>
+__device__ __forceinline__ void vstore(V *p, V v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
+template <int CH, bool NT = false>
 __device__ __forceinline__ void load_bf16(float (&v)[CH], const uint16_t *p) {
   if constexpr (CH >= 8) {
 #pragma unroll
     for (int q = 0; q < CH / 8; ++q) {
-      u32x4 u = *reinterpret_cast<const u32x4 *>(p + 8 * q);
+      const u32x4 u = vload<NT>(reinterpret_cast<const u32x4 *>(p + 8 * q));
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         v[8 * q + 2 * e] = __uint_as_float(u[e] << 16);
@@ -78,7 +95,7 @@ __device__ __forceinline__ void load_bf16(float (&v)[CH], const uint16_t *p) {
       }
     }
   } else if constexpr (CH == 4) {
-    u32x2 u = *reinterpret_cast<const u32x2 *>(p);
+    const u32x2 u = vload<NT>(reinterpret_cast<const u32x2 *>(p));
     v[0] = __uint_as_float(u[0] << 16); v[1] = __uint_as_float(u[0] & 0xffff0000u);
     v[2] = __uint_as_float(u[1] << 16); v[3] = __uint_as_float(u[1] & 0xffff0000u);
   } else {
@@ -87,7 +104,7 @@ __device__ __forceinline__ void load_bf16(float (&v)[CH], const uint16_t *p) {
   }
 }
 
-template <int CH>
+template <int CH, bool NT = false>
 __device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[CH]) {
   if constexpr (CH >= 8) {
 #pragma unroll
@@ -95,25 +112,25 @@ __device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[CH]) {
       u32x4 u;
 #pragma unroll
       for (int e = 0; e < 4; ++e) u[e] = pack_bf16(v[8 * q + 2 * e], v[8 * q + 2 * e + 1]);
-      *reinterpret_cast<u32x4 *>(p + 8 * q) = u;
+      vstore<NT>(reinterpret_cast<u32x4 *>(p + 8 * q), u);
     }
   } else if constexpr (CH == 4) {
     u32x2 u;
     u[0] = pack_bf16(v[0], v[1]);
     u[1] = pack_bf16(v[2], v[3]);
-    *reinterpret_cast<u32x2 *>(p) = u;
+    vstore<NT>(reinterpret_cast<u32x2 *>(p), u);
   } else {
 #pragma unroll
     for (int e = 0; e < CH; ++e) p[e] = f2bf(v[e]);
   }
 }
 
-template <int CH>
+template <int CH, bool NT = false>
 __device__ __forceinline__ void load_f32(float (&v)[CH], const float *p) {
   if constexpr (CH >= 4) {
 #pragma unroll
     for (int q = 0; q < CH / 4; ++q) {
-      f32x4 u = *reinterpret_cast<const f32x4 *>(p + 4 * q);
+      const f32x4 u = vload<NT>(reinterpret_cast<const f32x4 *>(p + 4 * q));
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[4 * q + e] = u[e];
     }
@@ -299,8 +316,8 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
     int p = pos[t];
     p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
     const int64_t off = (int64_t)t * ld_token + (int64_t)hd * 2 * half + i;
-    const u32x2 ua = *reinterpret_cast<const u32x2 *>(x + off);
-    const u32x2 ub = *reinterpret_cast<const u32x2 *>(x + off + half);
+    const u32x2 ua = vload<true>(reinterpret_cast<const u32x2 *>(x + off));
+    const u32x2 ub = vload<true>(reinterpret_cast<const u32x2 *>(x + off + half));
     const f32x4 c = *reinterpret_cast<const f32x4 *>(cos_tab + (int64_t)p * half + i);
     const f32x4 sn = *reinterpret_cast<const f32x4 *>(sin_tab + (int64_t)p * half + i);
     const float a[4] = {__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
@@ -320,8 +337,8 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
     oa[1] = pack_bf16(ya[2], ya[3]);
     ob[0] = pack_bf16(yb[0], yb[1]);
     ob[1] = pack_bf16(yb[2], yb[3]);
-    *reinterpret_cast<u32x2 *>(y + off) = oa;
-    *reinterpret_cast<u32x2 *>(y + off + half) = ob;
+    vstore<true>(reinterpret_cast<u32x2 *>(y + off), oa);
+    vstore<true>(reinterpret_cast<u32x2 *>(y + off + half), ob);
   }
 }
 
@@ -407,12 +424,12 @@ k_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols, 
   for (int row = blockIdx.y; row < rows; row += gridDim.y) {
     if constexpr (VEC) {
       float gv[8], uv[8];
-      load_bf16<8>(gv, g + (int64_t)row * ldg + col);
-      load_bf16<8>(uv, u + (int64_t)row * ldu + col);
+      load_bf16<8, true>(gv, g + (int64_t)row * ldg + col);
+      load_bf16<8, true>(uv, u + (int64_t)row * ldu + col);
       silu_n<8>(gv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) gv[e] = gv[e] * uv[e];
-      store_bf16<8>(o + (int64_t)row * ldo + col, gv);
+      store_bf16<8, true>(o + (int64_t)row * ldo + col, gv);
     } else {
       o[(int64_t)row * ldo + col] =
           f2bf(silu(bf2f(g[(int64_t)row * ldg + col])) * bf2f(u[(int64_t)row * ldu + col]));
@@ -659,7 +676,7 @@ k_gather_rows(const uint16_t *table, int64_t ld_table, int rows, const int32_t *
     if constexpr (VEC) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (ok) v = *reinterpret_cast<const u32x4 *>(table + (int64_t)r * ld_table + col);
-      *reinterpret_cast<u32x4 *>(out + (int64_t)i * ld_out + col) = v;
+      vstore<true>(reinterpret_cast<u32x4 *>(out + (int64_t)i * ld_out + col), v);
     } else {
       out[(int64_t)i * ld_out + col] = ok ? table[(int64_t)r * ld_table + col] : (uint16_t)0;
     }
