@@ -32,12 +32,12 @@ METRIC = "invariant GEMM TFLOP/s (% MFMA peak, overhead vs hipBLASLt); 0 bit mis
 # The headline's shard-partials kernel, as named in a rocprofv3 kernel trace.
 HEAD_KERNEL = "k_gemm_ring<4, 4, 2, 2, 4, 2, false, 28, 1, 0, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs (profiles/
-# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64870 KiB x 2.000
+# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64842 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000, the factors being what a plain 1 GiB device
 # copy reads on the same counters (524303 KiB fetched, 1048576 KiB written).
 # Valid only for the GEMM sources the counters were taken on (hash below).
-HEAD_TRAFFIC_BYTES = (64870 * 2 + 32768) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "a174ee68e79d2393e0c84f00cef368c2f675c57dd88dfde1ec4ca95700e46371"
+HEAD_TRAFFIC_BYTES = (64842 * 2 + 32768) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "30d4e4b575fb82ec48527abff2248b03c99b290ba6f5e2c5adc6aa11af772974"
 
 
 def gemm_source_sha256(root):
@@ -197,6 +197,21 @@ def main():
         mismatches += int((Cm.view(torch.int32) != ref[:m].view(torch.int32)).sum().item())
     log("bit mismatches across tp {1,2,4,8} and M {1,32,255,256}: %d" % mismatches)
 
+    # negative control: the same tp split done the usual way -- each shard's
+    # partial from torch's GEMM, the shards summed in rank order -- is not
+    # tp-invariant (why the tree exists); count its mismatches against tp=1
+    naive_mism = {}
+    one = torch.matmul(A, W0.t()).float()
+    for t in (2, 4, 8):
+        ks = K // t
+        acc = None
+        for r in range(t):
+            part = torch.matmul(A[:, r * ks:(r + 1) * ks], W0[:, r * ks:(r + 1) * ks].t()).float()
+            acc = part if acc is None else acc + part
+        naive_mism["tp%d" % t] = int((acc.view(torch.int32) != one.view(torch.int32)).sum().item())
+    del one
+    log("negative control (hipBLASLt per shard + sequential sum vs tp=1): %s" % naive_mism)
+
     # non-invariant baseline: torch bf16 GEMM (hipBLASLt), same shape
     rot = {"i": 0}
 
@@ -245,6 +260,10 @@ def main():
                    "A": "bf16 ~N(0,1)", "W": "bf16 ~N(0,0.02)", "accumulate": "fp32 tree"},
         "pct_mfma_peak": round(value / PEAK_BF16_TFLOPS * 100, 2),
         "bit_mismatches": mismatches,
+        "negative_control_mismatches": {
+            "what": "torch bf16 GEMM per K shard, shards summed in rank order, vs the "
+                    "unsplit torch GEMM (not tp-invariant); out of %d outputs" % (M * N),
+            **naive_mism},
         "roofline": roofline,
         "hipblaslt": hipblaslt,
         "cpu_baseline": cpu,
