@@ -485,3 +485,23 @@ def test_rowops_unaligned_strides(orc):
     ld[:, :32000] = torch.from_numpy(logits).to(DEV)
     lp, _ = tb.tbik_logsoftmax_gather(ld[:, :32000], torch.from_numpy(tgt).to(DEV), 4)
     assert same_bits(lp.cpu().numpy(), orc.logsoftmax_gather(logits, tgt, 4)[0])
+
+
+@pytest.mark.parametrize("M,K,N", [(2048, 2048, 4096), (2048, 1024, 4096), (4096, 2048, 2100)])
+def test_gemm_whole_part_perfect_tree(orc, M, K, N):
+    """Power-of-two groups: the part's tree is one perfect tree evaluated as a
+    single compile-time group.  Same bits across tp and batch, accurate,
+    and exact on integer data."""
+    A = inputs.normal_bf16((M, K), 4600 + K, device=DEV)
+    W = inputs.normal_bf16((N, K), 4601 + K, std=0.02, device=DEV)
+    say("perfect-tree gemm", M, K, N)
+    ref = f32_bits_t(tb.tbik_gemm(A, W, ws=None)[0])
+    for tp in (2, 4, 8):
+        assert np.array_equal(f32_bits_t(tb.tbik_gemm_tpsim(A, W, tp)[0]), ref), tp
+    for m in (1, 33, 257):
+        assert np.array_equal(f32_bits_t(tb.tbik_gemm(A[:m], W)[0]), ref[:m]), m
+    Ai = inputs.integer_bf16((M, K), 4602).to(DEV)
+    Wi = inputs.integer_bf16((N, K), 4603).to(DEV)
+    Ci = tb.tbik_gemm(Ai, Wi)[0].cpu().numpy().astype(np.float64)
+    exact = Ai.float().cpu().numpy().astype(np.float64) @ Wi.float().cpu().numpy().astype(np.float64).T
+    assert np.array_equal(Ci, exact)

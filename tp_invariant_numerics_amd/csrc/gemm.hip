@@ -53,6 +53,10 @@
 #ifndef TBIK_RING_WIDE_PIPE
 #define TBIK_RING_WIDE_PIPE 0
 #endif
+// whole-part perfect trees as one compile-time group (power-of-two G)
+#ifndef TBIK_RING_PERFECT
+#define TBIK_RING_PERFECT 1
+#endif
 // wide (128 x 128) tiles where the tree state fits
 #ifndef TBIK_RING_WIDE
 #define TBIK_RING_WIDE 1
@@ -884,6 +888,18 @@ static int launch_ring(const GemmArgs &a, hipStream_t s) {
   // (a stack depth TD >= log2(groups) is valid; TD = 1 for a single group
   //  allocates registers better than TD = 0)
   if (G == 28 && a.gpp <= 2) return launch_wide<28, 1>(a, s);
+#if TBIK_RING_PERFECT
+  // G a power of two: the part's tree (PAIR of each group = a perfect tree,
+  // then the perfect top over gpp groups) is one perfect tree over G * gpp
+  // leaves, evaluated as a single compile-time group
+  // (16 and 32 leaves fit the register budget; 64 would spill)
+  if ((G & (G - 1)) == 0 && a.gpp > 1 && (G * a.gpp == 16 || G * a.gpp == 32)) {
+    GemmArgs b = a;
+    b.G = G * a.gpp;
+    b.gpp = 1;
+    return b.G == 32 ? launch_wide<32, 1>(b, s) : launch_wide<16, 1>(b, s);
+  }
+#endif
   if (G == 8) {
     switch (a.gpp) {
       case 1:
