@@ -278,6 +278,26 @@ int tbik_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, tbik_bf1
                         float scale, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Fused causal self-attention of the decoder composition (TBIK summary
+ * page, "technical framework").  For every sequence b < batch and head
+ * h < heads it writes exactly the bits of the unfused composition
+ *   S = tbik_gemm(Q_bh, K_bh)                      (fp32, K = head_dim)
+ *   P = tbik_softmax_causal(S, offset 0, scale)    (bf16)
+ *   O_bh = bf16(tbik_gemm(P, Vt_bh))
+ * without writing S or P to memory.
+ *  Q, K   [batch*L, ldq / ldk] bf16: token t = b*L + i; head h in columns
+ *         [h*128, h*128 + 128).
+ *  Vt     [heads*128, ldvt] bf16: V transposed, row h*128 + n, column
+ *         b*L + j (ldvt >= batch*L).
+ *  O      [batch*L, ldo] bf16, same layout as Q.
+ *  head_dim must be 128; L one of 64, 128, 256, 512; strides multiples of 8
+ *  and Q, K, Vt 16-byte aligned.
+ * ---------------------------------------------------------------------- */
+int tbik_attention_causal(const tbik_bf16 *Q, int64_t ldq, const tbik_bf16 *K, int64_t ldk,
+                          const tbik_bf16 *Vt, int64_t ldvt, tbik_bf16 *O, int64_t ldo, int L,
+                          int heads, int head_dim, int batch, float scale, void *stream);
+
+/* ------------------------------------------------------------------------
  * Row gather, the embedding lookup of the decoder composition (TBIK summary
  * page, "technical framework": the invariant kernels inside a full model):
  *   out[i, :] = table[idx[i], :]  for i < n; an index outside [0, rows)

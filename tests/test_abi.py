@@ -80,6 +80,18 @@ def test_logprob_fused_validation(L):
     assert h(FAKE, 8, FAKE2, FAKE3, 4, 8, 1, FAKE, 1, 1, None, 0, None) == E_WS
 
 
+def test_attention_validation(L):
+    a = L.tbik_attention_causal
+    sc = C.c_float(0.088)
+    assert a(None, 256, FAKE, 256, FAKE2, 512, FAKE3, 256, 512, 2, 128, 1, sc, None) == E_NULL
+    assert a(FAKE, 256, FAKE, 256, FAKE2, 512, FAKE3, 256, 512, 2, 64, 1, sc, None) == E_SHAPE
+    assert a(FAKE, 256, FAKE, 256, FAKE2, 512, FAKE3, 256, 500, 2, 128, 1, sc, None) == E_SHAPE
+    assert a(FAKE, 128, FAKE, 256, FAKE2, 512, FAKE3, 256, 512, 2, 128, 1, sc, None) == E_SHAPE
+    assert a(FAKE, 256, FAKE, 256, FAKE2, 256, FAKE3, 256, 512, 2, 128, 1, sc, None) == E_SHAPE
+    assert a(MISAL, 256, FAKE, 256, FAKE2, 512, FAKE3, 256, 512, 2, 128, 1, sc, None) == E_ALIGN
+    assert a(FAKE, 256, FAKE, 256, FAKE2, 512, FAKE3, 256, 512, 2, 128, 0, sc, None) == OK
+
+
 def test_version_and_strerror(L):
     import tp_invariant_numerics_amd as t
     assert t.tbik_version() >= 10000

@@ -93,3 +93,46 @@ def test_decoder_full_batch_invariant(full):
     for b in (0, 5):
         lp1 = decoder_forward(w, tok[b:b + 1], cfg, tp=1)
         assert np.array_equal(u32(lp8)[b:b + 1], u32(lp1))
+
+
+def _attention_unfused(q, k, vT, B, L, H, scale):
+    """The decoder's unfused attention through the C ABI (strided-batched tree
+    GEMMs and the causal softmax), one sequence at a time."""
+    lib = tb.lib()
+    st = tb._stream()
+    d = H * 128
+    T = B * L
+    S = torch.empty((H, L, L), dtype=torch.float32, device=DEV)
+    P = torch.empty((H, L, L), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    e = 2
+    for b in range(B):
+        r0 = b * L
+        assert lib.tbik_gemm_strided_batched(
+            q.data_ptr() + r0 * q.stride(0) * e, q.stride(0), 128,
+            k.data_ptr() + r0 * k.stride(0) * e, k.stride(0), 128,
+            S.data_ptr(), L, L * L, None, L, L, 128, H, tb.LEAF_MFMA, st) == 0
+        assert lib.tbik_softmax_causal(S.data_ptr(), L, L * L, P.data_ptr(), L, L * L, L, L, H, 0,
+                                       scale, st) == 0
+        assert lib.tbik_gemm_strided_batched(
+            P.data_ptr(), L, L * L, vT.data_ptr() + r0 * e, vT.stride(0), 128 * vT.stride(0),
+            None, d, 128, out.data_ptr() + r0 * d * e, L, 128, L, H, tb.LEAF_MFMA, st) == 0
+    return out
+
+
+@pytest.mark.parametrize("B,L,H", [(2, 64, 3), (2, 128, 2), (1, 256, 2), (3, 512, 4)])
+def test_fused_attention_equals_composition(B, L, H):
+    d = H * 128
+    T = B * L
+    q = inputs.normal_bf16((T, 2 * d), 5100 + L, device=DEV)[:, :d]       # row stride 2d
+    k = inputs.normal_bf16((T, d), 5101 + L, device=DEV)
+    vT = inputs.normal_bf16((d, T), 5102 + L, device=DEV)
+    scale = float(torch.tensor(1.0 / 128 ** 0.5, dtype=torch.float32))
+    say("fused attention", B, L, H)
+    ref = _attention_unfused(q, k, vT, B, L, H, scale)
+    out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    rc = tb.lib().tbik_attention_causal(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0),
+                                        vT.data_ptr(), vT.stride(0), out.data_ptr(), d, L, H, 128,
+                                        B, scale, tb._stream())
+    assert rc == 0
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))

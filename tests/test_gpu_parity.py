@@ -421,7 +421,8 @@ def test_logsoftmax_bitexact(orc, M, V, tps):
 
 
 # ------------------------------------------------------------------ causal softmax
-@pytest.mark.parametrize("B,Lq,Lk,offset", [(2, 512, 512, 0), (3, 64, 128, 64), (1, 9, 24, 0)])
+@pytest.mark.parametrize("B,Lq,Lk,offset", [(2, 512, 512, 0), (3, 64, 128, 64), (1, 9, 24, 0),
+                                            (2, 130, 256, 0), (2, 64, 64, 0), (1, 512, 1024, 512)])
 def test_softmax_causal_bitexact(orc, B, Lq, Lk, offset):
     rng = np.random.default_rng(Lk + offset)
     S = (rng.standard_normal((B, Lq, Lk)) * 30).astype(np.float32)

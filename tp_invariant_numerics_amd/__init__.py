@@ -73,6 +73,8 @@ def _sigs():
         "tbik_logsoftmax_gather_pmax": (i32, [p, i64, p, p, i32, i32, i32, p, i64, i32, p, sz,
                                               p]),
         "tbik_gather_rows": (i32, [p, i64, i32, p, i32, i32, p, i64, p]),
+        "tbik_attention_causal": (i32, [p, i64, p, i64, p, i64, p, i64, i32, i32, i32, i32, f32,
+                                        p]),
     }
 
 

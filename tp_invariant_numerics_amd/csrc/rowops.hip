@@ -633,10 +633,72 @@ k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, in
   }
 }
 
+// One wave per query row for Lk = 64 * CH (CH a power of two <= 16): lane l
+// owns keys [l*CH, l*CH + CH).  Then T = 8, each group is 64/8 lanes and
+// every level of the tree (chunk, PAIR of the group -- a perfect tree since
+// the group size is a power of two -- and the top) is a perfect tree: the
+// chunk tree in registers followed by a butterfly over all 64 lanes gives
+// the row sum in every lane, with no LDS and no barrier.
+template <int CH>
+__global__ void __launch_bounds__(256)
+k_softmax_causal_wave(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, int64_t ld_p,
+                      int64_t stride_p, int Lq, int offset, float scale) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  if (i >= Lq) return;
+  const float *srow = S + (int64_t)b * stride_s + (int64_t)i * ld_s + lane * CH;
+  uint16_t *prow = P + (int64_t)b * stride_p + (int64_t)i * ld_p + lane * CH;
+  const int last = i + offset;
+  float v[CH];
+  load_f32<CH>(v, srow);
+  float m = -__builtin_inff();
+#pragma unroll
+  for (int e = 0; e < CH; ++e) {
+    v[e] = v[e] * scale;
+    if (lane * CH + e <= last) m = __builtin_fmaxf(m, v[e]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  float ex[CH];
+#pragma unroll
+  for (int e = 0; e < CH; ++e) ex[e] = (lane * CH + e <= last) ? exp_f32(v[e] - m) : 0.0f;
+  float t[CH];
+#pragma unroll
+  for (int e = 0; e < CH; ++e) t[e] = ex[e];
+  float ssum = chunk_tree<CH>(t);
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) ssum = ssum + __shfl_xor(ssum, off);
+#pragma unroll
+  for (int e = 0; e < CH; ++e) ex[e] = (lane * CH + e <= last) ? ex[e] / ssum : 0.0f;
+  store_bf16<CH>(prow, ex);
+}
+
 int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P,
                           int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
                           float scale, hipStream_t s) {
   const int T = tree_T(Lk);
+  {
+    // one wave per row when Lk = 64 * CH and every row start allows the
+    // vector accesses of a CH-wide chunk
+    const int chw = Lk / 64;
+    const int as = elem_align(S, ld_s, 4) < elem_align(S, stride_s, 4) ? elem_align(S, ld_s, 4)
+                                                                       : elem_align(S, stride_s, 4);
+    const int ap = elem_align(P, ld_p, 2) < elem_align(P, stride_p, 2) ? elem_align(P, ld_p, 2)
+                                                                       : elem_align(P, stride_p, 2);
+    if (Lk % 64 == 0 && (chw & (chw - 1)) == 0 && chw <= 16 && as >= (chw < 4 ? chw : 4) &&
+        ap >= (chw < 8 ? chw : 8)) {
+      dim3 g((unsigned)((Lq + 3) / 4), (unsigned)batch), blk(256);
+      switch (chw) {
+        case 16: hipLaunchKernelGGL(k_softmax_causal_wave<16>, g, blk, 0, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, offset, scale); break;
+        case 8: hipLaunchKernelGGL(k_softmax_causal_wave<8>, g, blk, 0, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, offset, scale); break;
+        case 4: hipLaunchKernelGGL(k_softmax_causal_wave<4>, g, blk, 0, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, offset, scale); break;
+        case 2: hipLaunchKernelGGL(k_softmax_causal_wave<2>, g, blk, 0, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, offset, scale); break;
+        default: hipLaunchKernelGGL(k_softmax_causal_wave<1>, g, blk, 0, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, offset, scale); break;
+      }
+      return check_launch();
+    }
+  }
   int ch = chunk_for(Lk / T);
   if (ch > 8) ch = 8;
   ch = cap_f32(ch, elem_align(S, ld_s, 4) < elem_align(S, stride_s, 4) ? elem_align(S, ld_s, 4)

@@ -295,6 +295,24 @@ int tbik_gemm_logits(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_
   return tbik::launch_gemm(c, as_stream(stream));
 }
 
+int tbik_attention_causal(const tbik_bf16 *Q, int64_t ldq, const tbik_bf16 *K, int64_t ldk,
+                          const tbik_bf16 *Vt, int64_t ldvt, tbik_bf16 *O, int64_t ldo, int L,
+                          int heads, int head_dim, int batch, float scale, void *stream) {
+  if (!Q || !K || !Vt || !O) return TBIK_ERR_NULL;
+  if (head_dim != 128 || heads < 1 || batch < 0 || (int64_t)heads * batch > 65535)
+    return TBIK_ERR_SHAPE;
+  if (L != 64 && L != 128 && L != 256 && L != 512) return TBIK_ERR_SHAPE;
+  if (ldq < (int64_t)heads * head_dim || ldk < (int64_t)heads * head_dim ||
+      ldo < (int64_t)heads * head_dim || ldvt < (int64_t)batch * L)
+    return TBIK_ERR_SHAPE;
+  if (!ld_ok(ldq) || !ld_ok(ldk) || !ld_ok(ldvt) || !ld_ok(ldo)) return TBIK_ERR_ALIGN;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(Vt) || !aligned(O, 2)) return TBIK_ERR_ALIGN;
+  if (!isfinite(scale)) return TBIK_ERR_ARG;
+  if (batch == 0) return TBIK_OK;
+  return tbik::launch_attn_causal(Q, ldq, K, ldk, Vt, ldvt, O, ldo, L, heads, batch, scale,
+                                  as_stream(stream));
+}
+
 int tbik_gather_rows(const tbik_bf16 *table, int64_t ld_table, int rows, const int32_t *idx,
                      int n, int cols, tbik_bf16 *out, int64_t ld_out, void *stream) {
   if (!table || !idx || !out) return TBIK_ERR_NULL;

@@ -45,6 +45,9 @@ int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16
                           int64_t ld_p, int64_t stride_p, int Lq, int Lk, int batch, int offset,
                           float scale, hipStream_t s);
 int launch_primitive(int op, const float *x, float *y, int64_t n, hipStream_t s);
+int launch_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk,
+                       const uint16_t *Vt, int64_t ldvt, uint16_t *O, int64_t ldo, int L, int heads,
+                       int batch, float scale, hipStream_t s);
 int launch_gather_rows(const uint16_t *table, int64_t ld_table, int rows, const int32_t *idx,
                        int n, int cols, uint16_t *out, int64_t ld_out, hipStream_t s);
 

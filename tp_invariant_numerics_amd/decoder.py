@@ -12,6 +12,7 @@ page, Abstract and "technical framework"; rounding-alignment article,
     S        = q k^T per (sequence, head)            tbik_gemm_strided_batched
     P        = causal softmax(S / sqrt(head_dim))    tbik_softmax_causal
     O        = P V per (sequence, head)              tbik_gemm_strided_batched
+               (MFMA mode: the three in one kernel,  tbik_attention_causal)
     x        = O W_o^T                               row-parallel: tp K shards
     h, resid = RMSNorm(x + resid)
     g | u    = h W_gu^T;  a = SwiGLU(g, u)           tbik_gemm, tbik_swiglu
@@ -125,18 +126,26 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA):
             rc = L_.tbik_rope(_p(qk, off), _p(qk, off), _p(pos), _p(c_tab), _p(s_tab), T, H, hd,
                               2 * d, L, st)
             _chk(rc, "tbik_rope")
-        for b in range(B):
-            r0 = b * L
-            rc = L_.tbik_gemm_strided_batched(
-                _p(qk, r0 * 2 * d), 2 * d, hd, _p(qk, r0 * 2 * d + d), 2 * d, hd,
-                _p(S), L, L * L, None, L, L, hd, H, leaf_mode, st)
-            _chk(rc, "tbik_gemm_strided_batched")
-            rc = L_.tbik_softmax_causal(_p(S), L, L * L, _p(P), L, L * L, L, L, H, 0, scale, st)
-            _chk(rc, "tbik_softmax_causal")
-            rc = L_.tbik_gemm_strided_batched(
-                _p(P), L, L * L, _p(vT, r0), T, hd * T,
-                None, d, hd, _p(attn, r0 * d), L, hd, L, H, leaf_mode, st)
-            _chk(rc, "tbik_gemm_strided_batched")
+        if leaf_mode == LEAF_MFMA and hd == 128 and L in (64, 128, 256, 512):
+            # fused kernel: the same bits as the three steps below, without
+            # the score matrix in HBM
+            rc = L_.tbik_attention_causal(_p(qk), 2 * d, _p(qk, d), 2 * d, _p(vT), T, _p(attn), d,
+                                          L, H, hd, B, scale, st)
+            _chk(rc, "tbik_attention_causal")
+        else:
+            for b in range(B):
+                r0 = b * L
+                rc = L_.tbik_gemm_strided_batched(
+                    _p(qk, r0 * 2 * d), 2 * d, hd, _p(qk, r0 * 2 * d + d), 2 * d, hd,
+                    _p(S), L, L * L, None, L, L, hd, H, leaf_mode, st)
+                _chk(rc, "tbik_gemm_strided_batched")
+                rc = L_.tbik_softmax_causal(_p(S), L, L * L, _p(P), L, L * L, L, L, H, 0, scale,
+                                            st)
+                _chk(rc, "tbik_softmax_causal")
+                rc = L_.tbik_gemm_strided_batched(
+                    _p(P), L, L * L, _p(vT, r0), T, hd * T,
+                    None, d, hd, _p(attn, r0 * d), L, hd, L, H, leaf_mode, st)
+                _chk(rc, "tbik_gemm_strided_batched")
         _gemm_rowpar(attn, lw["w_o"], x, tp, leaf_mode, ws)
         norm(x, lw["mlp_norm"])
         _gemm(h, d, lw["w_gu"], d, None, gu, 2 * f, T, 2 * f, d, leaf_mode)
