@@ -506,3 +506,34 @@ def test_gemm_whole_part_perfect_tree(orc, M, K, N):
     Ci = tb.tbik_gemm(Ai, Wi)[0].cpu().numpy().astype(np.float64)
     exact = Ai.float().cpu().numpy().astype(np.float64) @ Wi.float().cpu().numpy().astype(np.float64).T
     assert np.array_equal(Ci, exact)
+
+
+@pytest.mark.parametrize("M,N", [(4096, 2048), (256, 2048), (40, 520)])
+def test_gemm_group11_schedule(orc, M, N):
+    """K = 5632 (88 leaves, groups of 11, the decoder's down projection):
+    the compile-time group schedule starts groups at leaf offsets that are
+    not multiples of the ring depth.  Same bits for every tp and batch
+    subset, exact on integer data, accurate on random data."""
+    K = 5632
+    A = inputs.normal_bf16((M, K), 4700 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 4701 + N, std=0.02, device=DEV)
+    say("group-11 gemm", M, N, K)
+    ref = f32_bits_t(tb.tbik_gemm(A, W, ws=None)[0])
+    assert np.array_equal(f32_bits_t(tb.tbik_gemm(A, W)[0]), ref)
+    for tp in (2, 4, 8):
+        assert np.array_equal(f32_bits_t(tb.tbik_gemm_tpsim(A, W, tp)[0]), ref), tp
+    for m in (1, 31, 129):
+        if m < M:
+            assert np.array_equal(f32_bits_t(tb.tbik_gemm(A[:m], W)[0]), ref[:m]), m
+    rows = np.arange(0, M, max(1, M // 16))
+    cols = np.arange(0, N, max(1, N // 16))
+    rr, cc = np.meshgrid(rows, cols, indexing="ij")
+    exact = orc.gemm_f64(bits(A[rows]), bits(W[cols]))
+    got = ref.view(np.float32)[rr, cc].astype(np.float64)
+    assert np.abs(got - exact).max() / np.abs(exact).max() <= 1e-5
+    Ai = inputs.integer_bf16((M, K), 4702).to(DEV)
+    Wi = inputs.integer_bf16((N, K), 4703).to(DEV)
+    Ci = tb.tbik_gemm(Ai, Wi)[0].cpu().numpy().astype(np.float64)
+    Af = Ai.float().cpu().numpy().astype(np.float64)
+    Wf = Wi.float().cpu().numpy().astype(np.float64)
+    assert np.array_equal(Ci[rr, cc], (Af[rows] @ Wf[cols].T))

@@ -461,13 +461,15 @@ struct Ring {
   // Perfect tree over the next U leaves (U in {1,2,4,8}), merges resolved at
   // compile time; with NX == 3 the merge of leaf j-1 follows the MFMAs of
   // leaf j.  Advances l by U.
-  template <int U>
+  // AL: the block is known to start at a leaf index that is a multiple of
+  // U (then, with U % S == 0, its ring slots are known at compile time).
+  template <int U, bool AL = true>
   __device__ __forceinline__ void block(float (&out)[R]) {
     if constexpr (U == 1) {
       step(out, 0, false);
       l += 1;
     } else {
-      constexpr bool SS = (U % S) == 0;
+      constexpr bool SS = AL && (U % S) == 0;
       BlockTree<R, NX> bt;
 #define TBIK_LEAF_STEP(J)                                                    \
   if constexpr ((J) < U) {                                                   \
@@ -485,14 +487,14 @@ struct Ring {
 
   // Perfect tree over N leaves (N a power of two): halves recursively,
   // blocks of at most 8 leaves at the bottom.
-  template <int N>
+  template <int N, bool AL = true>
   __device__ __forceinline__ void perfect(float (&out)[R]) {
     if constexpr (N <= 8) {
-      block<N>(out);
+      block<N, AL>(out);
     } else {
       float left[R];
-      perfect<N / 2>(left);
-      perfect<N / 2>(out);
+      perfect<N / 2, AL>(left);
+      perfect<N / 2, AL>(out);
 #pragma unroll
       for (int r = 0; r < R; ++r) out[r] = left[r] + out[r];
     }
@@ -501,16 +503,16 @@ struct Ring {
   // PAIR over N leaves: the perfect tree over the largest power-of-two
   // prefix, added to PAIR over the rest (an odd tail moves up unchanged, so
   // PAIR is this right fold of its binary decomposition).
-  template <int N>
+  template <int N, bool AL = true>
   __device__ __forceinline__ void pair(float (&out)[R]) {
     constexpr int H = (N >= 256) ? 256 : (N >= 128) ? 128 : (N >= 64) ? 64 : (N >= 32) ? 32
                     : (N >= 16) ? 16 : (N >= 8) ? 8 : (N >= 4) ? 4 : (N >= 2) ? 2 : 1;
     if constexpr (H == N) {
-      perfect<N>(out);
+      perfect<N, AL>(out);
     } else {
       float left[R];
-      perfect<H>(left);
-      pair<N - H>(out);
+      perfect<H, AL>(left);
+      pair<N - H, AL>(out);
 #pragma unroll
       for (int r = 0; r < R; ++r) out[r] = left[r] + out[r];
     }
@@ -598,16 +600,20 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
       // Full 8-leaf blocks (perfect subtrees, aligned in the group) in a
       // loop, then the static tail of GS % 8 leaves; PAIR over the group is
       // PAIR over these block values, the tail's PAIR being the last item.
+      // Ring slots are static only if every group starts at a multiple
+      // of S leaves (GS % S == 0); otherwise the second group of a part
+      // would be read from the wrong slots.
       constexpr int NB = GS / 8, TAIL = GS % 8, NI = NB + (TAIL ? 1 : 0);
       constexpr int ID = cbit_length(NI - 1);
+      constexpr bool AL = (GS % S) == 0;
       float st[ID > 0 ? ID : 1][R];
 #pragma clang loop unroll(disable)
       for (int b = 0; b < NB; ++b) {
-        rg.template block<8>(node);
+        rg.template block<8, AL>(node);
         pair_push<R, ID>(st, node, b, NI);
       }
       if constexpr (TAIL > 0) {
-        rg.template pair<TAIL>(node);
+        rg.template pair<TAIL, AL>(node);
         pair_push<R, ID>(st, node, NB, NI);
       }
     } else {
@@ -888,16 +894,18 @@ static int launch_ring(const GemmArgs &a, hipStream_t s) {
   // (a stack depth TD >= log2(groups) is valid; TD = 1 for a single group
   //  allocates registers better than TD = 0)
   if (G == 28 && a.gpp <= 2) return launch_wide<28, 1>(a, s);
+  if (G == 11 && a.gpp <= 2) return launch_wide<11, 1>(a, s);
 #if TBIK_RING_PERFECT
   // G a power of two: the part's tree (PAIR of each group = a perfect tree,
   // then the perfect top over gpp groups) is one perfect tree over G * gpp
   // leaves, evaluated as a single compile-time group
-  // (16 and 32 leaves fit the register budget; 64 would spill)
-  if ((G & (G - 1)) == 0 && a.gpp > 1 && (G * a.gpp == 16 || G * a.gpp == 32)) {
+  // (8, 16 and 32 leaves fit the register budget; 64 would spill)
+  if ((G & (G - 1)) == 0 && a.gpp > 1 && G * a.gpp >= 8 && G * a.gpp <= 32) {
     GemmArgs b = a;
     b.G = G * a.gpp;
     b.gpp = 1;
-    return b.G == 32 ? launch_wide<32, 1>(b, s) : launch_wide<16, 1>(b, s);
+    return b.G == 32 ? launch_wide<32, 1>(b, s)
+                     : b.G == 16 ? launch_wide<16, 1>(b, s) : launch_wide<8, 1>(b, s);
   }
 #endif
   if (G == 8) {
@@ -911,6 +919,7 @@ static int launch_ring(const GemmArgs &a, hipStream_t s) {
   }
 #endif
   if (G == 28) return launch_narrow_td<28, 1, 0>(a, s);
+  if (G == 11) return launch_narrow_td<11, 1, 0>(a, s);
   if (G == 8) return launch_narrow_td<8, 1, 0>(a, s);
   if (G == 4) return launch_narrow_td<4, 1, 0>(a, s);
   if (G % 8 == 0 && bit_length(G / 8 - 1) <= 3) return launch_narrow_td<0, 8, 3>(a, s);
