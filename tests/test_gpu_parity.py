@@ -488,7 +488,8 @@ def test_rowops_unaligned_strides(orc):
     assert same_bits(lp.cpu().numpy(), orc.logsoftmax_gather(logits, tgt, 4)[0])
 
 
-@pytest.mark.parametrize("M,K,N", [(2048, 2048, 4096), (2048, 1024, 4096), (4096, 2048, 2100)])
+@pytest.mark.parametrize("M,K,N", [(2048, 2048, 4096), (2048, 1024, 4096), (4096, 2048, 2100),
+                                   (4096, 4096, 2048)])
 def test_gemm_whole_part_perfect_tree(orc, M, K, N):
     """Power-of-two groups: the part's tree is one perfect tree evaluated as a
     single compile-time group.  Same bits across tp and batch, accurate,

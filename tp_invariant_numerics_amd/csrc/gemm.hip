@@ -24,6 +24,14 @@
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
 
+// two-workgroups-per-CU tiles for small groups
+#ifndef TBIK_RING_TWIN_PERFECT
+#define TBIK_RING_TWIN_PERFECT 1
+#endif
+#ifndef TBIK_RING_TWIN
+#define TBIK_RING_TWIN 1
+#endif
+
 // Small-M kernel: leaves of operand loads in flight ahead of the MFMAs.
 #ifndef TBIK_SMALL_PF
 #define TBIK_SMALL_PF 2
@@ -519,13 +527,14 @@ struct Ring {
   }
 };
 
-// GS > 0: the group size G is the compile-time constant GS and each group
-// is evaluated by Ring::pair<GS>.  GS == 0: runtime G, blocks of U leaves
+// GS > 0: the group size G is the compile-time constant GS; U == 0 then
+// evaluates each group as one Ring::pair<GS>, any other U as 8-leaf blocks
+// plus a static tail.  GS == 0: runtime G, blocks of U leaves
 // pushed through a binary-counter stack of depth GD.  TD: stack depth over
 // the groups of one part.
 template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
-          int TD>
-__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N)
+          int TD, int MINB>
+__global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINB)
 k_gemm_ring(GemmArgs p, TileMap tm) {
   // The body uses buffer-resource builtins that only exist for the device;
   // the host compilation pass only needs the launch stub.
@@ -596,7 +605,12 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   float node[R];
   const int ngroups = gpp;
   for (int gi = 0; gi < ngroups; ++gi) {
-    if constexpr (GS > 0) {
+    if constexpr (GS > 0 && U == 0) {
+      // The whole group as one compile-time PAIR (perfect trees over the
+      // binary decomposition of GS, right-folded): one node fewer live than
+      // blocks of 8 pushed through a stack.  Same tree, same bits.
+      rg.template pair<GS, (GS % S) == 0>(node);
+    } else if constexpr (GS > 0) {
       // Full 8-leaf blocks (perfect subtrees, aligned in the group) in a
       // loop, then the static tail of GS % 8 leaves; PAIR over the group is
       // PAIR over these block values, the tail's PAIR being the last item.
@@ -834,7 +848,7 @@ static int launch_big(const GemmArgs &a, int batch, hipStream_t s) {
 }
 
 template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
-          int TD>
+          int TD, int MINB = 1>
 static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
   TileMap tm;
@@ -844,7 +858,7 @@ static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   tm.group_m = 8;
   const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * tm.parts;
   if (nb > 0x7fffffff) return TBIK_ERR_SHAPE;
-  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE, GS, U, GD, TD>),
+  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE, GS, U, GD, TD, MINB>),
                      dim3((unsigned)nb), dim3(64 * WAVES_M * WAVES_N), 0, s, a, tm);
   return check_launch();
 }
@@ -861,9 +875,32 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
                          TBIK_RING_S, TBIK_RING_NX, (TBIK_RING_PIPE != 0 && GS > 0), GS, U, GD, TD>(
       a, s);
 }
-template <int GS, int TD>
+template <int GS, int TD, int U = 0>
 static int launch_wide(const GemmArgs &a, hipStream_t s) {
-  return launch_ring_cfg<4, 4, 2, 2, 4, 2, TBIK_RING_WIDE_PIPE != 0, GS, 1, 0, TD>(a, s);
+  return launch_ring_cfg<4, 4, 2, 2, 4, 2, TBIK_RING_WIDE_PIPE != 0, GS, U, 0, TD>(a, s);
+}
+
+// "Twin" tiles: 128 x 64 like the narrow ones, but compiled for two
+// workgroups per CU (<= 256 registers per wave: two leaf accumulators, no
+// fragment pipelining, a 3-stage ring of 72 KB).  The copy of operands into
+// LDS proceeds at a fixed rate per workgroup whatever the ring depth, so a
+// second resident workgroup nearly doubles it; used where the group's tree
+// state fits the budget (groups of 4, 8 and 11 leaves).
+template <int GS, int U = 1>
+static int launch_twin(const GemmArgs &a, hipStream_t s) {
+  if constexpr (GS == 16 || GS == 32) {
+    // a whole part as one perfect tree (one group per part)
+    if (a.gpp == 1) return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, U, 0, 1, 2>(a, s);
+    return TBIK_ERR_ARG;
+  } else {
+    switch (a.gpp) {
+      case 1:
+      case 2: return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, 1, 0, 1, 2>(a, s);
+      case 4: return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, 1, 0, 2, 2>(a, s);
+      case 8: return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, 1, 0, 3, 2>(a, s);
+    }
+    return TBIK_ERR_ARG;
+  }
 }
 
 template <int GS, int U, int GD>
@@ -885,6 +922,26 @@ static bool ring_supported_g(int G) {
 
 static int launch_ring(const GemmArgs &a, hipStream_t s) {
   const int G = a.G;
+#if TBIK_RING_TWIN
+  {
+    const int64_t twin_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 63) / 64) * a.parts;
+    if (twin_tiles >= 512) {
+      if (TBIK_RING_TWIN_PERFECT && (G & (G - 1)) == 0 && a.gpp > 1 && G * a.gpp >= 8 &&
+          G * a.gpp <= 32) {
+        // the part's tree is one perfect tree over G * gpp leaves (as for
+        // the wide tiles below)
+        GemmArgs b = a;
+        b.G = G * a.gpp;
+        b.gpp = 1;
+        return b.G == 32 ? launch_twin<32, 0>(b, s)
+                         : b.G == 16 ? launch_twin<16, 0>(b, s) : launch_twin<8>(b, s);
+      }
+      if (G == 4) return launch_twin<4>(a, s);
+      if (G == 8) return launch_twin<8>(a, s);
+      if (G == 11) return launch_twin<11>(a, s);
+    }
+  }
+#endif
 #if TBIK_RING_WIDE
   // wide tiles where the live tree state fits (G = 28 with at most two
   // groups per part, G = 8 with any number) and there are enough of them to
@@ -904,8 +961,8 @@ static int launch_ring(const GemmArgs &a, hipStream_t s) {
     GemmArgs b = a;
     b.G = G * a.gpp;
     b.gpp = 1;
-    return b.G == 32 ? launch_wide<32, 1>(b, s)
-                     : b.G == 16 ? launch_wide<16, 1>(b, s) : launch_wide<8, 1>(b, s);
+    return b.G == 32 ? launch_wide<32, 1, 1>(b, s)
+                     : b.G == 16 ? launch_wide<16, 1, 1>(b, s) : launch_wide<8, 1, 1>(b, s);
   }
 #endif
   if (G == 8) {
