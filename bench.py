@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "invariant GEMM TFLOP/s (% MFMA peak, overhead vs hipBLASLt); 0 bit mismatches"
 
 # The headline's shard-partials kernel, as named in a rocprofv3 kernel trace.
-HEAD_KERNEL = "k_gemm_ring<4, 4, 2, 2, 4, 2, false, 28, 1, 0, 1>"
+HEAD_KERNEL = "k_gemm_ring<4, 4, 2, 2, 4, 2, false, 28, 0, 0, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs (profiles/
 # k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64840 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000, the factors being what a plain 1 GiB device
@@ -419,6 +419,35 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
                 "ms": round(t, 3), "tokens_per_s": round(B * L / t * 1e3, 1),
                 "note": "forward logprobs, every step in libtbik (MFMA leaves)"}
             log("decoder tp=%d: %.2f ms = %.0f tokens/s" % (tpv, t, B * L / t * 1e3))
+        # Rounding-location mismatch (rounding-alignment article, "three
+        # nodes"): the trainer stack is tp=1 with fp32-intermediate nodes;
+        # the engine runs tp=4 with the same nodes ("aligned") or with some
+        # nodes rounding every intermediate to bf16.  Gap = logprob
+        # differences over the 8 x 511 predicted tokens.
+        ref = decoder_forward(w, tok, cfg, tp=1).double()
+        gaps = {}
+        for name, nodes in (("aligned", ()), ("rope", ("rope",)), ("swiglu", ("swiglu",)),
+                            ("rmsnorm", ("rmsnorm",)),
+                            ("all_three", ("rmsnorm", "rope", "swiglu"))):
+            lp = decoder_forward(w, tok, cfg, tp=4,
+                                 rounding=dict.fromkeys(nodes, "each_op")).double()
+            d_lp = (lp - ref).abs()
+            d_p = (lp.exp() - ref.exp()).abs()
+            gaps[name] = {"tokens_differing": int((d_lp > 0).sum().item()),
+                          "tokens": int(d_lp.numel()),
+                          "max_abs_dlogprob": float(d_lp.max().item()),
+                          "mean_abs_dlogprob": float(d_lp.mean().item()),
+                          "max_abs_dprob": float(d_p.max().item())}
+            log("rounding gap engine(tp4, %s) vs trainer(tp1): %d/%d tokens differ, "
+                "max |dlp| %.3g, mean %.3g" % (name, gaps[name]["tokens_differing"],
+                                               gaps[name]["tokens"],
+                                               gaps[name]["max_abs_dlogprob"],
+                                               gaps[name]["mean_abs_dlogprob"]))
+        res["rounding_location_gap"] = {
+            "what": "engine tp=4 (nodes rounding each op to bf16) vs trainer tp=1 "
+                    "(fp32-intermediate nodes); random-init weights, so the mechanism, "
+                    "not the pages' RL numbers",
+            "gaps": gaps}
         del w
 
     if want("swiglu"):

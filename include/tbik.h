@@ -174,6 +174,18 @@ int tbik_tree_combine(const float *ws, int tp, float *C, int64_t ldc, tbik_bf16 
                       int M, int N, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Rounding location of the three nodes below ([ROUND] "the problem", "three
+ * nodes"): the aligned node keeps every intermediate in fp32 and rounds once,
+ * at its bf16 output (what tbik_rmsnorm_residual, tbik_rope and tbik_swiglu
+ * compute); the misaligned stack the article describes rounds intermediates
+ * to bf16 along the way.  TBIK_ROUND_EACH_OP is that stack read as eager
+ * bf16 tensor arithmetic: every elementwise operation is computed in fp32
+ * and rounded to bf16, and fp32 tables are stored as bf16.  The _ex entry
+ * points take one of these; any other value returns TBIK_ERR_ARG.
+ * ---------------------------------------------------------------------- */
+enum { TBIK_ROUND_ONCE = 0, TBIK_ROUND_EACH_OP = 1 };
+
+/* ------------------------------------------------------------------------
  * Fused residual-add + RMSNorm ([ROUND] "three nodes"; [TBIK] reduction
  * primitives).  Per row, all intermediates fp32:
  *   h = x + r;  r_out = bf16(h);  ss = TREE_j(h_j * h_j);  mean = ss / H;
@@ -186,6 +198,13 @@ int tbik_tree_combine(const float *ws, int tp, float *C, int64_t ldc, tbik_bf16 
 int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
                           tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,
                           float eps, void *stream);
+
+/* tbik_rmsnorm_residual with a rounding location.  TBIK_ROUND_EACH_OP:
+ *   h = bf16(x + r) (the residual output, and the input of the norm);
+ *   ss, rstd as above from that h;  y = bf16(bf16(h * rstd) * w). */
+int tbik_rmsnorm_residual_ex(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
+                             tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,
+                             float eps, int rounding, void *stream);
 
 /* ------------------------------------------------------------------------
  * RoPE, rotate-half pairing ([ROUND] "three nodes": fp32 intermediates).
@@ -204,6 +223,14 @@ int tbik_rope(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float 
               const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
               int max_pos, void *stream);
 
+/* tbik_rope with a rounding location.  TBIK_ROUND_EACH_OP: c = bf16(c),
+ * s = bf16(s), every product rounded to bf16, then
+ *   y[i] = bf16(bf16(x[i]*c) - bf16(x[i+d/2]*s)),
+ *   y[i+d/2] = bf16(bf16(x[i+d/2]*c) + bf16(x[i]*s)). */
+int tbik_rope_ex(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float *cos_tab,
+                 const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+                 int max_pos, int rounding, void *stream);
+
 /* HOST helper: cos_tab/sin_tab (host memory, [max_pos, d/2] fp32) with
  * angle = p * theta^(-2i/d) evaluated in binary64 and cos/sin rounded once
  * to fp32 (an fp32 angle would lose ~1e-3 rad at p ~ 3e4). */
@@ -217,6 +244,12 @@ int tbik_rope_table(double theta, int head_dim, int max_pos, float *cos_tab, flo
  * ---------------------------------------------------------------------- */
 int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows,
                 int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out, void *stream);
+
+/* tbik_swiglu with a rounding location.  TBIK_ROUND_EACH_OP:
+ *   out = bf16(bf16(g / (1 + EXP(-g))) * u). */
+int tbik_swiglu_ex(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows,
+                   int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out, int rounding,
+                   void *stream);
 
 /* ------------------------------------------------------------------------
  * Log-softmax + target gather ([TBIK] reduction primitives; [ISO] 叁 logprob

@@ -42,10 +42,10 @@ def lib():
             "or_gemm_f64": (i32, [p, i64, p, i64, p, i64, i32, i32, i32, i32]),
             "or_gemm_naive_tp": (i32, [p, i64, p, i64, p, i64, i32, i32, i32, i32, i32]),
             "or_gemm_sampled": (i32, [p, i64, p, i64, i32, p, p, i64, p, i32]),
-            "or_rmsnorm_residual": (None, [p, p, p, p, p, i32, i32, i64, f32]),
+            "or_rmsnorm_residual": (None, [p, p, p, p, p, i32, i32, i64, f32, i32]),
             "or_rope_table": (None, [f64, i32, i32, p, p]),
-            "or_rope": (None, [p, p, p, p, p, i32, i32, i32, i64]),
-            "or_swiglu": (None, [p, p, p, i32, i32, i64, i64, i64]),
+            "or_rope": (None, [p, p, p, p, p, i32, i32, i32, i64, i32]),
+            "or_swiglu": (None, [p, p, p, i32, i32, i64, i64, i64, i32]),
             "or_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p]),
             "or_softmax_causal": (None, [p, i64, p, i64, i32, i32, i32, f32]),
         }
@@ -185,12 +185,16 @@ def gemm_sampled(A, W, rows, cols, nthreads=0):
 
 # --- row reductions and elementwise nodes -----------------------------------
 
-def rmsnorm_residual(x, r, w, eps):
+ROUNDING = {"once": 0, "each_op": 1}
+
+
+def rmsnorm_residual(x, r, w, eps, rounding="once"):
+    """rounding: "once" (fp32 intermediates) or "each_op" (bf16 after every op)."""
     x = _c(x, np.uint16); r = _c(r, np.uint16); w = _c(w, np.uint16)
     rows, H = x.shape
     y = np.empty_like(x); r_out = np.empty_like(x)
     lib().or_rmsnorm_residual(_ptr(x), _ptr(r), _ptr(w), _ptr(y), _ptr(r_out), rows, H, H,
-                              np.float32(eps))
+                              np.float32(eps), ROUNDING[rounding])
     return y, r_out
 
 
@@ -202,7 +206,7 @@ def rope_table(theta, head_dim, max_pos):
     return c, s
 
 
-def rope(x, pos, cos_tab, sin_tab):
+def rope(x, pos, cos_tab, sin_tab, rounding="once"):
     """x [T, heads, head_dim] uint16."""
     x = _c(x, np.uint16)
     T, heads, hd = x.shape
@@ -210,15 +214,15 @@ def rope(x, pos, cos_tab, sin_tab):
     cos_tab = _c(cos_tab, np.float32); sin_tab = _c(sin_tab, np.float32)
     y = np.empty_like(x)
     lib().or_rope(_ptr(x), _ptr(y), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T, heads, hd,
-                  heads * hd)
+                  heads * hd, ROUNDING[rounding])
     return y
 
 
-def swiglu(g, u):
+def swiglu(g, u, rounding="once"):
     g = _c(g, np.uint16); u = _c(u, np.uint16)
     rows, cols = g.shape
     out = np.empty_like(g)
-    lib().or_swiglu(_ptr(g), _ptr(u), _ptr(out), rows, cols, cols, cols, cols)
+    lib().or_swiglu(_ptr(g), _ptr(u), _ptr(out), rows, cols, cols, cols, cols, ROUNDING[rounding])
     return out
 
 

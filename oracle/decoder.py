@@ -36,8 +36,16 @@ def _lin(x, w, tp=1):
     return f32_to_bf16(gemm_tpsim(x, w, tp)[0])
 
 
-def decoder_logprobs(w, tokens, cfg, tp=1):
-    """tokens [B, L] int32 -> [B, L-1] fp32 log-probabilities of tokens[:, 1:]."""
+NODES = ("rmsnorm", "rope", "swiglu")
+
+
+def decoder_logprobs(w, tokens, cfg, tp=1, rounding=None):
+    """tokens [B, L] int32 -> [B, L-1] fp32 log-probabilities of tokens[:, 1:].
+
+    rounding: optional {node: "once" | "each_op"} for the nodes RMSNorm, RoPE
+    and SwiGLU (rounding-alignment article, "three nodes"); default "once"."""
+    rd = dict.fromkeys(NODES, "once")
+    rd.update(rounding or {})
     tokens = np.asarray(tokens, np.int32)
     B, L = tokens.shape
     d, H, hd, f = cfg.d, cfg.heads, cfg.head_dim, cfg.ffn
@@ -49,10 +57,10 @@ def decoder_logprobs(w, tokens, cfg, tp=1):
     x = w["emb"][tokens.reshape(-1)]
     resid = np.zeros((T, d), np.uint16)
     for lw in w["layers"]:
-        h, resid = rmsnorm_residual(x, resid, lw["attn_norm"], cfg.eps)
+        h, resid = rmsnorm_residual(x, resid, lw["attn_norm"], cfg.eps, rd["rmsnorm"])
         wq, wk = lw["w_qk"][:d], lw["w_qk"][d:]
-        q = rope(_lin(h, wq).reshape(T, H, hd), pos, cos_t, sin_t)
-        k = rope(_lin(h, wk).reshape(T, H, hd), pos, cos_t, sin_t)
+        q = rope(_lin(h, wq).reshape(T, H, hd), pos, cos_t, sin_t, rd["rope"])
+        k = rope(_lin(h, wk).reshape(T, H, hd), pos, cos_t, sin_t, rd["rope"])
         v = _lin(h, lw["w_v"]).reshape(T, H, hd)
         o = np.empty((T, H, hd), np.uint16)
         for b in range(B):
@@ -62,11 +70,11 @@ def decoder_logprobs(w, tokens, cfg, tp=1):
                 P = softmax_causal(S, 0, scale)                    # [L, L] bf16
                 o[rows, j] = f32_to_bf16(gemm(P, v[rows, j].T))    # P V
         x = _lin(o.reshape(T, d), lw["w_o"], tp)
-        h, resid = rmsnorm_residual(x, resid, lw["mlp_norm"], cfg.eps)
+        h, resid = rmsnorm_residual(x, resid, lw["mlp_norm"], cfg.eps, rd["rmsnorm"])
         g = _lin(h, lw["w_gu"][:f])
         u = _lin(h, lw["w_gu"][f:])
-        x = _lin(swiglu(g, u), lw["w_down"], tp)
-    h, _ = rmsnorm_residual(x, resid, w["final_norm"], cfg.eps)
+        x = _lin(swiglu(g, u, rd["swiglu"]), lw["w_down"], tp)
+    h, _ = rmsnorm_residual(x, resid, w["final_norm"], cfg.eps, rd["rmsnorm"])
     logits = gemm(h, w["lm_head"])
     targets = np.zeros((B, L), np.int32)
     targets[:, :L - 1] = tokens[:, 1:]

@@ -34,7 +34,8 @@
  *  R3 GEMM leaves are 64-wide K blocks, accumulated from +0 in K order;
  *  R4 EXP / LOG are defined by the operation sequences written below
  *     (Cody-Waite reduction plus Taylor polynomials), not by a libm;
- *  R5 two-pass log-softmax with the exact row maximum.
+ *  R5 two-pass log-softmax with the exact row maximum;
+ *  R11 a misaligned rounding location is eager bf16 arithmetic (below).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (x86-64 SSE,
  * round-to-nearest, no FTZ/DAZ), so every float operation is one IEEE
@@ -414,14 +415,26 @@ OR_EXPORT int or_gemm_sampled(const uint16_t *A, int64_t lda, const uint16_t *W,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Rounding locations.  [ROUND] "the problem" and "three nodes": the aligned */
+/* node keeps its intermediates in fp32 and rounds once, at its bf16 output; */
+/* the misaligned stack rounds intermediates to bf16 along the way.  The     */
+/* page does not list which intermediates; the reading taken here (R11) is   */
+/* eager bf16 tensor arithmetic: every elementwise operation on bf16 operands */
+/* is computed in fp32 and rounded to bf16, and fp32 tables are stored as    */
+/* bf16.  `each_op` = 0: round once; 1: round after every operation.         */
+/* ------------------------------------------------------------------------ */
+static float bf_round(float v) { return or_bf16_to_f32(or_f32_to_bf16(v)); }
+
+/* ------------------------------------------------------------------------ */
 /* Residual-add + RMSNorm.  [ROUND] "three nodes": residual RMSNorm keeps    */
 /* fp32 intermediates and rounds to bf16 once at the output.                 */
 /*   h = x + r (fp32); r_out = bf16(h); ss = TREE(h*h); mean = ss/H;         */
 /*   rstd = 1/sqrt(mean + eps); y = bf16((h*rstd)*w).                        */
+/* each_op: h = bf16(x + r) before the norm, n = bf16(h*rstd), y = bf16(n*w). */
 /* ------------------------------------------------------------------------ */
 OR_EXPORT void or_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
                                    uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
-                                   float eps) {
+                                   float eps, int each_op) {
     float *h = (float *)malloc(sizeof(float) * (size_t)H);
     float *sq = (float *)malloc(sizeof(float) * (size_t)H);
     float *scratch = (float *)malloc(sizeof(float) * (size_t)H);
@@ -430,14 +443,18 @@ OR_EXPORT void or_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const u
         const uint16_t *ri = r + (int64_t)i * ld;
         for (int j = 0; j < H; j++) {
             h[j] = or_bf16_to_f32(xi[j]) + or_bf16_to_f32(ri[j]);
+            if (each_op) h[j] = bf_round(h[j]);
             sq[j] = h[j] * h[j];
             r_out[(int64_t)i * ld + j] = or_f32_to_bf16(h[j]);
         }
         float ss = or_tree(sq, H, scratch);
         float mean = ss / (float)H;
         float rstd = 1.0f / sqrtf(mean + eps);
-        for (int j = 0; j < H; j++)
-            y[(int64_t)i * ld + j] = or_f32_to_bf16((h[j] * rstd) * or_bf16_to_f32(w[j]));
+        for (int j = 0; j < H; j++) {
+            float n = h[j] * rstd;
+            if (each_op) n = bf_round(n);
+            y[(int64_t)i * ld + j] = or_f32_to_bf16(n * or_bf16_to_f32(w[j]));
+        }
     }
     free(h); free(sq); free(scratch);
 }
@@ -445,7 +462,9 @@ OR_EXPORT void or_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const u
 /* ------------------------------------------------------------------------ */
 /* RoPE.  [ROUND] "three nodes": the position-encoding node keeps fp32       */
 /* intermediates.  Rotate-half pairing (i, i+d/2); each product rounded to   */
-/* fp32 on its own, one bf16 rounding at the output.                         */
+/* fp32 on its own, one bf16 rounding at the output.  each_op: the table    */
+/* entries are rounded to bf16 and so is every product, then the difference */
+/* and the sum are rounded (rotate_half arithmetic on bf16 tensors).         */
 /* Table: angle(p,i) = p * theta^(-2i/d) in binary64, cos/sin in binary64,   */
 /* one rounding to fp32.                                                     */
 /* ------------------------------------------------------------------------ */
@@ -462,7 +481,8 @@ OR_EXPORT void or_rope_table(double theta, int head_dim, int max_pos, float *cos
 }
 
 OR_EXPORT void or_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
-                       const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token) {
+                       const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+                       int each_op) {
     int half = head_dim / 2;
     for (int t = 0; t < T; t++) {
         int p = pos[t];
@@ -474,7 +494,14 @@ OR_EXPORT void or_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const
                 float s = sin_tab[(int64_t)p * half + i];
                 float a = or_bf16_to_f32(xv[i]);
                 float b = or_bf16_to_f32(xv[i + half]);
-                float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+                float ac, bs, bc, as;
+                if (each_op) {
+                    c = bf_round(c); s = bf_round(s);
+                    ac = bf_round(a * c); bs = bf_round(b * s);
+                    bc = bf_round(b * c); as = bf_round(a * s);
+                } else {
+                    ac = a * c; bs = b * s; bc = b * c; as = a * s;
+                }
                 yv[i] = or_f32_to_bf16(ac - bs);
                 yv[i + half] = or_f32_to_bf16(bc + as);
             }
@@ -485,15 +512,17 @@ OR_EXPORT void or_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const
 /* ------------------------------------------------------------------------ */
 /* SwiGLU.  [ROUND] "three nodes": the gated activation keeps fp32          */
 /* intermediates.  y = bf16((g / (1 + EXP(-g))) * u).                        */
+/* each_op: the activation is rounded first, y = bf16(bf16(silu(g)) * u).    */
 /* ------------------------------------------------------------------------ */
 OR_EXPORT void or_swiglu(const uint16_t *gate, const uint16_t *up, uint16_t *out, int rows,
-                         int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out) {
+                         int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out, int each_op) {
     for (int i = 0; i < rows; i++)
         for (int j = 0; j < cols; j++) {
             float g = or_bf16_to_f32(gate[(int64_t)i * ld_gate + j]);
             float u = or_bf16_to_f32(up[(int64_t)i * ld_up + j]);
             float den = 1.0f + or_expf(-g);
             float silu = g / den;
+            if (each_op) silu = bf_round(silu);
             out[(int64_t)i * ld_out + j] = or_f32_to_bf16(silu * u);
         }
 }

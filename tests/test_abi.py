@@ -163,6 +163,14 @@ def test_rowop_validation(L):
     assert sw(FAKE, None, FAKE, 1, 8, 8, 8, 8, None) == E_NULL
     assert sw(FAKE, FAKE, FAKE, 1, 16, 8, 16, 16, None) == E_SHAPE
     assert sw(FAKE, FAKE, MISAL, 1, 8, 8, 8, 8, None) == E_ALIGN
+    # rounding location: only TBIK_ROUND_ONCE (0) and TBIK_ROUND_EACH_OP (1)
+    assert L.tbik_rmsnorm_residual_ex(FAKE, FAKE, FAKE, FAKE2, None, 1, 64, 64, 1e-6, 2,
+                                      None) == E_ARG
+    assert L.tbik_rope_ex(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 128, 128, 16, -1, None) == E_ARG
+    assert L.tbik_swiglu_ex(FAKE, FAKE, FAKE2, 1, 8, 8, 8, 8, 7, None) == E_ARG
+    assert L.tbik_swiglu_ex(FAKE, None, FAKE, 1, 8, 8, 8, 8, 1, None) == E_NULL
+    assert L.tbik_rmsnorm_residual_ex(FAKE, FAKE, FAKE, FAKE2, None, 0, 64, 64, 1e-6, 1,
+                                      None) == OK
     ls = L.tbik_logsoftmax_gather
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 3, FAKE, 1 << 20, None) == E_TP
     assert ls(FAKE, 24, FAKE, FAKE, 2, 12, 8, FAKE, 1 << 20, None) == E_TP   # T(12) = 4

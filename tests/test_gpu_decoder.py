@@ -68,6 +68,22 @@ def test_decoder_mfma_small(small):
     assert err.mean() <= 0.05 and err.max() <= 0.25, (err.mean(), err.max())
 
 
+@pytest.mark.parametrize("rd", [{"rope": "each_op"},
+                                {"rmsnorm": "each_op", "rope": "each_op", "swiglu": "each_op"}])
+def test_decoder_rounding_location_scalar_bitexact(small, rd):
+    """Misaligned rounding locations (rounding-alignment article, "three
+    nodes") through the GPU composition equal the oracle's, bit for bit."""
+    w, tok, ref = small
+    say("decoder scalar leaf, rounding", rd)
+    w_np = {"emb": inputs.bits(w["emb"].cpu()), "lm_head": inputs.bits(w["lm_head"].cpu()),
+            "final_norm": inputs.bits(w["final_norm"].cpu()),
+            "layers": [{k: inputs.bits(v.cpu()) for k, v in lw.items()} for lw in w["layers"]]}
+    refv = od.decoder_logprobs(w_np, tok.cpu().numpy(), SMALL, rounding=rd)
+    lp = decoder_forward(w, tok, SMALL, tp=1, leaf_mode=tb.LEAF_SCALAR, rounding=rd)
+    assert np.array_equal(u32(lp), refv.view(np.uint32))
+    assert not np.array_equal(refv.view(np.uint32), ref.view(np.uint32))
+
+
 @pytest.fixture(scope="module")
 def full():
     cfg = inputs.DecoderConfig()
@@ -84,6 +100,17 @@ def test_decoder_full_tp_invariant(full):
     lp4 = decoder_forward(w, tok, cfg, tp=4)
     assert torch.isfinite(lp1).all()
     assert np.array_equal(u32(lp1), u32(lp4))
+
+
+def test_decoder_full_rounding_variant_tp_invariant(full):
+    cfg, w, tok = full
+    rd = {"rmsnorm": "each_op", "rope": "each_op", "swiglu": "each_op"}
+    say("decoder full, all nodes each_op, tp1 / tp4")
+    lp1 = decoder_forward(w, tok, cfg, tp=1, rounding=rd)
+    lp4 = decoder_forward(w, tok, cfg, tp=4, rounding=rd)
+    assert np.array_equal(u32(lp1), u32(lp4))
+    lp0 = decoder_forward(w, tok, cfg, tp=1)
+    assert not np.array_equal(u32(lp1), u32(lp0))
 
 
 def test_decoder_full_batch_invariant(full):

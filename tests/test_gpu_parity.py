@@ -538,3 +538,41 @@ def test_gemm_group11_schedule(orc, M, N):
     Af = Ai.float().cpu().numpy().astype(np.float64)
     Wf = Wi.float().cpu().numpy().astype(np.float64)
     assert np.array_equal(Ci[rr, cc], (Af[rows] @ Wf[cols].T))
+
+
+# ------------------------------------------------------------------ rounding locations
+# (rounding-alignment article, "three nodes": the misaligned stack rounds
+# intermediates to bf16; TBIK_ROUND_EACH_OP is that stack as eager bf16
+# arithmetic, bit-exact against the oracle's variant)
+@pytest.mark.parametrize("rows,H", [(7, 4096), (300, 4096), (3, 5120), (2, 16384), (4, 1000)])
+def test_rmsnorm_each_op_bitexact(orc, rows, H):
+    x = inputs.outlier_bf16((rows, H), 8300 + H)
+    r = inputs.outlier_bf16((rows, H), 8301 + H)
+    w = inputs.normal_bf16((H,), 8302 + H, std=0.1, mean=1.0)
+    say("rmsnorm each_op", rows, H)
+    y, r_out = tb.tbik_rmsnorm_residual(x.to(DEV), r.to(DEV), w.to(DEV), 1e-6, rounding="each_op")
+    ry, rr = orc.rmsnorm_residual(bits(x), bits(r), bits(w), 1e-6, rounding="each_op")
+    assert np.array_equal(bits(y), ry)
+    assert np.array_equal(bits(r_out), rr)
+    y0, _ = tb.tbik_rmsnorm_residual(x.to(DEV), r.to(DEV), w.to(DEV), 1e-6)
+    assert np.count_nonzero(bits(y0) != ry) > 0
+
+
+@pytest.mark.parametrize("T,heads,d", [(2048, 16, 128), (33, 3, 64)])
+def test_rope_each_op_bitexact(orc, T, heads, d):
+    x = inputs.normal_bf16((T, heads, d), 9200 + T)
+    pos = inputs.positions(T, 32768, seed=11)
+    c, s = orc.rope_table(1e6, d, 32768)
+    say("rope each_op", T, heads, d)
+    y = tb.tbik_rope(x.to(DEV), pos.to(DEV), torch.from_numpy(c).to(DEV),
+                     torch.from_numpy(s).to(DEV), rounding="each_op")
+    assert np.array_equal(bits(y), orc.rope(bits(x), pos.numpy(), c, s, rounding="each_op"))
+
+
+@pytest.mark.parametrize("rows,cols", [(512, 14336), (3, 17)])
+def test_swiglu_each_op_bitexact(orc, rows, cols):
+    g = inputs.normal_bf16((rows, cols), 9800 + rows, std=3.0)
+    u = inputs.normal_bf16((rows, cols), 9801 + rows)
+    say("swiglu each_op", rows, cols)
+    y = tb.tbik_swiglu(g.to(DEV), u.to(DEV), rounding="each_op")
+    assert np.array_equal(bits(y), orc.swiglu(bits(g), bits(u), rounding="each_op"))

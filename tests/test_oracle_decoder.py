@@ -131,3 +131,28 @@ def test_decoder_tp_invariant(setup, tp):
     w, tok, lp = setup
     lpt = od.decoder_logprobs(w, tok, CFG, tp=tp)
     assert np.array_equal(lp.view(np.uint32), lpt.view(np.uint32))
+
+
+# --------------------------------------------------------------------------
+# rounding locations (rounding-alignment article, "three nodes")
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("nodes", [("rope",), ("swiglu",), ("rmsnorm",),
+                                   ("rmsnorm", "rope", "swiglu")])
+def test_decoder_rounding_location_gap(setup, nodes):
+    """Rounding the intermediates of a node to bf16 moves the logprobs (the
+    train/inference mismatch the article traces to these nodes) but not past
+    bf16 rounding noise, and the tree kernels keep every variant tp-invariant."""
+    w, tok, lp = setup
+    rd = dict.fromkeys(nodes, "each_op")
+    lpv = od.decoder_logprobs(w, tok, CFG, rounding=rd)
+    assert np.count_nonzero(lpv.view(np.uint32) != lp.view(np.uint32)) > 0
+    err = np.abs(lpv.astype(np.float64) - f64_decoder(w, tok, CFG))
+    assert err.mean() <= MEAN_TOL and err.max() <= MAX_TOL, (err.mean(), err.max())
+    lpt = od.decoder_logprobs(w, tok, CFG, tp=2, rounding=rd)
+    assert np.array_equal(lpv.view(np.uint32), lpt.view(np.uint32))
+
+
+def test_decoder_rounding_once_is_default(setup):
+    w, tok, lp = setup
+    lpo = od.decoder_logprobs(w, tok, CFG, rounding=dict.fromkeys(od.NODES, "once"))
+    assert np.array_equal(lpo.view(np.uint32), lp.view(np.uint32))

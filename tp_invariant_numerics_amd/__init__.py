@@ -20,12 +20,15 @@ __all__ = [
     "tbik_gemm_strided_batched", "tbik_gemm_tpsim", "tbik_gemm_tpsim_workspace_bytes",
     "tbik_tree_combine", "tbik_gemm_tp_partials", "tbik_gemm_shard", "tbik_rmsnorm_residual", "tbik_rope", "tbik_rope_table",
     "tbik_swiglu", "tbik_logsoftmax_gather", "tbik_logsoftmax_workspace_bytes",
-    "tbik_softmax_causal", "tbik_primitive", "LEAF_MFMA", "LEAF_SCALAR",
+    "tbik_softmax_causal", "tbik_primitive", "LEAF_MFMA", "LEAF_SCALAR", "ROUNDING",
 ]
 
 LEAF_MFMA = 0
 LEAF_SCALAR = 1
 PRIM_EXP, PRIM_LOG, PRIM_BF16, PRIM_SILU = 0, 1, 2, 3
+# rounding location of RMSNorm, RoPE and SwiGLU: fp32 intermediates rounded
+# once at the output, or bf16 after every elementwise operation
+ROUNDING = {"once": 0, "each_op": 1}
 
 _lib = None
 
@@ -65,6 +68,9 @@ def _sigs():
         "tbik_rope": (i32, [p, p, p, p, p, i32, i32, i32, i64, i32, p]),
         "tbik_rope_table": (i32, [f64, i32, i32, p, p]),
         "tbik_swiglu": (i32, [p, p, p, i32, i32, i64, i64, i64, p]),
+        "tbik_rmsnorm_residual_ex": (i32, [p, p, p, p, p, i32, i32, i64, f32, i32, p]),
+        "tbik_rope_ex": (i32, [p, p, p, p, p, i32, i32, i32, i64, i32, i32, p]),
+        "tbik_swiglu_ex": (i32, [p, p, p, i32, i32, i64, i64, i64, i32, p]),
         "tbik_logsoftmax_workspace_bytes": (sz, [i32, i32, i32]),
         "tbik_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p, sz, p]),
         "tbik_softmax_causal": (i32, [p, i64, i64, p, i64, i64, i32, i32, i32, i32, f32, p]),
@@ -255,7 +261,8 @@ def tbik_tree_combine(ws, out=None, out_bf16=None):
 
 # --- row ops ------------------------------------------------------------------
 
-def tbik_rmsnorm_residual(x, r, w, eps=1e-6, y=None, r_out=None, want_r_out=True):
+def tbik_rmsnorm_residual(x, r, w, eps=1e-6, y=None, r_out=None, want_r_out=True,
+                          rounding="once"):
     _bits(x); _bits(r); _bits(w); _need_gpu(x, r, w)
     rows, H = x.shape
     ld = _ld(x)
@@ -265,13 +272,13 @@ def tbik_rmsnorm_residual(x, r, w, eps=1e-6, y=None, r_out=None, want_r_out=True
         y = torch.empty_like(x)
     if r_out is None and want_r_out:
         r_out = torch.empty_like(x)
-    rc = lib().tbik_rmsnorm_residual(_ptr(x), _ptr(r), _ptr(w), _ptr(y), _ptr(r_out), rows, H, ld,
-                                     float(eps), _stream())
+    rc = lib().tbik_rmsnorm_residual_ex(_ptr(x), _ptr(r), _ptr(w), _ptr(y), _ptr(r_out), rows, H,
+                                        ld, float(eps), ROUNDING[rounding], _stream())
     _chk(rc, "tbik_rmsnorm_residual")
     return y, r_out
 
 
-def tbik_rope(x, pos, cos_tab, sin_tab, y=None):
+def tbik_rope(x, pos, cos_tab, sin_tab, y=None, rounding="once"):
     """x [T, heads, d] bf16 (heads contiguous); pos [T] int32; tables [max_pos, d/2]."""
     _bits(x); _need_gpu(x, pos, cos_tab, sin_tab)
     T, heads, d = x.shape
@@ -279,8 +286,8 @@ def tbik_rope(x, pos, cos_tab, sin_tab, y=None):
         raise ValueError("heads must be contiguous with stride head_dim")
     if y is None:
         y = torch.empty_like(x)
-    rc = lib().tbik_rope(_ptr(x), _ptr(y), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T, heads, d,
-                         x.stride(0), cos_tab.shape[0], _stream())
+    rc = lib().tbik_rope_ex(_ptr(x), _ptr(y), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T, heads,
+                            d, x.stride(0), cos_tab.shape[0], ROUNDING[rounding], _stream())
     _chk(rc, "tbik_rope")
     return y
 
@@ -295,13 +302,13 @@ def tbik_rope_table(theta, head_dim, max_pos):
     return c, s
 
 
-def tbik_swiglu(gate, up, out=None):
+def tbik_swiglu(gate, up, out=None, rounding="once"):
     _bits(gate); _bits(up); _need_gpu(gate, up)
     rows, cols = gate.shape
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=gate.device)
-    rc = lib().tbik_swiglu(_ptr(gate), _ptr(up), _ptr(out), rows, cols, _ld(gate), _ld(up),
-                           _ld(out), _stream())
+    rc = lib().tbik_swiglu_ex(_ptr(gate), _ptr(up), _ptr(out), rows, cols, _ld(gate), _ld(up),
+                              _ld(out), ROUNDING[rounding], _stream())
     _chk(rc, "tbik_swiglu")
     return out
 

@@ -177,7 +177,9 @@ static int cap_f32(int ch, int align) {
 // =============================================================================
 constexpr int kRowThreads = 256;
 
-template <int CH>
+// EACH (the misaligned rounding location): h = bf16(x + r) before the norm
+// and n = bf16(h * rstd) before the weight, as eager bf16 arithmetic does.
+template <int CH, bool EACH>
 __global__ void __launch_bounds__(kRowThreads)
 k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, uint16_t *r_out,
           int H, int64_t ld, float eps, int T) {
@@ -194,6 +196,7 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       a[e] = a[e] + b[e];          // h
+      if (EACH) a[e] = bf_round(a[e]);
       sq[e] = a[e] * a[e];
     }
     if (r_out) store_bf16<CH>(r_out + base + ch * CH, a);
@@ -209,7 +212,13 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
     load_bf16<CH>(b, rr + ch * CH);
     load_bf16<CH>(ww, w + ch * CH);
 #pragma unroll
-    for (int e = 0; e < CH; ++e) a[e] = ((a[e] + b[e]) * rstd) * ww[e];
+    for (int e = 0; e < CH; ++e) {
+      float h = a[e] + b[e];
+      if (EACH) h = bf_round(h);
+      float n = h * rstd;
+      if (EACH) n = bf_round(n);
+      a[e] = n * ww[e];
+    }
     store_bf16<CH>(y + base + ch * CH, a);
   }
 }
@@ -221,7 +230,7 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
 // is a perfect tree evaluated as a butterfly over those lanes (xor 1, 2, 4,
 // ...; every lane ends with the same bits since IEEE addition commutes).
 // The T group sums meet in LDS for the top perfect tree.
-template <int CH>
+template <int CH, bool EACH>
 __global__ void __launch_bounds__(kRowThreads)
 k_rmsnorm_reg(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y,
               uint16_t *r_out, int H, int64_t ld, float eps, int T, int gc) {
@@ -240,6 +249,7 @@ k_rmsnorm_reg(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t 
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       h[e] = h[e] + b[e];
+      if (EACH) h[e] = bf_round(h[e]);
       sq[e] = h[e] * h[e];
     }
     if (r_out) store_bf16<CH>(r_out + off, h);
@@ -259,12 +269,17 @@ k_rmsnorm_reg(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t 
   const float rstd = 1.0f / __builtin_sqrtf(mean + eps);
   if (own) {
 #pragma unroll
-    for (int e = 0; e < CH; ++e) h[e] = (h[e] * rstd) * ww[e];
+    for (int e = 0; e < CH; ++e) {
+      float n = h[e] * rstd;
+      if (EACH) n = bf_round(n);
+      h[e] = n * ww[e];
+    }
     store_bf16<CH>(y + off, h);
   }
 }
 
-int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+template <bool EACH>
+static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t *w,
                             uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
                             float eps, hipStream_t s) {
   const int T = tree_T(H);
@@ -280,29 +295,40 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
   dim3 grid((unsigned)rows), block(kRowThreads);
   if (nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
     switch (ch) {
-      case 16: hipLaunchKernelGGL(k_rmsnorm_reg<16>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
-      case 8: hipLaunchKernelGGL(k_rmsnorm_reg<8>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
-      case 4: hipLaunchKernelGGL(k_rmsnorm_reg<4>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
-      case 2: hipLaunchKernelGGL(k_rmsnorm_reg<2>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
-      default: hipLaunchKernelGGL(k_rmsnorm_reg<1>, grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 16: hipLaunchKernelGGL((k_rmsnorm_reg<16, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 8: hipLaunchKernelGGL((k_rmsnorm_reg<8, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 4: hipLaunchKernelGGL((k_rmsnorm_reg<4, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      case 2: hipLaunchKernelGGL((k_rmsnorm_reg<2, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
+      default: hipLaunchKernelGGL((k_rmsnorm_reg<1, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
     }
     return check_launch();
   }
   const size_t lds = 2 * (size_t)nch * sizeof(float);
   switch (ch) {
-    case 16: hipLaunchKernelGGL(k_rmsnorm<16>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    case 8: hipLaunchKernelGGL(k_rmsnorm<8>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    case 4: hipLaunchKernelGGL(k_rmsnorm<4>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    case 2: hipLaunchKernelGGL(k_rmsnorm<2>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    default: hipLaunchKernelGGL(k_rmsnorm<1>, grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 16: hipLaunchKernelGGL((k_rmsnorm<16, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 8: hipLaunchKernelGGL((k_rmsnorm<8, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 4: hipLaunchKernelGGL((k_rmsnorm<4, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    case 2: hipLaunchKernelGGL((k_rmsnorm<2, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+    default: hipLaunchKernelGGL((k_rmsnorm<1, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
   }
   return check_launch();
+}
+
+int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+                            uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
+                            float eps, int rounding, hipStream_t s) {
+  return rounding == TBIK_ROUND_EACH_OP
+             ? launch_rmsnorm_t<true>(x, r, w, y, r_out, rows, H, ld, eps, s)
+             : launch_rmsnorm_t<false>(x, r, w, y, r_out, rows, H, ld, eps, s);
 }
 
 // =============================================================================
 // RoPE (rotate-half).  One thread = 4 consecutive pairs (i..i+3, i+h..i+h+3);
 // grid.x covers the (head, pair-quad) items of one token, grid.y the tokens.
 // =============================================================================
+// EACH: table entries and every product rounded to bf16 before the
+// difference and the sum (rotate_half arithmetic on bf16 tensors).
+template <bool EACH>
 __global__ void __launch_bounds__(256)
 k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
        const float *sin_tab, int T, int heads, int half, int64_t ld_token, int max_pos,
@@ -318,8 +344,15 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
     const int64_t off = (int64_t)t * ld_token + (int64_t)hd * 2 * half + i;
     const u32x2 ua = vload<true>(reinterpret_cast<const u32x2 *>(x + off));
     const u32x2 ub = vload<true>(reinterpret_cast<const u32x2 *>(x + off + half));
-    const f32x4 c = *reinterpret_cast<const f32x4 *>(cos_tab + (int64_t)p * half + i);
-    const f32x4 sn = *reinterpret_cast<const f32x4 *>(sin_tab + (int64_t)p * half + i);
+    f32x4 c = *reinterpret_cast<const f32x4 *>(cos_tab + (int64_t)p * half + i);
+    f32x4 sn = *reinterpret_cast<const f32x4 *>(sin_tab + (int64_t)p * half + i);
+    if constexpr (EACH) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = bf_round(c[e]);
+        sn[e] = bf_round(sn[e]);
+      }
+    }
     const float a[4] = {__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
                         __uint_as_float(ua[1] << 16), __uint_as_float(ua[1] & 0xffff0000u)};
     const float b[4] = {__uint_as_float(ub[0] << 16), __uint_as_float(ub[0] & 0xffff0000u),
@@ -327,8 +360,14 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
     float ya[4], yb[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float ac = a[e] * c[e], bs = b[e] * sn[e];
-      const float bc = b[e] * c[e], as = a[e] * sn[e];
+      float ac = a[e] * c[e], bs = b[e] * sn[e];
+      float bc = b[e] * c[e], as = a[e] * sn[e];
+      if constexpr (EACH) {
+        ac = bf_round(ac);
+        bs = bf_round(bs);
+        bc = bf_round(bc);
+        as = bf_round(as);
+      }
       ya[e] = ac - bs;
       yb[e] = bc + as;
     }
@@ -344,7 +383,7 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
 
 int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
                 const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
-                int max_pos, hipStream_t s) {
+                int max_pos, int rounding, hipStream_t s) {
   if (T == 0) return TBIK_OK;
   const int half = head_dim / 2;
   const int q4 = half / 4;
@@ -354,8 +393,12 @@ int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float 
     if ((1 << b) == q4) q4_shift = b;
   const unsigned gx = (unsigned)((items + 255) / 256);
   const unsigned gy = (unsigned)(T < 65535 ? T : 65535);
-  hipLaunchKernelGGL(k_rope, dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab, T, heads,
-                     half, ld_token, max_pos, q4_shift);
+  if (rounding == TBIK_ROUND_EACH_OP)
+    hipLaunchKernelGGL((k_rope<true>), dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab, T,
+                       heads, half, ld_token, max_pos, q4_shift);
+  else
+    hipLaunchKernelGGL((k_rope<false>), dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab, T,
+                       heads, half, ld_token, max_pos, q4_shift);
   return check_launch();
 }
 
@@ -414,7 +457,8 @@ __device__ __forceinline__ float silu(float g) {
 }
 
 // grid.x covers the 8-element items of a row, grid.y the rows.
-template <bool VEC>
+// EACH: the activation is rounded to bf16 before the product with u.
+template <bool VEC, bool EACH>
 __global__ void __launch_bounds__(256)
 k_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols, int64_t ldg,
          int64_t ldu, int64_t ldo) {
@@ -428,26 +472,32 @@ k_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols, 
       load_bf16<8, true>(uv, u + (int64_t)row * ldu + col);
       silu_n<8>(gv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) gv[e] = gv[e] * uv[e];
+      for (int e = 0; e < 8; ++e) gv[e] = (EACH ? bf_round(gv[e]) : gv[e]) * uv[e];
       store_bf16<8, true>(o + (int64_t)row * ldo + col, gv);
     } else {
-      o[(int64_t)row * ldo + col] =
-          f2bf(silu(bf2f(g[(int64_t)row * ldg + col])) * bf2f(u[(int64_t)row * ldu + col]));
+      float a = silu(bf2f(g[(int64_t)row * ldg + col]));
+      if (EACH) a = bf_round(a);
+      o[(int64_t)row * ldo + col] = f2bf(a * bf2f(u[(int64_t)row * ldu + col]));
     }
   }
 }
 
 int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
-                  int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s) {
+                  int64_t ldg, int64_t ldu, int64_t ldo, int rounding, hipStream_t s) {
   if (rows == 0 || cols == 0) return TBIK_OK;
   const bool vec = (cols % 8) == 0 && elem_align(g, ldg, 2) >= 8 && elem_align(u, ldu, 2) >= 8 &&
                    elem_align(o, ldo, 2) >= 8;
   const int items = vec ? cols / 8 : cols;
   const dim3 grid((unsigned)((items + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
-  if (vec)
-    hipLaunchKernelGGL(k_swiglu<true>, grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+  const bool each = rounding == TBIK_ROUND_EACH_OP;
+  if (vec && each)
+    hipLaunchKernelGGL((k_swiglu<true, true>), grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+  else if (vec)
+    hipLaunchKernelGGL((k_swiglu<true, false>), grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+  else if (each)
+    hipLaunchKernelGGL((k_swiglu<false, true>), grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
   else
-    hipLaunchKernelGGL(k_swiglu<false>, grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
+    hipLaunchKernelGGL((k_swiglu<false, false>), grid, dim3(256), 0, s, g, u, o, rows, cols, ldg, ldu, ldo);
   return check_launch();
 }
 

@@ -184,23 +184,43 @@ int tbik_tree_combine(const float *ws, int tp, float *C, int64_t ldc, tbik_bf16 
   return tbik::launch_tree_combine(ws, tp, C, ldc, C_bf16, M, N, as_stream(stream));
 }
 
+static bool rounding_ok(int rounding) {
+  return rounding == TBIK_ROUND_ONCE || rounding == TBIK_ROUND_EACH_OP;
+}
+
 int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
                           tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld, float eps,
                           void *stream) {
+  return tbik_rmsnorm_residual_ex(x, r, w, y, r_out, rows, H, ld, eps, TBIK_ROUND_ONCE, stream);
+}
+
+int tbik_rmsnorm_residual_ex(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
+                             tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,
+                             float eps, int rounding, void *stream) {
   if (!x || !r || !w || !y) return TBIK_ERR_NULL;
+  if (!rounding_ok(rounding)) return TBIK_ERR_ARG;
   if (rows < 0 || H < 1 || H > 65536 || ld < H) return TBIK_ERR_SHAPE;
   if (!(eps >= 0.0f) || isinf(eps)) return TBIK_ERR_ARG;
   if (!aligned(x, 2) || !aligned(r, 2) || !aligned(w, 2) || !aligned(y, 2) ||
       (r_out && !aligned(r_out, 2)))
     return TBIK_ERR_ALIGN;
   if (rows == 0) return TBIK_OK;
-  return tbik::launch_rmsnorm_residual(x, r, w, y, r_out, rows, H, ld, eps, as_stream(stream));
+  return tbik::launch_rmsnorm_residual(x, r, w, y, r_out, rows, H, ld, eps, rounding,
+                                       as_stream(stream));
 }
 
 int tbik_rope(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float *cos_tab,
               const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
               int max_pos, void *stream) {
+  return tbik_rope_ex(x, y, pos, cos_tab, sin_tab, T, heads, head_dim, ld_token, max_pos,
+                      TBIK_ROUND_ONCE, stream);
+}
+
+int tbik_rope_ex(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float *cos_tab,
+                 const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
+                 int max_pos, int rounding, void *stream) {
   if (!x || !y || !pos || !cos_tab || !sin_tab) return TBIK_ERR_NULL;
+  if (!rounding_ok(rounding)) return TBIK_ERR_ARG;
   if (T < 0 || heads < 1 || max_pos < 1) return TBIK_ERR_SHAPE;
   if (head_dim < 2 || head_dim > 1024 || (head_dim % 8) != 0) return TBIK_ERR_SHAPE;
   if (ld_token < (int64_t)heads * head_dim) return TBIK_ERR_SHAPE;
@@ -210,7 +230,7 @@ int tbik_rope(const tbik_bf16 *x, tbik_bf16 *y, const int32_t *pos, const float 
     return TBIK_ERR_ALIGN;
   if (T == 0) return TBIK_OK;
   return tbik::launch_rope(x, y, pos, cos_tab, sin_tab, T, heads, head_dim, ld_token, max_pos,
-                           as_stream(stream));
+                           rounding, as_stream(stream));
 }
 
 int tbik_rope_table(double theta, int head_dim, int max_pos, float *cos_tab, float *sin_tab) {
@@ -231,12 +251,20 @@ int tbik_rope_table(double theta, int head_dim, int max_pos, float *cos_tab, flo
 
 int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows, int cols,
                 int64_t ld_gate, int64_t ld_up, int64_t ld_out, void *stream) {
+  return tbik_swiglu_ex(gate, up, out, rows, cols, ld_gate, ld_up, ld_out, TBIK_ROUND_ONCE,
+                        stream);
+}
+
+int tbik_swiglu_ex(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows,
+                   int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out, int rounding,
+                   void *stream) {
   if (!gate || !up || !out) return TBIK_ERR_NULL;
+  if (!rounding_ok(rounding)) return TBIK_ERR_ARG;
   if (rows < 0 || cols < 0 || ld_gate < cols || ld_up < cols || ld_out < cols)
     return TBIK_ERR_SHAPE;
   if (!aligned(gate, 2) || !aligned(up, 2) || !aligned(out, 2)) return TBIK_ERR_ALIGN;
   if (rows == 0 || cols == 0) return TBIK_OK;
-  return tbik::launch_swiglu(gate, up, out, rows, cols, ld_gate, ld_up, ld_out,
+  return tbik::launch_swiglu(gate, up, out, rows, cols, ld_gate, ld_up, ld_out, rounding,
                              as_stream(stream));
 }
 

@@ -33,6 +33,10 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
 // Two conversions in one instruction: a in the low half, b in the high half.
+// v rounded to the nearest bf16 and widened back: one bf16 operation of
+// eager bf16 arithmetic (the misaligned rounding location of a node)
+__device__ __forceinline__ float bf_round(float v) { return bf2f(f2bf(v)); }
+
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const f32x2 v = {a, b};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));

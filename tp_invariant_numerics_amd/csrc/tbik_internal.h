@@ -32,12 +32,12 @@ int launch_tree_combine(const float *ws, int tp, float *C, int64_t ldc, uint16_t
                         int N, hipStream_t s);
 int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t *w,
                             uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
-                            float eps, hipStream_t s);
+                            float eps, int rounding, hipStream_t s);
 int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
                 const float *sin_tab, int T, int heads, int head_dim, int64_t ld_token,
-                int max_pos, hipStream_t s);
+                int max_pos, int rounding, hipStream_t s);
 int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
-                  int64_t ldg, int64_t ldu, int64_t ldo, hipStream_t s);
+                  int64_t ldg, int64_t ldu, int64_t ldo, int rounding, hipStream_t s);
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out,
                       int M, int V, int tp, float *ws, const float *pmax, int64_t ld_pmax,
                       int npmax, hipStream_t s);

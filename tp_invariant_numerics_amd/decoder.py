@@ -34,10 +34,24 @@ import math
 
 import torch
 
-from . import lib, _chk, _stream, LEAF_MFMA
+from . import lib, _chk, _stream, LEAF_MFMA, ROUNDING
 from .inputs import DecoderConfig  # noqa: F401  (re-exported for callers)
 
-__all__ = ["decoder_forward", "DecoderConfig"]
+__all__ = ["decoder_forward", "DecoderConfig", "NODES"]
+
+# the three nodes whose rounding location the rounding-alignment article
+# studies; each is "once" (fp32 intermediates) or "each_op" (eager bf16)
+NODES = ("rmsnorm", "rope", "swiglu")
+
+
+def _rounding_codes(rounding):
+    rd = dict.fromkeys(NODES, "once")
+    if rounding:
+        unknown = set(rounding) - set(NODES)
+        if unknown:
+            raise ValueError("unknown rounding nodes: %s" % sorted(unknown))
+        rd.update(rounding)
+    return {k: ROUNDING[v] for k, v in rd.items()}
 
 
 def _p(t, off=0):
@@ -79,9 +93,11 @@ def _rope_tables(theta, hd, L, dev):
     return _ROPE[key]
 
 
-def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA):
+def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA, rounding=None):
     """tokens [B, L] int32 on the device -> logprobs [B, L-1] fp32 of
-    tokens[:, 1:] given their prefixes."""
+    tokens[:, 1:] given their prefixes.  rounding: optional {node: "once" |
+    "each_op"} for the nodes in NODES (default: all "once")."""
+    rc_of = _rounding_codes(rounding)
     B, L = tokens.shape
     d, H, hd, f, V = cfg.d, cfg.heads, cfg.head_dim, cfg.ffn, cfg.vocab
     T = B * L
@@ -113,9 +129,9 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA):
 
     def norm(xin, w):
         nonlocal resid, resid2
-        rc = L_.tbik_rmsnorm_residual(_p(xin), _p(resid), _p(w), _p(h), _p(resid2), T, d, d,
-                                      float(cfg.eps), st)
-        _chk(rc, "tbik_rmsnorm_residual")
+        rc = L_.tbik_rmsnorm_residual_ex(_p(xin), _p(resid), _p(w), _p(h), _p(resid2), T, d, d,
+                                         float(cfg.eps), rc_of["rmsnorm"], st)
+        _chk(rc, "tbik_rmsnorm_residual_ex")
         resid, resid2 = resid2, resid
 
     for lw in weights["layers"]:
@@ -123,9 +139,9 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA):
         _gemm(h, d, lw["w_qk"], d, None, qk, 2 * d, T, 2 * d, d, leaf_mode)
         _gemm(lw["w_v"], d, h, d, None, vT, T, d, T, d, leaf_mode)
         for off in (0, d):                       # q, then k, rotated in place
-            rc = L_.tbik_rope(_p(qk, off), _p(qk, off), _p(pos), _p(c_tab), _p(s_tab), T, H, hd,
-                              2 * d, L, st)
-            _chk(rc, "tbik_rope")
+            rc = L_.tbik_rope_ex(_p(qk, off), _p(qk, off), _p(pos), _p(c_tab), _p(s_tab), T, H,
+                                 hd, 2 * d, L, rc_of["rope"], st)
+            _chk(rc, "tbik_rope_ex")
         if leaf_mode == LEAF_MFMA and hd == 128 and L in (64, 128, 256, 512):
             # fused kernel: the same bits as the three steps below, without
             # the score matrix in HBM
@@ -149,8 +165,8 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA):
         _gemm_rowpar(attn, lw["w_o"], x, tp, leaf_mode, ws)
         norm(x, lw["mlp_norm"])
         _gemm(h, d, lw["w_gu"], d, None, gu, 2 * f, T, 2 * f, d, leaf_mode)
-        rc = L_.tbik_swiglu(_p(gu), _p(gu, f), _p(a), T, f, 2 * f, 2 * f, f, st)
-        _chk(rc, "tbik_swiglu")
+        rc = L_.tbik_swiglu_ex(_p(gu), _p(gu, f), _p(a), T, f, 2 * f, 2 * f, f, rc_of["swiglu"], st)
+        _chk(rc, "tbik_swiglu_ex")
         _gemm_rowpar(a, lw["w_down"], x, tp, leaf_mode, ws)
     norm(x, weights["final_norm"])
     lm = weights["lm_head"]
