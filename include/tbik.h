@@ -354,6 +354,81 @@ enum { TBIK_PRIM_EXP = 0, TBIK_PRIM_LOG = 1, TBIK_PRIM_BF16 = 2, TBIK_PRIM_SILU 
 
 int tbik_primitive(int op, const float *x, float *y, int64_t n, void *stream);
 
+/* ========================================================================
+ * Training side ([TBIK] Abstract: the trainer -- FSDP, TP = 1 -- and the
+ * inference engine must give bit-identical results; [ROUND] "three nodes":
+ * fp32 intermediates, one bf16 rounding per output).  The pages give no
+ * backward formulas: each backward below is the derivative of the forward
+ * definition above, in fp32, in the order written.  Sums over tokens are
+ * TREE over 64-token leaves, so a data-parallel split of the tokens into dp
+ * ranks (dp in {1,2,4,8} dividing T of the leaf count) is a split at aligned
+ * groups, and the result is bit-identical for every dp; dp simulates that
+ * split on one GPU (shard nodes, then the top of the tree).
+ * ====================================================================== */
+
+/* y = x^T: x [rows, cols] bf16 (row stride ldx) -> y [cols, rows] bf16
+ * (row stride ldy).  Bits are copied.  rows <= 4194240. */
+int tbik_transpose_bf16(const tbik_bf16 *x, int64_t ldx, tbik_bf16 *y, int64_t ldy, int rows,
+                        int cols, void *stream);
+
+/* Input gradient of Y = X W^T:  dX = dY W, i.e. dX[m,k] = TREE_n(dY[m,n] W[n,k])
+ * over the N/64 leaves of n (the forward GEMM's tree with N as the reduced
+ * dimension).  dY [M,N] (ld_dy), W [N,K] (ldw), dX [M,K] fp32 (ld_dx) and/or
+ * dX_bf16 (same ld).  N must be a positive multiple of 64.  W is transposed
+ * into ws first: ws_bytes >= tbik_gemm_dgrad_workspace_bytes(M, N, K),
+ * ws 16-byte aligned, device memory owned by the caller. */
+size_t tbik_gemm_dgrad_workspace_bytes(int M, int N, int K);
+int tbik_gemm_dgrad(const tbik_bf16 *dY, int64_t ld_dy, const tbik_bf16 *W, int64_t ldw, float *dX,
+                    int64_t ld_dx, tbik_bf16 *dX_bf16, int M, int N, int K, int leaf_mode,
+                    void *ws, size_t ws_bytes, void *stream);
+
+/* Weight gradient of Y = X W^T:  dW = dY^T X, i.e. dW[n,k] = TREE_m(dY[m,n] X[m,k])
+ * over the M/64 token leaves.  dY [M,N] (ld_dy), X [M,K] (ldx), dW [N,K] fp32
+ * (ld_dw).  M must be a positive multiple of 64; dp in {1,2,4,8} divides
+ * T(M/64) (else TBIK_ERR_TP).  ws (>= tbik_gemm_wgrad_workspace_bytes) holds
+ * dY^T [N,M] bf16, then X^T [K,M] bf16, each at a 256-byte boundary, then
+ * with dp > 1 the dp shard partials [dp][N][K] fp32 (kept after return). */
+size_t tbik_gemm_wgrad_workspace_bytes(int M, int N, int K, int dp);
+int tbik_gemm_wgrad(const tbik_bf16 *dY, int64_t ld_dy, const tbik_bf16 *X, int64_t ldx, float *dW,
+                    int64_t ld_dw, int M, int N, int K, int dp, int leaf_mode, void *ws,
+                    size_t ws_bytes, void *stream);
+
+/* RoPE backward: the adjoint of the rotation, the rotation by -angle:
+ *   dx[i] = bf16(dy[i]*c + dy[i+d/2]*s),  dx[i+d/2] = bf16(dy[i+d/2]*c - dy[i]*s),
+ * each product rounded to fp32 separately.  Layout and limits as tbik_rope;
+ * dx == dy (in place) is allowed. */
+int tbik_rope_backward(const tbik_bf16 *dy, tbik_bf16 *dx, const int32_t *pos,
+                       const float *cos_tab, const float *sin_tab, int T, int heads, int head_dim,
+                       int64_t ld_token, int max_pos, void *stream);
+
+/* SwiGLU backward for out = silu(g) * u:
+ *   den = 1 + EXP(-g);  sig = 1/den;  silu = g/den   (divisions correctly rounded)
+ *   dup   = bf16(dout * silu)
+ *   dgate = bf16((dout * u) * (sig * (1 + g * (1 - sig)))).
+ *  gate, up, dout, dgate, dup  [rows, cols] bf16 with their own row strides. */
+int tbik_swiglu_backward(const tbik_bf16 *gate, const tbik_bf16 *up, const tbik_bf16 *dout,
+                         tbik_bf16 *dgate, tbik_bf16 *dup, int rows, int cols, int64_t ld_gate,
+                         int64_t ld_up, int64_t ld_dout, int64_t ld_dgate, int64_t ld_dup,
+                         void *stream);
+
+/* Residual RMSNorm backward.  The forward (tbik_rmsnorm_residual) is
+ * recomputed: h = x + r, rstd from TREE_j(h_j*h_j) with the same bits.  Given
+ * dy = dL/dy and dr = dL/dr_out (NULL = zero), per row:
+ *   g_j = dy_j * w_j;  dot = TREE_j(g_j * h_j);  c = (dot * ((rstd*rstd)*rstd)) / H;
+ *   dh_j = bf16(((rstd * g_j) - (c * h_j)) + dr_j)          (= dL/dx = dL/dr);
+ * and, when dw is not NULL, the weight gradient over the rows (tokens):
+ *   leaf b of column j = sum over rows 64b..64b+63, in row order from +0, of
+ *   dy_ij * (h_ij * rstd_i);  dw_j = TREE over the leaves as dp shards.
+ * rows must then be a positive multiple of 64 and dp divide T(rows/64).
+ * ws (fp32, >= tbik_rmsnorm_backward_workspace_bytes) holds, in floats:
+ * rstd per row (rows rounded up to a multiple of 64), then with dw the
+ * (rows/64) x H leaves and the dp x H shard nodes (kept after return). */
+size_t tbik_rmsnorm_backward_workspace_bytes(int rows, int H, int dp, int want_dw);
+int tbik_rmsnorm_backward(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
+                          const tbik_bf16 *dy, const tbik_bf16 *dr, tbik_bf16 *dh, float *dw,
+                          int rows, int H, int64_t ld, float eps, int dp, float *ws,
+                          size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,9 @@ def lib():
             "or_rope_table": (None, [f64, i32, i32, p, p]),
             "or_rope": (None, [p, p, p, p, p, i32, i32, i32, i64, i32]),
             "or_swiglu": (None, [p, p, p, i32, i32, i64, i64, i64, i32]),
+            "or_rope_backward": (None, [p, p, p, p, p, i32, i32, i32, i64]),
+            "or_swiglu_backward": (None, [p, p, p, p, p, i32, i32, i64]),
+            "or_rmsnorm_backward": (i32, [p, p, p, p, p, p, p, i32, i32, i64, f32, i32, p]),
             "or_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p]),
             "or_softmax_causal": (None, [p, i64, p, i64, i32, i32, i32, f32]),
         }
@@ -246,3 +249,57 @@ def softmax_causal(S, offset, scale):
     P = np.empty((Lq, Lk), np.uint16)
     lib().or_softmax_causal(_ptr(S), Lk, _ptr(P), Lk, Lq, Lk, offset, np.float32(scale))
     return P
+
+
+# --- training side: backward passes -------------------------------------------
+
+def gemm_dgrad(dY, W, nthreads=0):
+    """dX = dY W: dY [M,N], W [N,K] (uint16) -> [M,K] fp32, TREE over the N
+    leaves (the GEMM with the weight transposed on the host)."""
+    return gemm(dY, np.ascontiguousarray(np.asarray(W, np.uint16).T), nthreads)
+
+
+def gemm_wgrad(dY, X, dp=1, nthreads=0):
+    """dW = dY^T X: dY [M,N], X [M,K] -> ([N,K] fp32, partials [dp,N,K]);
+    TREE over the M/64 token leaves, evaluated as dp data-parallel shards."""
+    dYt = np.ascontiguousarray(np.asarray(dY, np.uint16).T)
+    Xt = np.ascontiguousarray(np.asarray(X, np.uint16).T)
+    return gemm_tpsim(dYt, Xt, dp, nthreads)
+
+
+def rope_backward(dy, pos, cos_tab, sin_tab):
+    """dy [T, heads, head_dim] uint16 -> dx (the rotation by -angle)."""
+    dy = _c(dy, np.uint16)
+    T, heads, hd = dy.shape
+    pos = _c(np.asarray(pos, np.int32), np.int32)
+    cos_tab = _c(cos_tab, np.float32); sin_tab = _c(sin_tab, np.float32)
+    dx = np.empty_like(dy)
+    lib().or_rope_backward(_ptr(dy), _ptr(dx), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T, heads,
+                           hd, heads * hd)
+    return dx
+
+
+def swiglu_backward(g, u, dout):
+    """-> (dgate, dup) uint16."""
+    g = _c(g, np.uint16); u = _c(u, np.uint16); dout = _c(dout, np.uint16)
+    rows, cols = g.shape
+    dg = np.empty_like(g); du = np.empty_like(g)
+    lib().or_swiglu_backward(_ptr(g), _ptr(u), _ptr(dout), _ptr(dg), _ptr(du), rows, cols, cols)
+    return dg, du
+
+
+def rmsnorm_backward(x, r, w, dy, dr, eps, dp=1, want_dw=True):
+    """-> (dh uint16 [rows,H], dw fp32 [H] or None, dw_shards [dp,H] or None)."""
+    x = _c(x, np.uint16); r = _c(r, np.uint16); w = _c(w, np.uint16); dy = _c(dy, np.uint16)
+    dr = None if dr is None else _c(dr, np.uint16)
+    rows, H = x.shape
+    dh = np.empty_like(x)
+    dw = np.empty(H, np.float32) if want_dw else None
+    shards = np.empty((dp, H), np.float32) if want_dw else None
+    rc = lib().or_rmsnorm_backward(_ptr(x), _ptr(r), _ptr(w), _ptr(dy),
+                                   None if dr is None else _ptr(dr), _ptr(dh),
+                                   None if dw is None else _ptr(dw), rows, H, H,
+                                   np.float32(eps), dp, None if shards is None else _ptr(shards))
+    if rc:
+        raise ValueError("oracle rmsnorm_backward: error %d" % rc)
+    return dh, dw, shards

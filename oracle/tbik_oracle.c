@@ -35,7 +35,9 @@
  *  R4 EXP / LOG are defined by the operation sequences written below
  *     (Cody-Waite reduction plus Taylor polynomials), not by a libm;
  *  R5 two-pass log-softmax with the exact row maximum;
- *  R11 a misaligned rounding location is eager bf16 arithmetic (below).
+ *  R11 a misaligned rounding location is eager bf16 arithmetic (below);
+ *  R12 backward passes: derivatives of the forward definitions in fp32,
+ *      token sums by TREE over 64-token leaves (below).
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fno-fast-math (x86-64 SSE,
  * round-to-nearest, no FTZ/DAZ), so every float operation is one IEEE
@@ -525,6 +527,129 @@ OR_EXPORT void or_swiglu(const uint16_t *gate, const uint16_t *up, uint16_t *out
             if (each_op) silu = bf_round(silu);
             out[(int64_t)i * ld_out + j] = or_f32_to_bf16(silu * u);
         }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Training side: backward passes of the three nodes.  [TBIK] Abstract: the */
+/* trainer (FSDP, TP = 1) and the inference engine must agree bit for bit;  */
+/* [ROUND] "three nodes": the nodes keep fp32 intermediates and round once. */
+/* The pages give no backward formulas; R12 takes the derivatives of the    */
+/* forward definitions above, evaluated in fp32 in the order written here,  */
+/* each output rounded once to bf16, and sums over tokens with TREE over    */
+/* 64-token leaves (R1, R3) so that data-parallel shards are subtrees.      */
+/* ------------------------------------------------------------------------ */
+
+/* RoPE backward: the adjoint of the rotation is the rotation by -angle,
+ *   dx[i] = bf16(dy[i]*c + dy[i+d/2]*s),  dx[i+d/2] = bf16(dy[i+d/2]*c - dy[i]*s),
+ * each product rounded to fp32 separately. */
+OR_EXPORT void or_rope_backward(const uint16_t *dy, uint16_t *dx, const int32_t *pos,
+                                const float *cos_tab, const float *sin_tab, int T, int heads,
+                                int head_dim, int64_t ld_token) {
+    int half = head_dim / 2;
+    for (int t = 0; t < T; t++) {
+        int p = pos[t];
+        for (int hd = 0; hd < heads; hd++) {
+            const uint16_t *gv = dy + (int64_t)t * ld_token + (int64_t)hd * head_dim;
+            uint16_t *ov = dx + (int64_t)t * ld_token + (int64_t)hd * head_dim;
+            for (int i = 0; i < half; i++) {
+                float c = cos_tab[(int64_t)p * half + i];
+                float s = sin_tab[(int64_t)p * half + i];
+                float a = or_bf16_to_f32(gv[i]);
+                float b = or_bf16_to_f32(gv[i + half]);
+                float ac = a * c, bs = b * s, bc = b * c, as = a * s;
+                ov[i] = or_f32_to_bf16(ac + bs);
+                ov[i + half] = or_f32_to_bf16(bc - as);
+            }
+        }
+    }
+}
+
+/* SwiGLU backward for out = silu(g) * u, silu(g) = g * sigma(g):
+ *   den = 1 + EXP(-g);  sig = 1 / den;  silu = g / den;
+ *   du = bf16(dout * silu);
+ *   dsilu = sig * (1 + g * (1 - sig));   dg = bf16((dout * u) * dsilu). */
+OR_EXPORT void or_swiglu_backward(const uint16_t *gate, const uint16_t *up, const uint16_t *dout,
+                                  uint16_t *dgate, uint16_t *dup, int rows, int cols,
+                                  int64_t ld) {
+    for (int i = 0; i < rows; i++)
+        for (int j = 0; j < cols; j++) {
+            int64_t o = (int64_t)i * ld + j;
+            float g = or_bf16_to_f32(gate[o]);
+            float u = or_bf16_to_f32(up[o]);
+            float d = or_bf16_to_f32(dout[o]);
+            float den = 1.0f + or_expf(-g);
+            float sig = 1.0f / den;
+            float silu = g / den;
+            dup[o] = or_f32_to_bf16(d * silu);
+            float dsilu = sig * (1.0f + g * (1.0f - sig));
+            dgate[o] = or_f32_to_bf16((d * u) * dsilu);
+        }
+}
+
+/* Residual RMSNorm backward.  Forward (above): h = x + r, rstd from TREE of
+ * h*h, y = bf16((h*rstd)*w), r_out = bf16(h).  Given dy and the gradient
+ * dr of the residual output (may be NULL = zero), per row:
+ *   rstd as in the forward (same operations, same bits);
+ *   g_j = dy_j * w_j;  dot = TREE_j(g_j * h_j);  c = (dot * ((rstd*rstd)*rstd)) / H;
+ *   dh_j = bf16(((rstd * g_j) - (c * h_j)) + dr_j)      (dx = dr_in = dh);
+ * and over the rows (tokens), for the weight:
+ *   p_ij = dy_ij * (h_ij * rstd_i);  leaf b of column j = p_{64b,j} + ... +
+ *   p_{64b+63,j} added in row order from +0;  dw_j = TREE over the leaves,
+ *   evaluated as dp data-parallel shards (dp divides T) whose shard nodes
+ *   are written to dw_shards [dp][H] when it is not NULL.
+ * rows must be a multiple of 64 when dw is requested.  Returns 0 or -2/-3. */
+OR_EXPORT int or_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+                                  const uint16_t *dy, const uint16_t *dr, uint16_t *dh,
+                                  float *dw, int rows, int H, int64_t ld, float eps, int dp,
+                                  float *dw_shards) {
+    if (dw && (rows % LEAF)) return -2;
+    int64_t nleaf = rows / LEAF;
+    if (dw && nleaf > 0 && (dp < 1 || or_tree_T(nleaf) % dp)) return -3;
+    float *h = (float *)malloc(sizeof(float) * (size_t)H);
+    float *q = (float *)malloc(sizeof(float) * (size_t)H);
+    float *scratch = (float *)malloc(sizeof(float) * (size_t)(H > nleaf ? H : nleaf));
+    float *leaves = dw ? (float *)calloc((size_t)(nleaf > 0 ? nleaf : 1) * (size_t)H,
+                                         sizeof(float)) : NULL;
+    for (int i = 0; i < rows; i++) {
+        const int64_t o = (int64_t)i * ld;
+        for (int j = 0; j < H; j++) {
+            h[j] = or_bf16_to_f32(x[o + j]) + or_bf16_to_f32(r[o + j]);
+            q[j] = h[j] * h[j];
+        }
+        float ss = or_tree(q, H, scratch);
+        float mean = ss / (float)H;
+        float rstd = 1.0f / sqrtf(mean + eps);
+        for (int j = 0; j < H; j++) {
+            float g = or_bf16_to_f32(dy[o + j]) * or_bf16_to_f32(w[j]);
+            q[j] = g * h[j];
+        }
+        float dot = or_tree(q, H, scratch);
+        float c = (dot * ((rstd * rstd) * rstd)) / (float)H;
+        for (int j = 0; j < H; j++) {
+            float g = or_bf16_to_f32(dy[o + j]) * or_bf16_to_f32(w[j]);
+            float v = (rstd * g) - (c * h[j]);
+            if (dr) v = v + or_bf16_to_f32(dr[o + j]);
+            dh[o + j] = or_f32_to_bf16(v);
+            if (leaves) {
+                float pr = or_bf16_to_f32(dy[o + j]) * (h[j] * rstd);
+                float *lf = leaves + (int64_t)(i / LEAF) * H + j;
+                *lf = *lf + pr;
+            }
+        }
+    }
+    if (dw) {
+        float *col = (float *)malloc(sizeof(float) * (size_t)(nleaf > 0 ? nleaf : 1));
+        for (int j = 0; j < H; j++) {
+            for (int64_t b = 0; b < nleaf; b++) col[b] = leaves[b * H + j];
+            float nodes[8];
+            dw[j] = or_tree_sharded(col, nleaf, dp, scratch, nodes);
+            if (dw_shards)
+                for (int t = 0; t < dp; t++) dw_shards[(int64_t)t * H + j] = nleaf ? nodes[t] : 0.0f;
+        }
+        free(col);
+    }
+    free(h); free(q); free(scratch); free(leaves);
+    return 0;
 }
 
 /* ------------------------------------------------------------------------ */

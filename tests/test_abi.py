@@ -183,6 +183,40 @@ def test_rowop_validation(L):
     assert L.tbik_primitive(0, None, FAKE2, 4, None) == E_NULL
 
 
+def test_training_validation(L):
+    # transpose
+    assert L.tbik_transpose_bf16(None, 8, FAKE2, 8, 4, 8, None) == E_NULL
+    assert L.tbik_transpose_bf16(FAKE, 4, FAKE2, 8, 4, 8, None) == E_SHAPE
+    assert L.tbik_transpose_bf16(FAKE, 8, FAKE2, 8, 0, 8, None) == OK
+    # input gradient: the reduced dimension N must be a multiple of 64
+    dg = L.tbik_gemm_dgrad
+    assert dg(FAKE, 96, FAKE2, 64, FAKE3, 64, None, 4, 96, 64, 0, FAKE, 1 << 20, None) == E_SHAPE
+    assert dg(FAKE, 128, FAKE2, 64, FAKE3, 64, None, 4, 128, 64, 0, None, 0, None) == E_WS
+    assert dg(FAKE, 128, FAKE2, 64, FAKE3, 64, None, 4, 128, 64, 0, FAKE, 64, None) == E_WS
+    assert dg(FAKE, 128, FAKE2, 64, FAKE3, 64, None, 0, 128, 64, 0, None, 0, None) == OK
+    # weight gradient: tokens a multiple of 64, dp dividing T(M/64)
+    wg = L.tbik_gemm_wgrad
+    assert wg(FAKE, 64, FAKE2, 64, FAKE3, 64, 100, 64, 64, 1, 0, FAKE, 1 << 20, None) == E_SHAPE
+    assert wg(FAKE, 64, FAKE2, 64, FAKE3, 64, 256, 64, 64, 3, 0, FAKE, 1 << 20, None) == E_TP
+    assert wg(FAKE, 64, FAKE2, 64, FAKE3, 64, 64 * 12, 64, 64, 8, 0, FAKE, 1 << 24, None) == E_TP
+    assert wg(FAKE, 64, FAKE2, 64, FAKE3, 64, 256, 64, 64, 2, 0, FAKE, 1024, None) == E_WS
+    assert L.tbik_gemm_wgrad_workspace_bytes(256, 64, 32, 2) == 32768 + 16384 + 2 * 64 * 32 * 4
+    # backward passes
+    assert L.tbik_rope_backward(FAKE, FAKE, None, FAKE, FAKE, 1, 1, 128, 128, 16, None) == E_NULL
+    sb = L.tbik_swiglu_backward
+    assert sb(FAKE, FAKE, FAKE, FAKE2, None, 1, 8, 8, 8, 8, 8, 8, None) == E_NULL
+    assert sb(FAKE, FAKE, FAKE, FAKE2, FAKE3, 1, 16, 16, 16, 8, 16, 16, None) == E_SHAPE
+    rb = L.tbik_rmsnorm_backward
+    assert rb(FAKE, FAKE, FAKE, FAKE, None, FAKE2, FAKE3, 100, 64, 64, 1e-6, 1, FAKE, 1 << 20,
+              None) == E_SHAPE
+    assert rb(FAKE, FAKE, FAKE, FAKE, None, FAKE2, FAKE3, 128, 64, 64, 1e-6, 4, FAKE, 1 << 20,
+              None) == E_TP
+    assert rb(FAKE, FAKE, FAKE, FAKE, None, FAKE2, None, 7, 64, 64, 1e-6, 1, None, 0,
+              None) == E_WS
+    assert rb(FAKE, FAKE, FAKE, FAKE, None, FAKE2, None, 0, 64, 64, 1e-6, 1, None, 0,
+              None) == OK
+
+
 def test_empty_shapes_are_no_ops(L):
     # M = 0 / rows = 0 return OK before touching any pointer or launching
     assert L.tbik_gemm(FAKE, 64, FAKE2, 64, FAKE3, 64, None, 0, 4, 64, 0, None, 0, None) == OK

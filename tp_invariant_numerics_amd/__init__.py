@@ -21,6 +21,8 @@ __all__ = [
     "tbik_tree_combine", "tbik_gemm_tp_partials", "tbik_gemm_shard", "tbik_rmsnorm_residual", "tbik_rope", "tbik_rope_table",
     "tbik_swiglu", "tbik_logsoftmax_gather", "tbik_logsoftmax_workspace_bytes",
     "tbik_softmax_causal", "tbik_primitive", "LEAF_MFMA", "LEAF_SCALAR", "ROUNDING",
+    "tbik_transpose_bf16", "tbik_gemm_dgrad", "tbik_gemm_wgrad", "tbik_rope_backward",
+    "tbik_swiglu_backward", "tbik_rmsnorm_backward",
 ]
 
 LEAF_MFMA = 0
@@ -81,6 +83,15 @@ def _sigs():
         "tbik_gather_rows": (i32, [p, i64, i32, p, i32, i32, p, i64, p]),
         "tbik_attention_causal": (i32, [p, i64, p, i64, p, i64, p, i64, i32, i32, i32, i32, f32,
                                         p]),
+        "tbik_transpose_bf16": (i32, [p, i64, p, i64, i32, i32, p]),
+        "tbik_gemm_dgrad_workspace_bytes": (sz, [i32, i32, i32]),
+        "tbik_gemm_dgrad": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, p, sz, p]),
+        "tbik_gemm_wgrad_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "tbik_gemm_wgrad": (i32, [p, i64, p, i64, p, i64, i32, i32, i32, i32, i32, p, sz, p]),
+        "tbik_rope_backward": (i32, [p, p, p, p, p, i32, i32, i32, i64, i32, p]),
+        "tbik_swiglu_backward": (i32, [p, p, p, p, p, i32, i32, i64, i64, i64, i64, i64, p]),
+        "tbik_rmsnorm_backward_workspace_bytes": (sz, [i32, i32, i32, i32]),
+        "tbik_rmsnorm_backward": (i32, [p, p, p, p, p, p, p, i32, i32, i64, f32, i32, p, sz, p]),
     }
 
 
@@ -391,3 +402,106 @@ def tbik_primitive(op, x, y=None):
     rc = lib().tbik_primitive(op, _ptr(x), _ptr(y), x.numel(), _stream())
     _chk(rc, "tbik_primitive")
     return y
+
+
+# --- training side -------------------------------------------------------------
+
+def tbik_transpose_bf16(x, out=None):
+    _bits(x); _need_gpu(x)
+    rows, cols = x.shape
+    if out is None:
+        out = torch.empty((cols, rows), dtype=torch.bfloat16, device=x.device)
+    rc = lib().tbik_transpose_bf16(_ptr(x), _ld(x), _ptr(out), _ld(out), rows, cols, _stream())
+    _chk(rc, "tbik_transpose_bf16")
+    return out
+
+
+def _bytes_ws(nbytes, dev):
+    return torch.empty((max(1, (nbytes + 15) // 16) * 4,), dtype=torch.float32, device=dev)
+
+
+def tbik_gemm_dgrad(dY, W, leaf_mode=LEAF_MFMA, want_fp32=True, want_bf16=False, ws=None):
+    """dX = dY W (tree over N): dY [M,N], W [N,K] -> (dX fp32 or None, dX bf16 or None)."""
+    _bits(dY); _bits(W); _need_gpu(dY, W)
+    M, N = dY.shape
+    K = W.shape[1]
+    dX = torch.empty((M, K), dtype=torch.float32, device=dY.device) if want_fp32 else None
+    dXb = torch.empty((M, K), dtype=torch.bfloat16, device=dY.device) if want_bf16 else None
+    need = lib().tbik_gemm_dgrad_workspace_bytes(M, N, K)
+    if ws is None:
+        ws = _bytes_ws(need, dY.device)
+    rc = lib().tbik_gemm_dgrad(_ptr(dY), _ld(dY), _ptr(W), _ld(W), _ptr(dX), K, _ptr(dXb), M, N,
+                               K, leaf_mode, _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _chk(rc, "tbik_gemm_dgrad")
+    return dX, dXb
+
+
+def tbik_gemm_wgrad(dY, X, dp=1, leaf_mode=LEAF_MFMA, ws=None, out=None):
+    """dW = dY^T X (tree over the M/64 token leaves, dp simulated data-parallel
+    shards): dY [M,N], X [M,K] -> (dW [N,K] fp32, shard partials [dp,N,K] or None)."""
+    _bits(dY); _bits(X); _need_gpu(dY, X)
+    M, N = dY.shape
+    K = X.shape[1]
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.float32, device=dY.device)
+    need = lib().tbik_gemm_wgrad_workspace_bytes(M, N, K, dp)
+    if ws is None:
+        ws = _bytes_ws(need, dY.device)
+    rc = lib().tbik_gemm_wgrad(_ptr(dY), _ld(dY), _ptr(X), _ld(X), _ptr(out), _ld(out), M, N, K, dp,
+                               leaf_mode, _ptr(ws), ws.numel() * ws.element_size(), _stream())
+    _chk(rc, "tbik_gemm_wgrad")
+    parts = None
+    if dp > 1:
+        r256 = lambda b: (b + 255) // 256 * 256
+        off = (r256(N * M * 2) + r256(K * M * 2)) // 4
+        parts = ws.view(torch.float32)[off:off + dp * N * K].view(dp, N, K)
+    return out, parts
+
+
+def tbik_rope_backward(dy, pos, cos_tab, sin_tab, dx=None):
+    _bits(dy); _need_gpu(dy, pos, cos_tab, sin_tab)
+    T, heads, d = dy.shape
+    if dy.stride(2) != 1 or dy.stride(1) != d:
+        raise ValueError("heads must be contiguous with stride head_dim")
+    if dx is None:
+        dx = torch.empty_like(dy)
+    rc = lib().tbik_rope_backward(_ptr(dy), _ptr(dx), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T,
+                                  heads, d, dy.stride(0), cos_tab.shape[0], _stream())
+    _chk(rc, "tbik_rope_backward")
+    return dx
+
+
+def tbik_swiglu_backward(gate, up, dout):
+    """-> (dgate, dup) bf16."""
+    _bits(gate); _bits(up); _bits(dout); _need_gpu(gate, up, dout)
+    rows, cols = gate.shape
+    dg = torch.empty((rows, cols), dtype=torch.bfloat16, device=gate.device)
+    du = torch.empty_like(dg)
+    rc = lib().tbik_swiglu_backward(_ptr(gate), _ptr(up), _ptr(dout), _ptr(dg), _ptr(du), rows,
+                                    cols, _ld(gate), _ld(up), _ld(dout), _ld(dg), _ld(du),
+                                    _stream())
+    _chk(rc, "tbik_swiglu_backward")
+    return dg, du
+
+
+def tbik_rmsnorm_backward(x, r, w, dy, dr=None, eps=1e-6, dp=1, want_dw=True):
+    """-> (dh bf16 [rows,H], dw fp32 [H] or None, shard nodes [dp,H] or None)."""
+    _bits(x); _bits(r); _bits(w); _bits(dy); _need_gpu(x, r, w, dy)
+    rows, H = x.shape
+    ld = _ld(x)
+    for t in (r, dy) + ((dr,) if dr is not None else ()):
+        if _ld(t) != ld:
+            raise ValueError("x, r, dy and dr must share the row stride")
+    dh = torch.empty_like(x)
+    dw = torch.empty((H,), dtype=torch.float32, device=x.device) if want_dw else None
+    need = lib().tbik_rmsnorm_backward_workspace_bytes(rows, H, dp, int(want_dw))
+    ws = torch.empty((max(1, need // 4),), dtype=torch.float32, device=x.device)
+    rc = lib().tbik_rmsnorm_backward(_ptr(x), _ptr(r), _ptr(w), _ptr(dy), _ptr(dr), _ptr(dh),
+                                     _ptr(dw), rows, H, ld, float(eps), dp, _ptr(ws), need,
+                                     _stream())
+    _chk(rc, "tbik_rmsnorm_backward")
+    shards = None
+    if want_dw:
+        off = (rows + 63) // 64 * 64 + (rows // 64) * H
+        shards = ws[off:off + dp * H].view(dp, H)
+    return dh, dw, shards

@@ -328,7 +328,9 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
 // =============================================================================
 // EACH: table entries and every product rounded to bf16 before the
 // difference and the sum (rotate_half arithmetic on bf16 tensors).
-template <bool EACH>
+// INV: the rotation by -angle, the adjoint used by the backward pass:
+// y[i] = x[i]*c + x[i+h]*s, y[i+h] = x[i+h]*c - x[i]*s.
+template <bool EACH, bool INV = false>
 __global__ void __launch_bounds__(256)
 k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
        const float *sin_tab, int T, int heads, int half, int64_t ld_token, int max_pos,
@@ -368,8 +370,8 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
         bc = bf_round(bc);
         as = bf_round(as);
       }
-      ya[e] = ac - bs;
-      yb[e] = bc + as;
+      ya[e] = INV ? ac + bs : ac - bs;
+      yb[e] = INV ? bc - as : bc + as;
     }
     u32x2 oa, ob;
     oa[0] = pack_bf16(ya[0], ya[1]);
@@ -393,7 +395,10 @@ int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float 
     if ((1 << b) == q4) q4_shift = b;
   const unsigned gx = (unsigned)((items + 255) / 256);
   const unsigned gy = (unsigned)(T < 65535 ? T : 65535);
-  if (rounding == TBIK_ROUND_EACH_OP)
+  if (rounding == kRopeInverse)
+    hipLaunchKernelGGL((k_rope<false, true>), dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab,
+                       sin_tab, T, heads, half, ld_token, max_pos, q4_shift);
+  else if (rounding == TBIK_ROUND_EACH_OP)
     hipLaunchKernelGGL((k_rope<true>), dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab, sin_tab, T,
                        heads, half, ld_token, max_pos, q4_shift);
   else
@@ -832,6 +837,226 @@ int launch_primitive(int op, const float *x, float *y, int64_t n, hipStream_t s)
   if (blocks > 262144) blocks = 262144;
   if (blocks < 1) blocks = 1;
   hipLaunchKernelGGL(k_primitive, dim3((unsigned)blocks), dim3(256), 0, s, op, x, y, n);
+  return check_launch();
+}
+
+// =============================================================================
+// Backward passes (training side).  fp32 intermediates in the order the
+// header gives, each output rounded once to bf16; sums over tokens are trees
+// over 64-token leaves whose T groups are the data-parallel shards.
+// =============================================================================
+int launch_rope_backward(const uint16_t *dy, uint16_t *dx, const int32_t *pos,
+                         const float *cos_tab, const float *sin_tab, int T, int heads,
+                         int head_dim, int64_t ld_token, int max_pos, hipStream_t s) {
+  return launch_rope(dy, dx, pos, cos_tab, sin_tab, T, heads, head_dim, ld_token, max_pos,
+                     kRopeInverse, s);
+}
+
+// SwiGLU backward: du = bf16(d * silu(g)),
+// dg = bf16((d * u) * (sig * (1 + g * (1 - sig)))) with sig = 1 / (1 + EXP(-g))
+// and silu = g / (1 + EXP(-g)), both divisions correctly rounded.
+__device__ __forceinline__ void swiglu_bwd_1(float g, float u, float d, float &dg, float &du) {
+  const float den = silu_den(g);
+  const float sig = 1.0f / den;
+  const float sl = g / den;
+  du = d * sl;
+  dg = (d * u) * (sig * (1.0f + g * (1.0f - sig)));
+}
+
+template <bool VEC>
+__global__ void __launch_bounds__(256)
+k_swiglu_bwd(const uint16_t *g, const uint16_t *u, const uint16_t *d, uint16_t *dg, uint16_t *du,
+             int rows, int cols, int64_t ldg, int64_t ldu, int64_t ldd, int64_t lddg,
+             int64_t lddu) {
+  const int per = VEC ? 8 : 1;
+  const int col = (blockIdx.x * blockDim.x + threadIdx.x) * per;
+  if (col >= cols) return;
+  for (int row = blockIdx.y; row < rows; row += gridDim.y) {
+    if constexpr (VEC) {
+      float gv[8], uv[8], dv[8], og[8], ou[8];
+      load_bf16<8, true>(gv, g + (int64_t)row * ldg + col);
+      load_bf16<8, true>(uv, u + (int64_t)row * ldu + col);
+      load_bf16<8, true>(dv, d + (int64_t)row * ldd + col);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) swiglu_bwd_1(gv[e], uv[e], dv[e], og[e], ou[e]);
+      store_bf16<8, true>(dg + (int64_t)row * lddg + col, og);
+      store_bf16<8, true>(du + (int64_t)row * lddu + col, ou);
+    } else {
+      float og, ou;
+      swiglu_bwd_1(bf2f(g[(int64_t)row * ldg + col]), bf2f(u[(int64_t)row * ldu + col]),
+                   bf2f(d[(int64_t)row * ldd + col]), og, ou);
+      dg[(int64_t)row * lddg + col] = f2bf(og);
+      du[(int64_t)row * lddu + col] = f2bf(ou);
+    }
+  }
+}
+
+int launch_swiglu_backward(const uint16_t *g, const uint16_t *u, const uint16_t *d, uint16_t *dg,
+                           uint16_t *du, int rows, int cols, int64_t ldg, int64_t ldu,
+                           int64_t ldd, int64_t lddg, int64_t lddu, hipStream_t s) {
+  if (rows == 0 || cols == 0) return TBIK_OK;
+  const bool vec = (cols % 8) == 0 && elem_align(g, ldg, 2) >= 8 && elem_align(u, ldu, 2) >= 8 &&
+                   elem_align(d, ldd, 2) >= 8 && elem_align(dg, lddg, 2) >= 8 &&
+                   elem_align(du, lddu, 2) >= 8;
+  const int items = vec ? cols / 8 : cols;
+  const dim3 grid((unsigned)((items + 255) / 256), (unsigned)(rows < 65535 ? rows : 65535));
+  if (vec)
+    hipLaunchKernelGGL(k_swiglu_bwd<true>, grid, dim3(256), 0, s, g, u, d, dg, du, rows, cols,
+                       ldg, ldu, ldd, lddg, lddu);
+  else
+    hipLaunchKernelGGL(k_swiglu_bwd<false>, grid, dim3(256), 0, s, g, u, d, dg, du, rows, cols,
+                       ldg, ldu, ldd, lddg, lddu);
+  return check_launch();
+}
+
+// Residual RMSNorm backward, one workgroup per row: rstd from the forward's
+// tree (same chunks, same LDS tree, same bits), dot = TREE(g*h) with
+// g = dy*w, c = (dot * ((rstd*rstd)*rstd)) / H, dh = bf16(((rstd*g) - (c*h)) + dr).
+// rstd of the row goes to rstd_out for the weight gradient.
+template <int CH>
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uint16_t *dy,
+              const uint16_t *dr, uint16_t *dh, float *rstd_out, int H, int64_t ld, float eps,
+              int T) {
+  extern __shared__ float lds[];
+  const int nch = H / CH;
+  const int gc = nch / T;
+  const int64_t base = (int64_t)blockIdx.x * ld;
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float a[CH], b[CH];
+    load_bf16<CH>(a, x + base + ch * CH);
+    load_bf16<CH>(b, r + base + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      a[e] = a[e] + b[e];
+      a[e] = a[e] * a[e];
+    }
+    lds[ch] = chunk_tree<CH>(a);
+  }
+  __syncthreads();
+  const float ss = lds_row_tree<kRowThreads>(lds, lds + nch, gc, T);
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)H + eps);
+  __syncthreads();                       // every thread has read the root
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float a[CH], b[CH], gy[CH], ww[CH];
+    load_bf16<CH>(a, x + base + ch * CH);
+    load_bf16<CH>(b, r + base + ch * CH);
+    load_bf16<CH>(gy, dy + base + ch * CH);
+    load_bf16<CH>(ww, w + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) a[e] = (gy[e] * ww[e]) * (a[e] + b[e]);
+    lds[ch] = chunk_tree<CH>(a);
+  }
+  __syncthreads();
+  const float dot = lds_row_tree<kRowThreads>(lds, lds + nch, gc, T);
+  const float c = (dot * ((rstd * rstd) * rstd)) / (float)H;
+  for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
+    float a[CH], b[CH], gy[CH], ww[CH], gr[CH];
+    load_bf16<CH>(a, x + base + ch * CH);
+    load_bf16<CH>(b, r + base + ch * CH);
+    load_bf16<CH>(gy, dy + base + ch * CH);
+    load_bf16<CH>(ww, w + ch * CH);
+    if (dr) load_bf16<CH>(gr, dr + base + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const float h = a[e] + b[e];
+      float v = (rstd * (gy[e] * ww[e])) - (c * h);
+      if (dr) v = v + gr[e];
+      a[e] = v;
+    }
+    store_bf16<CH>(dh + base + ch * CH, a);
+  }
+  if (threadIdx.x == 0) rstd_out[blockIdx.x] = rstd;
+}
+
+// Leaves of the weight gradient: leaf b of column j adds
+// dy_ij * ((x_ij + r_ij) * rstd_i) over the 64 rows of leaf b in row order
+// from +0.  grid.x covers the columns (one per thread), grid.y the leaves.
+__global__ void __launch_bounds__(256)
+k_rmsnorm_dw_leaves(const uint16_t *x, const uint16_t *r, const uint16_t *dy, const float *rstd,
+                    float *leaves, int H, int64_t ld) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= H) return;
+  const int r0 = blockIdx.y * 64;
+  float acc = 0.0f;
+  for (int i = 0; i < 64; ++i) {
+    const int64_t o = (int64_t)(r0 + i) * ld + col;
+    const float n = (bf2f(x[o]) + bf2f(r[o])) * rstd[r0 + i];
+    acc = acc + bf2f(dy[o]) * n;
+  }
+  leaves[(int64_t)blockIdx.y * H + col] = acc;
+}
+
+// Tree over the nleaf leaves of each column: PAIR inside each of the T
+// groups, then the shards (perfect trees over T/dp groups; shard nodes to
+// shards[dp][H] when not null) and the perfect tree over the dp shards.
+// T/dp and dp are powers of two, so this is the perfect top over the T
+// groups for every dp.
+__global__ void __launch_bounds__(256)
+k_colsum_tree(const float *leaves, int nleaf, int H, int T, int dp, float *shards, float *out) {
+  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  if (col >= H) return;
+  const int G = nleaf / T;
+  float gv[8];
+  for (int q = 0; q < T; ++q) {
+    float st[20][1];
+    float node[1] = {0.0f};
+    for (int i = 0; i < G; ++i) {
+      node[0] = leaves[(int64_t)(q * G + i) * H + col];
+      pair_push<1, 20>(st, node, i, G);
+    }
+    gv[q] = node[0];
+  }
+  const int per = T / dp;
+  float sv[8];
+  for (int t = 0; t < dp; ++t) {
+    float v[8];
+    for (int q = 0; q < per; ++q) v[q] = gv[t * per + q];
+    for (int wdt = per; wdt > 1; wdt >>= 1)
+      for (int q = 0; q < wdt / 2; ++q) v[q] = v[2 * q] + v[2 * q + 1];
+    sv[t] = v[0];
+    if (shards) shards[(int64_t)t * H + col] = v[0];
+  }
+  for (int wdt = dp; wdt > 1; wdt >>= 1)
+    for (int q = 0; q < wdt / 2; ++q) sv[q] = sv[2 * q] + sv[2 * q + 1];
+  out[col] = sv[0];
+}
+
+int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+                            const uint16_t *dy, const uint16_t *dr, uint16_t *dh, float *dw,
+                            int rows, int H, int64_t ld, float eps, int dp, float *ws,
+                            hipStream_t s) {
+  const int T = tree_T(H);
+  int al = elem_align(x, ld, 2);
+  al = al < elem_align(r, ld, 2) ? al : elem_align(r, ld, 2);
+  al = al < elem_align(dy, ld, 2) ? al : elem_align(dy, ld, 2);
+  al = al < elem_align(dh, ld, 2) ? al : elem_align(dh, ld, 2);
+  al = al < elem_align(w, 16, 2) ? al : elem_align(w, 16, 2);
+  if (dr) al = al < elem_align(dr, ld, 2) ? al : elem_align(dr, ld, 2);
+  const int ch = cap_bf16(chunk_for(H / T), al);
+  const int nch = H / ch;
+  if (nch > 8192) return TBIK_ERR_SHAPE;
+  const size_t lds = 2 * (size_t)nch * sizeof(float);
+  float *rstd = ws;                                 // [rows]
+  const dim3 grid((unsigned)rows), block(kRowThreads);
+  switch (ch) {
+    case 16: hipLaunchKernelGGL(k_rmsnorm_bwd<16>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
+    case 8: hipLaunchKernelGGL(k_rmsnorm_bwd<8>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
+    case 4: hipLaunchKernelGGL(k_rmsnorm_bwd<4>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
+    case 2: hipLaunchKernelGGL(k_rmsnorm_bwd<2>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
+    default: hipLaunchKernelGGL(k_rmsnorm_bwd<1>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
+  }
+  int rc = check_launch();
+  if (rc != TBIK_OK || !dw) return rc;
+  const int nleaf = rows / 64;
+  float *leaves = ws + rmsnorm_bwd_rstd_floats(rows);
+  float *shards = leaves + (int64_t)nleaf * H;
+  hipLaunchKernelGGL(k_rmsnorm_dw_leaves, dim3((unsigned)((H + 255) / 256), (unsigned)nleaf),
+                     dim3(256), 0, s, x, r, dy, rstd, leaves, H, ld);
+  rc = check_launch();
+  if (rc != TBIK_OK) return rc;
+  hipLaunchKernelGGL(k_colsum_tree, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s, leaves,
+                     nleaf, H, tree_T(nleaf), dp, shards, dw);
   return check_launch();
 }
 

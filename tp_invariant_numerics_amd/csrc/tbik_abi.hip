@@ -268,6 +268,145 @@ int tbik_swiglu_ex(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, i
                              as_stream(stream));
 }
 
+// ---------------------------------------------------------------- training side
+
+int tbik_transpose_bf16(const tbik_bf16 *x, int64_t ldx, tbik_bf16 *y, int64_t ldy, int rows,
+                        int cols, void *stream) {
+  if (!x || !y) return TBIK_ERR_NULL;
+  if (rows < 0 || cols < 0 || rows > 4194240 || ldx < cols || ldy < rows) return TBIK_ERR_SHAPE;
+  if (!aligned(x, 2) || !aligned(y, 2)) return TBIK_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return TBIK_OK;
+  return tbik::launch_transpose_bf16(x, ldx, y, ldy, rows, cols, as_stream(stream));
+}
+
+static size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+size_t tbik_gemm_dgrad_workspace_bytes(int M, int N, int K) {
+  if (M < 0 || N <= 0 || K <= 0) return 0;
+  return round256((size_t)K * (size_t)N * 2);
+}
+
+int tbik_gemm_dgrad(const tbik_bf16 *dY, int64_t ld_dy, const tbik_bf16 *W, int64_t ldw, float *dX,
+                    int64_t ld_dx, tbik_bf16 *dX_bf16, int M, int N, int K, int leaf_mode,
+                    void *ws, size_t ws_bytes, void *stream) {
+  if (!dY || !W || (!dX && !dX_bf16)) return TBIK_ERR_NULL;
+  if (M < 0 || K < 0 || N <= 0 || (N % 64) != 0 || ldw < K) return TBIK_ERR_SHAPE;
+  if (!aligned(W, 2)) return TBIK_ERR_ALIGN;
+  if (M == 0 || K == 0) return TBIK_OK;
+  if (!ws) return TBIK_ERR_WORKSPACE;
+  if (!aligned16(ws)) return TBIK_ERR_ALIGN;
+  if (ws_bytes < tbik_gemm_dgrad_workspace_bytes(M, N, K)) return TBIK_ERR_WORKSPACE;
+  tbik_bf16 *Wt = static_cast<tbik_bf16 *>(ws);                  // [K, N]
+  // the GEMM's own checks on the transposed layout, before anything runs
+  int rc = check_gemm(dY, ld_dy, Wt, N, dX, ld_dx, dX_bf16, M, K, N, leaf_mode);
+  if (rc) return rc;
+  rc = tbik::launch_transpose_bf16(W, ldw, Wt, N, N, K, as_stream(stream));
+  if (rc) return rc;
+  return tbik_gemm_strided_batched(dY, ld_dy, 0, Wt, N, 0, dX, ld_dx, 0, dX_bf16, M, K, N, 1,
+                                   leaf_mode, stream);
+}
+
+size_t tbik_gemm_wgrad_workspace_bytes(int M, int N, int K, int dp) {
+  if (M <= 0 || N < 0 || K < 0 || dp < 1) return 0;
+  size_t b = round256((size_t)N * (size_t)M * 2) + round256((size_t)K * (size_t)M * 2);
+  if (dp > 1) b += (size_t)dp * (size_t)N * (size_t)K * sizeof(float);
+  return b;
+}
+
+int tbik_gemm_wgrad(const tbik_bf16 *dY, int64_t ld_dy, const tbik_bf16 *X, int64_t ldx, float *dW,
+                    int64_t ld_dw, int M, int N, int K, int dp, int leaf_mode, void *ws,
+                    size_t ws_bytes, void *stream) {
+  if (!dY || !X || !dW) return TBIK_ERR_NULL;
+  if (M <= 0 || (M % 64) != 0 || N < 0 || K < 0 || ld_dy < N || ldx < K || ld_dw < K)
+    return TBIK_ERR_SHAPE;
+  if (M > 4194240) return TBIK_ERR_SHAPE;
+  if (!tp_ok(dp) || (tbik::tree_T(M / 64) % dp) != 0) return TBIK_ERR_TP;
+  if (!aligned(dY, 2) || !aligned(X, 2) || !aligned(dW, 4)) return TBIK_ERR_ALIGN;
+  if (leaf_mode != TBIK_LEAF_MFMA && leaf_mode != TBIK_LEAF_SCALAR) return TBIK_ERR_ARG;
+  const int nb = M / 64;
+  if (nb / tbik::tree_T(nb) > tbik::kMaxGroupLeaves) return TBIK_ERR_SHAPE;
+  if (N == 0 || K == 0) return TBIK_OK;
+  if (!ws) return TBIK_ERR_WORKSPACE;
+  if (!aligned16(ws)) return TBIK_ERR_ALIGN;
+  if (ws_bytes < tbik_gemm_wgrad_workspace_bytes(M, N, K, dp)) return TBIK_ERR_WORKSPACE;
+  char *base = static_cast<char *>(ws);
+  tbik_bf16 *dYt = reinterpret_cast<tbik_bf16 *>(base);                       // [N, M]
+  tbik_bf16 *Xt = reinterpret_cast<tbik_bf16 *>(base + round256((size_t)N * M * 2));  // [K, M]
+  float *parts = reinterpret_cast<float *>(base + round256((size_t)N * M * 2) +
+                                           round256((size_t)K * M * 2));
+  hipStream_t s = as_stream(stream);
+  int rc = tbik::launch_transpose_bf16(dY, ld_dy, dYt, M, M, N, s);
+  if (rc) return rc;
+  rc = tbik::launch_transpose_bf16(X, ldx, Xt, M, M, K, s);
+  if (rc) return rc;
+  if (dp == 1)
+    return tbik_gemm_strided_batched(dYt, M, 0, Xt, M, 0, dW, ld_dw, 0, nullptr, N, K, M, 1,
+                                     leaf_mode, stream);
+  return tbik_gemm_tpsim(dYt, M, Xt, M, dW, ld_dw, nullptr, N, K, M, dp, leaf_mode, parts,
+                         (size_t)dp * N * K * sizeof(float), stream);
+}
+
+int tbik_rope_backward(const tbik_bf16 *dy, tbik_bf16 *dx, const int32_t *pos,
+                       const float *cos_tab, const float *sin_tab, int T, int heads, int head_dim,
+                       int64_t ld_token, int max_pos, void *stream) {
+  if (!dy || !dx || !pos || !cos_tab || !sin_tab) return TBIK_ERR_NULL;
+  if (T < 0 || heads < 1 || max_pos < 1) return TBIK_ERR_SHAPE;
+  if (head_dim < 2 || head_dim > 1024 || (head_dim % 8) != 0) return TBIK_ERR_SHAPE;
+  if (ld_token < (int64_t)heads * head_dim) return TBIK_ERR_SHAPE;
+  if (!ld_ok(ld_token)) return TBIK_ERR_ALIGN;
+  if (!aligned16(dy) || !aligned16(dx) || !aligned16(cos_tab) || !aligned16(sin_tab) ||
+      ((uintptr_t)pos & 3u))
+    return TBIK_ERR_ALIGN;
+  if (T == 0) return TBIK_OK;
+  return tbik::launch_rope_backward(dy, dx, pos, cos_tab, sin_tab, T, heads, head_dim, ld_token,
+                                    max_pos, as_stream(stream));
+}
+
+int tbik_swiglu_backward(const tbik_bf16 *gate, const tbik_bf16 *up, const tbik_bf16 *dout,
+                         tbik_bf16 *dgate, tbik_bf16 *dup, int rows, int cols, int64_t ld_gate,
+                         int64_t ld_up, int64_t ld_dout, int64_t ld_dgate, int64_t ld_dup,
+                         void *stream) {
+  if (!gate || !up || !dout || !dgate || !dup) return TBIK_ERR_NULL;
+  if (rows < 0 || cols < 0 || ld_gate < cols || ld_up < cols || ld_dout < cols ||
+      ld_dgate < cols || ld_dup < cols)
+    return TBIK_ERR_SHAPE;
+  if (!aligned(gate, 2) || !aligned(up, 2) || !aligned(dout, 2) || !aligned(dgate, 2) ||
+      !aligned(dup, 2))
+    return TBIK_ERR_ALIGN;
+  if (rows == 0 || cols == 0) return TBIK_OK;
+  return tbik::launch_swiglu_backward(gate, up, dout, dgate, dup, rows, cols, ld_gate, ld_up,
+                                      ld_dout, ld_dgate, ld_dup, as_stream(stream));
+}
+
+size_t tbik_rmsnorm_backward_workspace_bytes(int rows, int H, int dp, int want_dw) {
+  if (rows < 0 || H < 1 || dp < 1) return 0;
+  return (size_t)tbik::rmsnorm_bwd_ws_floats(rows, H, dp, want_dw != 0) * sizeof(float);
+}
+
+int tbik_rmsnorm_backward(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
+                          const tbik_bf16 *dy, const tbik_bf16 *dr, tbik_bf16 *dh, float *dw,
+                          int rows, int H, int64_t ld, float eps, int dp, float *ws,
+                          size_t ws_bytes, void *stream) {
+  if (!x || !r || !w || !dy || !dh) return TBIK_ERR_NULL;
+  if (rows < 0 || H < 1 || H > 65536 || ld < H) return TBIK_ERR_SHAPE;
+  if (!(eps >= 0.0f) || isinf(eps)) return TBIK_ERR_ARG;
+  if (dw) {
+    if (rows == 0 || (rows % 64) != 0) return TBIK_ERR_SHAPE;
+    if (!tp_ok(dp) || (tbik::tree_T(rows / 64) % dp) != 0) return TBIK_ERR_TP;
+    if ((rows / 64) / tbik::tree_T(rows / 64) > (1 << 20)) return TBIK_ERR_SHAPE;
+  }
+  if (!aligned(x, 2) || !aligned(r, 2) || !aligned(w, 2) || !aligned(dy, 2) || !aligned(dh, 2) ||
+      (dr && !aligned(dr, 2)) || (dw && !aligned(dw, 4)))
+    return TBIK_ERR_ALIGN;
+  if (rows == 0) return TBIK_OK;
+  if (!ws) return TBIK_ERR_WORKSPACE;
+  if (!aligned(ws, 4)) return TBIK_ERR_ALIGN;
+  if (ws_bytes < tbik_rmsnorm_backward_workspace_bytes(rows, H, dw ? dp : 1, dw != nullptr))
+    return TBIK_ERR_WORKSPACE;
+  return tbik::launch_rmsnorm_backward(x, r, w, dy, dr, dh, dw, rows, H, ld, eps, dw ? dp : 1, ws,
+                                       as_stream(stream));
+}
+
 size_t tbik_logsoftmax_workspace_bytes(int M, int V, int tp) {
   (void)V;
   if (M < 0 || tp < 1) return 0;

@@ -38,6 +38,28 @@ int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float 
                 int max_pos, int rounding, hipStream_t s);
 int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, int cols,
                   int64_t ldg, int64_t ldu, int64_t ldo, int rounding, hipStream_t s);
+// launch_rope's rounding argument selecting the inverse rotation (backward)
+constexpr int kRopeInverse = 100;
+int launch_rope_backward(const uint16_t *dy, uint16_t *dx, const int32_t *pos,
+                         const float *cos_tab, const float *sin_tab, int T, int heads,
+                         int head_dim, int64_t ld_token, int max_pos, hipStream_t s);
+int launch_swiglu_backward(const uint16_t *g, const uint16_t *u, const uint16_t *d, uint16_t *dg,
+                           uint16_t *du, int rows, int cols, int64_t ldg, int64_t ldu,
+                           int64_t ldd, int64_t lddg, int64_t lddu, hipStream_t s);
+// Workspace of the RMSNorm backward, in floats: rstd per row (rounded up to
+// 64 floats), then with dw the nleaf x H leaves and the dp x H shard nodes.
+inline int64_t rmsnorm_bwd_rstd_floats(int rows) { return ((int64_t)rows + 63) / 64 * 64; }
+inline int64_t rmsnorm_bwd_ws_floats(int rows, int H, int dp, bool want_dw) {
+  int64_t n = rmsnorm_bwd_rstd_floats(rows);
+  if (want_dw) n += (int64_t)(rows / 64) * H + (int64_t)dp * H;
+  return n;
+}
+int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t *w,
+                            const uint16_t *dy, const uint16_t *dr, uint16_t *dh, float *dw,
+                            int rows, int H, int64_t ld, float eps, int dp, float *ws,
+                            hipStream_t s);
+int launch_transpose_bf16(const uint16_t *x, int64_t ldx, uint16_t *y, int64_t ldy, int rows,
+                          int cols, hipStream_t s);
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out,
                       int M, int V, int tp, float *ws, const float *pmax, int64_t ld_pmax,
                       int npmax, hipStream_t s);
