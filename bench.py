@@ -450,6 +450,61 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
             "gaps": gaps}
         del w
 
+    if want("training"):
+        # Training side at the down projection's shape: Y = A W^T with
+        # A [4096 tokens, 14336], W [4096, 14336].  dW = dY^T A sums over the
+        # tokens (token-axis tree, dp = simulated data-parallel ranks),
+        # dA = dY W sums over the 4096 outputs; both include their operand
+        # transposes.  hipBLASLt on the same products for reference.
+        M, d, f = 4096, 4096, 14336
+        dY = inputs.normal_bf16((M, d), 3800, device=dev)
+        A = inputs.normal_bf16((M, f), 3801, device=dev)
+        W = inputs.normal_bf16((d, f), 3802, std=0.02, device=dev)
+        dW = torch.empty((d, f), dtype=torch.float32, device=dev)
+        flops = 2.0 * M * d * f
+        tr = {}
+        for dp in (1, 8):
+            ws = torch.empty((tb.lib().tbik_gemm_wgrad_workspace_bytes(M, d, f, dp) // 4 + 4,),
+                             dtype=torch.float32, device=dev)
+            t = timed(lambda: tb.tbik_gemm_wgrad(dY, A, dp=dp, ws=ws, out=dW), 10)
+            tr["wgrad_dp%d" % dp] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 1)}
+            log("wgrad dp=%d: %.3f ms = %.1f TFLOP/s" % (dp, t, flops / t / 1e9))
+            del ws
+        t = timed(lambda: torch.matmul(dY.t(), A), 10)
+        tr["wgrad_hipblaslt"] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 1)}
+        wsd = torch.empty((tb.lib().tbik_gemm_dgrad_workspace_bytes(M, d, f) // 4 + 4,),
+                          dtype=torch.float32, device=dev)
+        t = timed(lambda: tb.tbik_gemm_dgrad(dY, W, ws=wsd, want_fp32=False, want_bf16=True), 10)
+        tr["dgrad_bf16"] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 1)}
+        log("dgrad: %.3f ms = %.1f TFLOP/s" % (t, flops / t / 1e9))
+        t = timed(lambda: torch.matmul(dY, W), 10)
+        tr["dgrad_hipblaslt"] = {"ms": round(t, 4), "tflops": round(flops / t / 1e9, 1)}
+        del dY, A, W, dW, wsd
+        # backward row kernels, bytes = inputs read once + outputs written once
+        rows, H = 4096, 4096
+        x = inputs.outlier_bf16((rows, H), 3810, device=dev)
+        r = inputs.outlier_bf16((rows, H), 3811, device=dev)
+        w = inputs.normal_bf16((H,), 3812, std=0.1, mean=1.0, device=dev)
+        gy = inputs.normal_bf16((rows, H), 3813, device=dev)
+        gr = inputs.normal_bf16((rows, H), 3814, device=dev)
+        t = timed(lambda: tb.tbik_rmsnorm_backward(x, r, w, gy, gr, dp=8), 20)
+        nb = 5 * rows * H * 2 + H * 2 + H * 4
+        tr["rmsnorm_backward_4096x4096"] = {"ms": round(t, 4), "gbs": round(nb / t / 1e6, 1),
+                                            "hbm_frac": round(nb / t / 1e6 / 8000, 4)}
+        log("rmsnorm backward: %.4f ms = %.0f GB/s" % (t, nb / t / 1e6))
+        del x, r, gy, gr
+        rows, cols = 4096, 14336
+        g = inputs.normal_bf16((rows, cols), 3820, std=3.0, device=dev)
+        u = inputs.normal_bf16((rows, cols), 3821, device=dev)
+        gd = inputs.normal_bf16((rows, cols), 3822, device=dev)
+        t = timed(lambda: tb.tbik_swiglu_backward(g, u, gd), 20)
+        nb = 5 * rows * cols * 2
+        tr["swiglu_backward_4096x14336"] = {"ms": round(t, 4), "gbs": round(nb / t / 1e6, 1),
+                                            "hbm_frac": round(nb / t / 1e6 / 8000, 4)}
+        log("swiglu backward: %.4f ms = %.0f GB/s" % (t, nb / t / 1e6))
+        del g, u, gd
+        res["training"] = tr
+
     if want("swiglu"):
         rows, cols = 4096, 14336
         g = inputs.normal_bf16((rows, cols), 3600, std=3.0, device=dev)

@@ -969,22 +969,114 @@ k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uin
   if (threadIdx.x == 0) rstd_out[blockIdx.x] = rstd;
 }
 
+// Register-resident variant (the forward's k_rmsnorm_reg layout and tree):
+// every thread owns at most one chunk, x/r/dy/w/dr are read once; the two
+// row trees are the chunk tree, a butterfly over the gc lanes of a group
+// (a perfect tree, gc a power of two dividing 64) and the perfect top over
+// the T group sums in LDS.
+template <int CH>
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm_bwd_reg(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uint16_t *dy,
+                  const uint16_t *dr, uint16_t *dh, float *rstd_out, int H, int64_t ld, float eps,
+                  int T, int gc) {
+  __shared__ float gsum[2][8];
+  const int nch = H / CH;
+  const int ch = threadIdx.x;
+  const bool own = ch < nch;
+  const int64_t off = (int64_t)blockIdx.x * ld + (int64_t)ch * CH;
+  float h[CH], g[CH];
+  float part = 0.0f;
+  if (own) {
+    float b[CH], ww[CH], sq[CH];
+    load_bf16<CH>(h, x + off);
+    load_bf16<CH>(b, r + off);
+    load_bf16<CH>(g, dy + off);
+    load_bf16<CH>(ww, w + ch * CH);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      h[e] = h[e] + b[e];
+      sq[e] = h[e] * h[e];
+      g[e] = g[e] * ww[e];
+    }
+    part = chunk_tree<CH>(sq);
+  }
+  for (int o = 1; o < gc; o <<= 1) part = part + __shfl_xor(part, o);
+  if (own && (ch & (gc - 1)) == 0) gsum[0][ch / gc] = part;
+  float q2 = 0.0f;
+  if (own) {
+    float q[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) q[e] = g[e] * h[e];
+    q2 = chunk_tree<CH>(q);
+  }
+  for (int o = 1; o < gc; o <<= 1) q2 = q2 + __shfl_xor(q2, o);
+  if (own && (ch & (gc - 1)) == 0) gsum[1][ch / gc] = q2;
+  __syncthreads();
+  float t0[8], t1[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    t0[q] = q < T ? gsum[0][q] : 0.0f;
+    t1[q] = q < T ? gsum[1][q] : 0.0f;
+  }
+  for (int wdt = T; wdt > 1; wdt >>= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < wdt / 2) {
+        t0[q] = t0[2 * q] + t0[2 * q + 1];
+        t1[q] = t1[2 * q] + t1[2 * q + 1];
+      }
+  const float rstd = 1.0f / __builtin_sqrtf(t0[0] / (float)H + eps);
+  const float c = (t1[0] * ((rstd * rstd) * rstd)) / (float)H;
+  if (own) {
+    float gr[CH];
+    if (dr) load_bf16<CH>(gr, dr + off);
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      float v = (rstd * g[e]) - (c * h[e]);
+      if (dr) v = v + gr[e];
+      h[e] = v;
+    }
+    store_bf16<CH>(dh + off, h);
+  }
+  if (threadIdx.x == 0) rstd_out[blockIdx.x] = rstd;
+}
+
 // Leaves of the weight gradient: leaf b of column j adds
 // dy_ij * ((x_ij + r_ij) * rstd_i) over the 64 rows of leaf b in row order
 // from +0.  grid.x covers the columns (one per thread), grid.y the leaves.
+// VEC = 2: two consecutive columns per thread (4-byte loads; a leaf is a
+// sequential sum, so the parallelism is columns x leaves), else one.
+template <int VEC>
 __global__ void __launch_bounds__(256)
 k_rmsnorm_dw_leaves(const uint16_t *x, const uint16_t *r, const uint16_t *dy, const float *rstd,
                     float *leaves, int H, int64_t ld) {
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
+  const int col = (blockIdx.x * blockDim.x + threadIdx.x) * VEC;
   if (col >= H) return;
   const int r0 = blockIdx.y * 64;
-  float acc = 0.0f;
+  float acc[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) acc[e] = 0.0f;
+#pragma unroll 8
   for (int i = 0; i < 64; ++i) {
     const int64_t o = (int64_t)(r0 + i) * ld + col;
-    const float n = (bf2f(x[o]) + bf2f(r[o])) * rstd[r0 + i];
-    acc = acc + bf2f(dy[o]) * n;
+    const float rs = rstd[r0 + i];
+    float a[VEC], b[VEC], gy[VEC];
+    if constexpr (VEC == 2) {
+      const uint32_t ua = *reinterpret_cast<const uint32_t *>(x + o);
+      const uint32_t ub = *reinterpret_cast<const uint32_t *>(r + o);
+      const uint32_t ug = *reinterpret_cast<const uint32_t *>(dy + o);
+      a[0] = __uint_as_float(ua << 16); a[1] = __uint_as_float(ua & 0xffff0000u);
+      b[0] = __uint_as_float(ub << 16); b[1] = __uint_as_float(ub & 0xffff0000u);
+      gy[0] = __uint_as_float(ug << 16); gy[1] = __uint_as_float(ug & 0xffff0000u);
+    } else {
+      a[0] = bf2f(x[o]); b[0] = bf2f(r[o]); gy[0] = bf2f(dy[o]);
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = acc[e] + gy[e] * ((a[e] + b[e]) * rs);
   }
-  leaves[(int64_t)blockIdx.y * H + col] = acc;
+  float *out = leaves + (int64_t)blockIdx.y * H + col;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) out[e] = acc[e];
 }
 
 // Tree over the nleaf leaves of each column: PAIR inside each of the T
@@ -992,33 +1084,40 @@ k_rmsnorm_dw_leaves(const uint16_t *x, const uint16_t *r, const uint16_t *dy, co
 // shards[dp][H] when not null) and the perfect tree over the dp shards.
 // T/dp and dp are powers of two, so this is the perfect top over the T
 // groups for every dp.
-__global__ void __launch_bounds__(256)
+// Block (64, T): thread (c, q) evaluates PAIR over group q of column c;
+// the group values meet in LDS and lane q == 0 finishes the column.
+__global__ void __launch_bounds__(512)
 k_colsum_tree(const float *leaves, int nleaf, int H, int T, int dp, float *shards, float *out) {
-  const int col = blockIdx.x * blockDim.x + threadIdx.x;
-  if (col >= H) return;
+  __shared__ float gs[8][64];
+  const int col = blockIdx.x * 64 + threadIdx.x;
+  const int q = threadIdx.y;
   const int G = nleaf / T;
-  float gv[8];
-  for (int q = 0; q < T; ++q) {
+  if (col < H) {
     float st[20][1];
     float node[1] = {0.0f};
     for (int i = 0; i < G; ++i) {
       node[0] = leaves[(int64_t)(q * G + i) * H + col];
       pair_push<1, 20>(st, node, i, G);
     }
-    gv[q] = node[0];
+    gs[q][threadIdx.x] = node[0];
   }
+  __syncthreads();
+  if (q != 0 || col >= H) return;
+  float gv[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) gv[k] = k < T ? gs[k][threadIdx.x] : 0.0f;
   const int per = T / dp;
   float sv[8];
   for (int t = 0; t < dp; ++t) {
     float v[8];
-    for (int q = 0; q < per; ++q) v[q] = gv[t * per + q];
+    for (int k = 0; k < per; ++k) v[k] = gv[t * per + k];
     for (int wdt = per; wdt > 1; wdt >>= 1)
-      for (int q = 0; q < wdt / 2; ++q) v[q] = v[2 * q] + v[2 * q + 1];
+      for (int k = 0; k < wdt / 2; ++k) v[k] = v[2 * k] + v[2 * k + 1];
     sv[t] = v[0];
     if (shards) shards[(int64_t)t * H + col] = v[0];
   }
   for (int wdt = dp; wdt > 1; wdt >>= 1)
-    for (int q = 0; q < wdt / 2; ++q) sv[q] = sv[2 * q] + sv[2 * q + 1];
+    for (int k = 0; k < wdt / 2; ++k) sv[k] = sv[2 * k] + sv[2 * k + 1];
   out[col] = sv[0];
 }
 
@@ -1039,7 +1138,16 @@ int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t
   const size_t lds = 2 * (size_t)nch * sizeof(float);
   float *rstd = ws;                                 // [rows]
   const dim3 grid((unsigned)rows), block(kRowThreads);
-  switch (ch) {
+  const int gc = nch / T;
+  if (nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
+    switch (ch) {
+      case 16: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<16>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
+      case 8: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<8>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
+      case 4: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<4>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
+      case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<2>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
+      default: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<1>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
+    }
+  } else switch (ch) {
     case 16: hipLaunchKernelGGL(k_rmsnorm_bwd<16>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
     case 8: hipLaunchKernelGGL(k_rmsnorm_bwd<8>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
     case 4: hipLaunchKernelGGL(k_rmsnorm_bwd<4>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
@@ -1051,12 +1159,19 @@ int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t
   const int nleaf = rows / 64;
   float *leaves = ws + rmsnorm_bwd_rstd_floats(rows);
   float *shards = leaves + (int64_t)nleaf * H;
-  hipLaunchKernelGGL(k_rmsnorm_dw_leaves, dim3((unsigned)((H + 255) / 256), (unsigned)nleaf),
-                     dim3(256), 0, s, x, r, dy, rstd, leaves, H, ld);
+  const bool vec = (H % 2) == 0 && elem_align(x, ld, 2) >= 2 && elem_align(r, ld, 2) >= 2 &&
+                   elem_align(dy, ld, 2) >= 2;
+  if (vec)
+    hipLaunchKernelGGL(k_rmsnorm_dw_leaves<2>, dim3((unsigned)((H / 2 + 255) / 256), (unsigned)nleaf),
+                       dim3(256), 0, s, x, r, dy, rstd, leaves, H, ld);
+  else
+    hipLaunchKernelGGL(k_rmsnorm_dw_leaves<1>, dim3((unsigned)((H + 255) / 256), (unsigned)nleaf),
+                       dim3(256), 0, s, x, r, dy, rstd, leaves, H, ld);
   rc = check_launch();
   if (rc != TBIK_OK) return rc;
-  hipLaunchKernelGGL(k_colsum_tree, dim3((unsigned)((H + 255) / 256)), dim3(256), 0, s, leaves,
-                     nleaf, H, tree_T(nleaf), dp, shards, dw);
+  const int Tl = tree_T(nleaf);
+  hipLaunchKernelGGL(k_colsum_tree, dim3((unsigned)((H + 63) / 64)), dim3(64, (unsigned)Tl), 0, s,
+                     leaves, nleaf, H, Tl, dp, shards, dw);
   return check_launch();
 }
 
