@@ -15,11 +15,19 @@
 // operand mapping as the GEMM kernels.  No score matrix goes to HBM.
 //
 // Workgroup = 4 waves = 64 query rows of one (sequence, head); wave w owns 16
-// query rows and all Lk keys.  MFMA accumulator lane l, register i holds
-// row 4(l/16)+i, column l%16 of a 16x16 block.
+// query rows.  Each 64-key chunk of K and of V^T is read from HBM once per
+// workgroup into LDS and shared by the four waves; chunks past the
+// workgroup's diagonal hold only masked keys and are skipped (their zeros
+// still enter the trees at their places, so the bits do not change).  MFMA
+// accumulator lane l, register i holds row 4(l/16)+i, column l%16 of a
+// 16x16 block.
 #include "tbik_device.h"
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
+
+#ifndef TBIK_ATTN_MINB
+#define TBIK_ATTN_MINB 2
+#endif
 
 namespace tbik {
 
@@ -38,20 +46,33 @@ __device__ __forceinline__ f32x4 mfma2(const u32x4 &a0, const u32x4 &b0, const u
 }  // namespace
 
 template <int LK>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, TBIK_ATTN_MINB)
 k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, const uint16_t *Vt,
               int64_t ldvt, uint16_t *O, int64_t ldo, int heads, float scale) {
   constexpr int HD = 128;
   constexpr int NB = LK / 16;          // 16-key blocks
-  constexpr int NL = LK / 64;          // 64-key leaves of P V
-  __shared__ u32x4 pl[4][16][LK / 8];  // P rows of each wave, bf16
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int NL = LK / 64;          // 64-key chunks = leaves of P V
+  constexpr int PC = LK / 8;           // 16-byte chunks per P row
+  // LDS: one 16 KB tile that holds the current K chunk [64 keys][128 dims]
+  // during S and the current V^T chunk [128 dims][64 keys] during P V, and
+  // the P rows of each wave [16][LK].  16-byte chunks are XOR-swizzled by
+  // row so that the 16 rows one fragment read touches fall in distinct
+  // banks; 80 KB in all for LK = 512, two workgroups per CU.
+  __shared__ u32x4 tile[1024];
+  __shared__ u32x4 pl[4][16 * PC];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int xb = gridDim.x - 1 - blockIdx.x;   // longest row blocks first
   const int h = blockIdx.y % heads, b = blockIdx.y / heads;
-  const int r0 = blockIdx.x * 64 + wave * 16;        // first query row of this wave
+  const int r0 = xb * 64 + wave * 16;          // first query row of this wave
+  const int nkc = xb + 1;                      // chunks holding a visible key
   const int64_t tok0 = (int64_t)b * LK;
-  const int lr = lane & 15, lk = (lane >> 4) * 8;
+  const int lr = lane & 15, lg = lane >> 4, lk = lg * 8;
+  u32x4 *pw = pl[wave];
 
-  // ---- S = Q K^T for the wave's 16 rows and all keys
+  // ---- S = Q K^T for the wave's 16 rows over the visible chunks; the K
+  //      chunk is staged in LDS once for the four waves.  Chunks past the
+  //      diagonal hold no visible key and are not computed.
   u32x4 qa[2][2];
   {
     const uint16_t *qp = Q + (tok0 + r0 + lr) * ldq + (int64_t)h * HD + lk;
@@ -63,21 +84,47 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
   }
   float s[NB][4];
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const uint16_t *kp = K + (tok0 + nb * 16 + lr) * ldk + (int64_t)h * HD + lk;
-    u32x4 kb[2][2];
+  for (int kc = 0; kc < NL; ++kc) {
+    if (kc < nkc) {                            // uniform over the workgroup
+      u32x4 ld4[4];
 #pragma unroll
-    for (int lf = 0; lf < 2; ++lf)
+      for (int i = 0; i < 4; ++i) {
+        const int row = (tid >> 4) + 16 * i;
+        ld4[i] = *reinterpret_cast<const u32x4 *>(K + (tok0 + kc * 64 + row) * ldk +
+                                                  (int64_t)h * HD + (tid & 15) * 8);
+      }
+      __syncthreads();                         // the previous chunk is consumed
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-        kb[lf][hf] = *reinterpret_cast<const u32x4 *>(kp + 64 * lf + 32 * hf);
-    const f32x4 l0 = mfma2(qa[0][0], kb[0][0], qa[0][1], kb[0][1]);
-    const f32x4 l1 = mfma2(qa[1][0], kb[1][0], qa[1][1], kb[1][1]);
+      for (int i = 0; i < 4; ++i) {
+        const int row = (tid >> 4) + 16 * i;   // key; 16 chunks of 8 dims per row
+        tile[row * 16 + ((tid & 15) ^ (row & 15))] = ld4[i];
+      }
+      __syncthreads();
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s[nb][i] = l0[i] + l1[i];
+      for (int n4 = 0; n4 < 4; ++n4) {
+        const u32x4 *kp = &tile[(n4 * 16 + lr) * 16];
+        u32x4 kb[2][2];
+#pragma unroll
+        for (int lf = 0; lf < 2; ++lf)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf)
+            kb[lf][hf] = kp[(8 * lf + 4 * hf + lg) ^ lr];
+        const f32x4 l0 = mfma2(qa[0][0], kb[0][0], qa[0][1], kb[0][1]);
+        const f32x4 l1 = mfma2(qa[1][0], kb[1][0], qa[1][1], kb[1][1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kc * 4 + n4][i] = l0[i] + l1[i];
+      }
+    } else {
+#pragma unroll
+      for (int n4 = 0; n4 < 4; ++n4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[kc * 4 + n4][i] = 0.0f;
+    }
   }
 
-  // ---- causal softmax per row: row 4(l/16)+i, key 16 nb + l%16
+  // ---- causal softmax per row: row 4(l/16)+i, key 16 nb + l%16.  A key
+  //      block past the diagonal contributes EXP-free zeros, exactly what
+  //      the masked entries of the full row contribute.
   const int rowb = r0 + 4 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -85,21 +132,26 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
     float m = -__builtin_inff();
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      s[nb][i] = s[nb][i] * scale;
-      if (nb * 16 + lr <= row) m = __builtin_fmaxf(m, s[nb][i]);
+      if (nb < 4 * nkc) {
+        s[nb][i] = s[nb][i] * scale;
+        if (nb * 16 + lr <= row) m = __builtin_fmaxf(m, s[nb][i]);
+      }
     }
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) s[nb][i] = (nb * 16 + lr <= row) ? exp_f32(s[nb][i] - m) : 0.0f;
+    for (int nb = 0; nb < NB; ++nb)
+      s[nb][i] = (nb < 4 * nkc && nb * 16 + lr <= row) ? exp_f32(s[nb][i] - m) : 0.0f;
     // perfect tree over the keys: the 16 columns of a block across lanes
     // (xor 1, 2, 4, 8 pairs neighbouring columns), then the blocks in-lane
     float blk[NB];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       float v = s[nb][i];
+      if (nb < 4 * nkc) {
 #pragma unroll
-      for (int off = 1; off < 16; off <<= 1) v = v + __shfl_xor(v, off);
+        for (int off = 1; off < 16; off <<= 1) v = v + __shfl_xor(v, off);
+      }
       blk[nb] = v;
     }
 #pragma unroll
@@ -107,32 +159,58 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
 #pragma unroll
       for (int q = 0; q < w / 2; ++q) blk[q] = blk[2 * q] + blk[2 * q + 1];
     const float ssum = blk[0];
-    uint16_t *prow = reinterpret_cast<uint16_t *>(&pl[wave][4 * (lane >> 4) + i][0]);
+    const int prw = 4 * (lane >> 4) + i;      // row of the wave's P
+    uint16_t *prow = reinterpret_cast<uint16_t *>(pw + prw * PC);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const float p = (nb * 16 + lr <= row) ? s[nb][i] / ssum : 0.0f;
-      prow[nb * 16 + lr] = f2bf(p);
+      if (nb < 4 * nkc) {
+        const float p = (nb * 16 + lr <= row) ? s[nb][i] / ssum : 0.0f;
+        const int e = nb * 16 + lr;            // key; chunk e / 8 swizzled by the row
+        prow[(((e >> 3) ^ prw) << 3) | (e & 7)] = f2bf(p);
+      }
     }
   }
-  __syncthreads();
 
-  // ---- O = P V: leaves of 64 keys, perfect tree over the NL leaves
+  // ---- O = P V: leaves of 64 keys (one V^T chunk in LDS each), perfect
+  //      tree over the NL leaves; a leaf past the diagonal is +0, the value
+  //      of a leaf whose P entries are all zero.
   float node[8][4];
   float st[4][8][4];                   // perfect-tree stack (NL <= 8)
 #pragma unroll
   for (int kl = 0; kl < NL; ++kl) {
-    u32x4 pa[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) pa[hf] = pl[wave][lr][(64 * kl + 32 * hf + lk) / 8];
     float leaf[8][4];
+    if (kl < nkc) {
+      u32x4 ld4[4];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const uint16_t *vp = Vt + ((int64_t)h * HD + nb * 16 + lr) * ldvt + tok0 + 64 * kl + lk;
-      const u32x4 v0 = *reinterpret_cast<const u32x4 *>(vp);
-      const u32x4 v1 = *reinterpret_cast<const u32x4 *>(vp + 32);
-      const f32x4 acc = mfma2(pa[0], v0, pa[1], v1);
+      for (int i = 0; i < 4; ++i) {
+        const int d = (tid >> 3) + 32 * i;
+        ld4[i] = *reinterpret_cast<const u32x4 *>(Vt + ((int64_t)h * HD + d) * ldvt + tok0 +
+                                                  64 * kl + (tid & 7) * 8);
+      }
+      __syncthreads();                         // previous chunk consumed; P visible
 #pragma unroll
-      for (int i = 0; i < 4; ++i) leaf[nb][i] = acc[i];
+      for (int i = 0; i < 4; ++i) {
+        const int d = (tid >> 3) + 32 * i;     // dim; 8 chunks of 8 keys per row
+        tile[d * 8 + ((tid & 7) ^ ((d >> 1) & 7))] = ld4[i];
+      }
+      __syncthreads();
+      u32x4 pa[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) pa[hf] = pw[lr * PC + ((8 * kl + 4 * hf + lg) ^ lr)];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int d = nb * 16 + lr;
+        const u32x4 v0 = tile[d * 8 + (lg ^ ((d >> 1) & 7))];
+        const u32x4 v1 = tile[d * 8 + ((4 + lg) ^ ((d >> 1) & 7))];
+        const f32x4 acc = mfma2(pa[0], v0, pa[1], v1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) leaf[nb][i] = acc[i];
+      }
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) leaf[nb][i] = 0.0f;
     }
     // binary-counter merge: leaf kl joins the subtrees of the set low bits
     int lvl = 0;
