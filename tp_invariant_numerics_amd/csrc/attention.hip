@@ -53,6 +53,7 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
   constexpr int NB = LK / 16;          // 16-key blocks
   constexpr int NL = LK / 64;          // 64-key chunks = leaves of P V
   constexpr int PC = LK / 8;           // 16-byte chunks per P row
+  constexpr int PSW = (PC < 16 ? PC : 16) - 1;   // P swizzle mask: stays inside the row
   // LDS: one 16 KB tile that holds the current K chunk [64 keys][128 dims]
   // during S and the current V^T chunk [128 dims][64 keys] during P V, and
   // the P rows of each wave [16][LK].  16-byte chunks are XOR-swizzled by
@@ -166,7 +167,7 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
       if (nb < 4 * nkc) {
         const float p = (nb * 16 + lr <= row) ? s[nb][i] / ssum : 0.0f;
         const int e = nb * 16 + lr;            // key; chunk e / 8 swizzled by the row
-        prow[(((e >> 3) ^ prw) << 3) | (e & 7)] = f2bf(p);
+        prow[(((e >> 3) ^ (prw & PSW)) << 3) | (e & 7)] = f2bf(p);
       }
     }
   }
@@ -196,7 +197,7 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
       __syncthreads();
       u32x4 pa[2];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) pa[hf] = pw[lr * PC + ((8 * kl + 4 * hf + lg) ^ lr)];
+      for (int hf = 0; hf < 2; ++hf) pa[hf] = pw[lr * PC + ((8 * kl + 4 * hf + lg) ^ (lr & PSW))];
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         const int d = nb * 16 + lr;
