@@ -43,6 +43,28 @@ __device__ __forceinline__ f32x4 mfma2(const u32x4 &a0, const u32x4 &b0, const u
   return acc;
 }
 
+// src of another lane of the same 16-lane row, by a DPP pattern:
+// 0xB1 / 0x4E quad permutations [1,0,3,2] / [2,3,0,1] (lane ^ 1, lane ^ 2);
+// 0x121..0x12F rotate right by 1..15 (lane i reads lane (i - k) mod 16).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Perfect tree over the 16 lanes of a row (lane = column): levels 1-2 pair
+// lanes ^1 and ^2 (every lane gets its quad's sum), levels 3-4 add the
+// quad 4 and then 8 lanes below (mod 16), which pairs quads (0,1), (2,3)
+// in lanes 4-7 and 12-15 and then the two halves there.  Only lanes with
+// bit 2 set hold the block sum afterwards.
+__device__ __forceinline__ float row16_sum(float v) {
+  v = v + dpp<0xB1>(v);
+  v = v + dpp<0x4E>(v);
+  v = v + dpp<0x124>(v);
+  v = v + dpp<0x128>(v);
+  return v;
+}
+
 }  // namespace
 
 template <int LK>
@@ -138,28 +160,30 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
         if (nb * 16 + lr <= row) m = __builtin_fmaxf(m, s[nb][i]);
       }
     }
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+    // exact maximum over the row's 16 lanes (rotations by 1, 2, 4, 8)
+    m = __builtin_fmaxf(m, dpp<0x121>(m));
+    m = __builtin_fmaxf(m, dpp<0x122>(m));
+    m = __builtin_fmaxf(m, dpp<0x124>(m));
+    m = __builtin_fmaxf(m, dpp<0x128>(m));
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb)
       s[nb][i] = (nb < 4 * nkc && nb * 16 + lr <= row) ? exp_f32(s[nb][i] - m) : 0.0f;
     // perfect tree over the keys: the 16 columns of a block across lanes
-    // (xor 1, 2, 4, 8 pairs neighbouring columns), then the blocks in-lane
+    // (row16_sum), then the blocks in-lane; lanes 4-7 and 12-15 of the row
+    // finish it and pass the sum to the lanes 4 below them (mod 16)
     float blk[NB];
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      float v = s[nb][i];
-      if (nb < 4 * nkc) {
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) v = v + __shfl_xor(v, off);
-      }
-      blk[nb] = v;
-    }
+    for (int nb = 0; nb < NB; ++nb) blk[nb] = nb < 4 * nkc ? row16_sum(s[nb][i]) : 0.0f;
 #pragma unroll
     for (int w = NB; w > 1; w >>= 1)
 #pragma unroll
       for (int q = 0; q < w / 2; ++q) blk[q] = blk[2 * q] + blk[2 * q + 1];
-    const float ssum = blk[0];
+    // one DPP move with bank mask 0b0101: lanes 0-3 and 8-11 take the value
+    // of the lanes 4 below them (mod 16), lanes 4-7 and 12-15 keep theirs
+    // (no branch: a DPP read of lanes switched off by a branch gives 0)
+    const float ssum = __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, blk[0]),
+                                           __builtin_bit_cast(int, blk[0]), 0x124, 0xf, 0x5, false));
     const int prw = 4 * (lane >> 4) + i;      // row of the wave's P
     uint16_t *prow = reinterpret_cast<uint16_t *>(pw + prw * PC);
 #pragma unroll
