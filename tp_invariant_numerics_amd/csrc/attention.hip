@@ -105,17 +105,26 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
       for (int hf = 0; hf < 2; ++hf)
         qa[lf][hf] = *reinterpret_cast<const u32x4 *>(qp + 64 * lf + 32 * hf);
   }
+  // chunk loads: K chunk kc row (tid >> 4) + 16 i, dims 8 (tid & 15) ..;
+  // V^T chunk kl dim (tid >> 3) + 32 i, keys 64 kl + 8 (tid & 7) ..
+  auto load_k = [&](u32x4 (&r)[4], int kc) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = *reinterpret_cast<const u32x4 *>(K + (tok0 + kc * 64 + (tid >> 4) + 16 * i) * ldk +
+                                              (int64_t)h * HD + (tid & 15) * 8);
+  };
+  auto load_v = [&](u32x4 (&r)[4], int kl) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r[i] = *reinterpret_cast<const u32x4 *>(Vt + ((int64_t)h * HD + (tid >> 3) + 32 * i) * ldvt +
+                                              tok0 + 64 * kl + (tid & 7) * 8);
+  };
+  u32x4 ld4[4];                                // the next chunk, in flight
+  load_k(ld4, 0);
   float s[NB][4];
 #pragma unroll
   for (int kc = 0; kc < NL; ++kc) {
     if (kc < nkc) {                            // uniform over the workgroup
-      u32x4 ld4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = (tid >> 4) + 16 * i;
-        ld4[i] = *reinterpret_cast<const u32x4 *>(K + (tok0 + kc * 64 + row) * ldk +
-                                                  (int64_t)h * HD + (tid & 15) * 8);
-      }
       __syncthreads();                         // the previous chunk is consumed
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -123,6 +132,8 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
         tile[row * 16 + ((tid & 15) ^ (row & 15))] = ld4[i];
       }
       __syncthreads();
+      if (kc + 1 < nkc) load_k(ld4, kc + 1);
+      else load_v(ld4, 0);                     // first V^T chunk, during the softmax
 #pragma unroll
       for (int n4 = 0; n4 < 4; ++n4) {
         const u32x4 *kp = &tile[(n4 * 16 + lr) * 16];
@@ -205,13 +216,6 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
   for (int kl = 0; kl < NL; ++kl) {
     float leaf[8][4];
     if (kl < nkc) {
-      u32x4 ld4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int d = (tid >> 3) + 32 * i;
-        ld4[i] = *reinterpret_cast<const u32x4 *>(Vt + ((int64_t)h * HD + d) * ldvt + tok0 +
-                                                  64 * kl + (tid & 7) * 8);
-      }
       __syncthreads();                         // previous chunk consumed; P visible
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -219,6 +223,7 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
         tile[d * 8 + ((tid & 7) ^ ((d >> 1) & 7))] = ld4[i];
       }
       __syncthreads();
+      if (kl + 1 < nkc) load_v(ld4, kl + 1);
       u32x4 pa[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) pa[hf] = pw[lr * PC + ((8 * kl + 4 * hf + lg) ^ (lr & PSW))];
