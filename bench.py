@@ -443,12 +443,67 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
                                                gaps[name]["tokens"],
                                                gaps[name]["max_abs_dlogprob"],
                                                gaps[name]["mean_abs_dlogprob"]))
+        # Negative control at the logprob level (TBIK summary page, Abstract:
+        # the TP size changes the outputs of ordinary kernels): the two
+        # row-parallel projections computed the usual way -- hipBLASLt on
+        # each K shard, the bf16 shard outputs summed in rank order -- at
+        # tp = 1, 2, 4, everything else unchanged.
+        def naive_rowpar(A_, W_, out, tpn):
+            ks = A_.shape[1] // tpn
+            acc = None
+            for t in range(tpn):
+                part = torch.matmul(A_[:, t * ks:(t + 1) * ks],
+                                    W_[:, t * ks:(t + 1) * ks].t().contiguous())
+                acc = part if acc is None else acc + part
+            out.copy_(acc)
+
+        base = decoder_forward(w, tok, cfg, tp=1, rowpar=naive_rowpar).double()
+        neg = {}
+        for tpn in (2, 4):
+            lp = decoder_forward(w, tok, cfg, tp=tpn, rowpar=naive_rowpar).double()
+            d_lp = (lp - base).abs()
+            neg["tp%d_vs_tp1" % tpn] = {"tokens_differing": int((d_lp > 0).sum().item()),
+                                        "tokens": int(d_lp.numel()),
+                                        "max_abs_dlogprob": float(d_lp.max().item()),
+                                        "mean_abs_dlogprob": float(d_lp.mean().item())}
+            log("negative control decoder (hipBLASLt shards, rank-order bf16 sum) tp%d vs tp1: "
+                "%d/%d tokens differ, max |dlp| %.3g" % (tpn, neg["tp%d_vs_tp1" % tpn]
+                                                         ["tokens_differing"], d_lp.numel(),
+                                                         d_lp.max().item()))
+        tb4 = decoder_forward(w, tok, cfg, tp=4).double()
+        res["tp_logprob_gap"] = {
+            "tbik_tp4_vs_tp1_tokens_differing": int((tb4 != ref).sum().item()),
+            "negative_control": neg}
         res["rounding_location_gap"] = {
             "what": "engine tp=4 (nodes rounding each op to bf16) vs trainer tp=1 "
                     "(fp32-intermediate nodes); random-init weights, so the mechanism, "
                     "not the pages' RL numbers",
             "gaps": gaps}
         del w
+
+    if want("ceilings"):
+        # measured ceilings beside the spec peaks: a large vendor GEMM for the
+        # matrix cores, a 1 GiB device copy and a 2 GiB read for HBM
+        n = 8192
+        a8 = inputs.normal_bf16((n, n), 3900, device=dev)
+        b8 = inputs.normal_bf16((n, n), 3901, device=dev)
+        t = timed(lambda: torch.matmul(a8, b8), 10)
+        ceil = {"hipblaslt_bf16_8192cubed_tflops": round(2.0 * n ** 3 / t / 1e9, 1)}
+        del a8, b8
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        t = timed(lambda: dst.copy_(src), 20)
+        ceil["copy_1GiB_gbs"] = round(2 * (1 << 30) / t / 1e6, 1)
+        del src, dst
+        rd = torch.ones((1 << 29,), dtype=torch.float32, device=dev)       # 2 GiB
+        t = timed(lambda: torch.sum(rd), 20)
+        ceil["read_2GiB_sum_gbs"] = round((1 << 31) / t / 1e6, 1)
+        del rd
+        ceil["spec"] = {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+        res["measured_ceilings"] = ceil
+        log("ceilings: hipBLASLt 8192^3 %.0f TFLOP/s, copy %.0f GB/s, read %.0f GB/s"
+            % (ceil["hipblaslt_bf16_8192cubed_tflops"], ceil["copy_1GiB_gbs"],
+               ceil["read_2GiB_sum_gbs"]))
 
     if want("training"):
         # Training side at the down projection's shape: Y = A W^T with
@@ -519,6 +574,17 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
     return res
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(inputs, np, log, A, W, tp):
     """The CPU oracle (scalar C, as it stands) on a bounded sample of the
     headline workload: all M rows x a block of output columns, simulated tp."""
@@ -540,6 +606,7 @@ def cpu_baseline(inputs, np, log, A, W, tp):
     log("cpu oracle: %d x %d outputs, K=%d, tp=%d, %d threads: %.2f s" % (M, cols, K, tp, nth, dt))
     return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
             "seconds": round(dt, 2),
+            "cpu_model": _cpu_model(),
             "sample": "oracle tpsim GEMM (scalar leaves, same tree) on A[%d,%d] x W[:%d] "
                       "(all rows, first %d output columns), tp=%d" % (M, K, cols, cols, tp)}
 

@@ -93,10 +93,14 @@ def _rope_tables(theta, hd, L, dev):
     return _ROPE[key]
 
 
-def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA, rounding=None):
+def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA, rounding=None,
+                    rowpar=None):
     """tokens [B, L] int32 on the device -> logprobs [B, L-1] fp32 of
     tokens[:, 1:] given their prefixes.  rounding: optional {node: "once" |
-    "each_op"} for the nodes in NODES (default: all "once")."""
+    "each_op"} for the nodes in NODES (default: all "once").  rowpar:
+    optional callable (A, W, out_bf16, tp) replacing the library's
+    row-parallel projection, for comparisons against other reduction
+    orders; None (the default) uses the tree."""
     rc_of = _rounding_codes(rounding)
     B, L = tokens.shape
     d, H, hd, f, V = cfg.d, cfg.heads, cfg.head_dim, cfg.ffn, cfg.vocab
@@ -162,12 +166,18 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA, rounding=No
                     _p(P), L, L * L, _p(vT, r0), T, hd * T,
                     None, d, hd, _p(attn, r0 * d), L, hd, L, H, leaf_mode, st)
                 _chk(rc, "tbik_gemm_strided_batched")
-        _gemm_rowpar(attn, lw["w_o"], x, tp, leaf_mode, ws)
+        if rowpar is None:
+            _gemm_rowpar(attn, lw["w_o"], x, tp, leaf_mode, ws)
+        else:
+            rowpar(attn, lw["w_o"], x, tp)
         norm(x, lw["mlp_norm"])
         _gemm(h, d, lw["w_gu"], d, None, gu, 2 * f, T, 2 * f, d, leaf_mode)
         rc = L_.tbik_swiglu_ex(_p(gu), _p(gu, f), _p(a), T, f, 2 * f, 2 * f, f, rc_of["swiglu"], st)
         _chk(rc, "tbik_swiglu_ex")
-        _gemm_rowpar(a, lw["w_down"], x, tp, leaf_mode, ws)
+        if rowpar is None:
+            _gemm_rowpar(a, lw["w_down"], x, tp, leaf_mode, ws)
+        else:
+            rowpar(a, lw["w_down"], x, tp)
     norm(x, weights["final_norm"])
     lm = weights["lm_head"]
     targets = torch.zeros((B, L), dtype=torch.int32, device=dev)
