@@ -163,3 +163,25 @@ def test_fused_attention_equals_composition(B, L, H):
                                         B, scale, tb._stream())
     assert rc == 0
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+def test_decoder_negative_control_rank_order_sum(full):
+    """Negative control (TBIK summary page, Abstract): the row-parallel
+    projections done the usual way -- hipBLASLt per K shard, bf16 shard
+    outputs summed in rank order -- change the logprobs with the TP size;
+    the library's tree does not."""
+    cfg, w, tok = full
+
+    def naive(A, W, out, tp):
+        ks = A.shape[1] // tp
+        acc = None
+        for t in range(tp):
+            part = torch.matmul(A[:, t * ks:(t + 1) * ks], W[:, t * ks:(t + 1) * ks].t().contiguous())
+            acc = part if acc is None else acc + part
+        out.copy_(acc)
+
+    say("decoder negative control tp1 / tp4")
+    n1 = decoder_forward(w, tok, cfg, tp=1, rowpar=naive)
+    n4 = decoder_forward(w, tok, cfg, tp=4, rowpar=naive)
+    assert np.count_nonzero(u32(n1) != u32(n4)) > 0
+    assert np.abs(n1.cpu().numpy() - n4.cpu().numpy()).max() < 0.5
