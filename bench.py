@@ -30,7 +30,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "invariant GEMM TFLOP/s (% MFMA peak, overhead vs hipBLASLt); 0 bit mismatches"
 
 # The headline's shard-partials kernel, as named in a rocprofv3 kernel trace.
-HEAD_KERNEL = "k_gemm_ring<4, 4, 2, 2, 4, 2, false, 28, 0, 0, 1, 1>"
+HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 28, 0, 0, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs (profiles/
 # k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 65017 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000, the factors being what a plain 1 GiB device

@@ -24,12 +24,9 @@
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
 
-// two-workgroups-per-CU tiles for small groups
-#ifndef TBIK_RING_TWIN_PERFECT
-#define TBIK_RING_TWIN_PERFECT 1
-#endif
-#ifndef TBIK_RING_TWIN
-#define TBIK_RING_TWIN 1
+// Minimum split of 28-leaf-group GEMMs when a workspace is given.
+#ifndef TBIK_SPLIT28_MIN
+#define TBIK_SPLIT28_MIN 2
 #endif
 
 // Small-M kernel: leaves of operand loads in flight ahead of the MFMAs.
@@ -37,8 +34,8 @@
 #define TBIK_SMALL_PF 2
 #endif
 
-// Ring geometry: RING_WM x RING_WN 16x16 blocks per wave, 4 waves stacked
-// along M, RING_S stages.
+// Narrow ring geometry: RING_WM x RING_WN 16x16 blocks per wave, 4 waves
+// stacked along M, RING_S stages.
 #ifndef TBIK_RING_WM
 #define TBIK_RING_WM 2
 #endif
@@ -54,20 +51,9 @@
 #ifndef TBIK_RING_WAVES_N
 #define TBIK_RING_WAVES_N 1
 #endif
-// fragment reads one leaf ahead of the MFMAs (narrow / wide tiles)
+// fragment reads one leaf ahead of the MFMAs (narrow tiles)
 #ifndef TBIK_RING_PIPE
 #define TBIK_RING_PIPE 1
-#endif
-#ifndef TBIK_RING_WIDE_PIPE
-#define TBIK_RING_WIDE_PIPE 0
-#endif
-// whole-part perfect trees as one compile-time group (power-of-two G)
-#ifndef TBIK_RING_PERFECT
-#define TBIK_RING_PERFECT 1
-#endif
-// wide (128 x 128) tiles where the tree state fits
-#ifndef TBIK_RING_WIDE
-#define TBIK_RING_WIDE 1
 #endif
 // leaf accumulators per wave: 3 lets a leaf's merge overlap the next leaf's
 // MFMAs, 2 saves one register tile
@@ -541,6 +527,8 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using RG = Ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE>;
   constexpr int MT = RG::MT, NT = RG::NT, R = RG::R, WAVES = RG::WAVES;
+  static_assert(WN == 4 || (WN == 2 && WAVES_N == 4),
+                "the row-maximum epilogue covers these wave tiles only");
   constexpr int DPW = RG::DPW, DPA = RG::DPA, SEGA = RG::SEGA;
   __shared__ u32x4 ring[S * RG::SLOT];
 
@@ -696,6 +684,47 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
           if ((lane & 15) == 15 && row < p.M && n0 + wn * 16 * WN < p.N)
             p.pmax[(int64_t)row * p.ld_pmax + cblk] = mx;
         }
+      }
+    }
+  } else if constexpr (WN == 2 && WAVES_N == 4) {
+    // 32-column waves: each wave's row maxima over its 32 columns go to LDS
+    // (the ring is free once every wave is past its last leaf), then the
+    // two halves of each 64-column block are combined.
+    if (p.pmax) {
+      float *pm = reinterpret_cast<float *>(ring);    // [MT rows][WAVES_N]
+      __syncthreads();
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int bn = 0; bn < WN; ++bn) {
+            const int col = n0 + wn * 16 * WN + 16 * bn + (lane & 15);
+            if (col < p.N) mx = __builtin_fmaxf(mx, node[(bm * WN + bn) * 4 + i]);
+          }
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x111, 0xf, 0xf, false)));
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x112, 0xf, 0xf, false)));
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x114, 0xf, 0xf, false)));
+          mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                       __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                       0x118, 0xf, 0xf, false)));
+          if ((lane & 15) == 15) pm[(wm * 16 * WM + 16 * bm + orow + i) * WAVES_N + wn] = mx;
+        }
+      }
+      __syncthreads();
+      for (int e = threadIdx.x; e < MT * (WAVES_N / 2); e += 64 * WAVES) {
+        const int r = e / (WAVES_N / 2), b = e - r * (WAVES_N / 2);
+        const int row = m0 + r, c0 = n0 + 64 * b;
+        if (row < p.M && c0 < p.N)
+          p.pmax[(int64_t)row * p.ld_pmax + c0 / 64] =
+              __builtin_fmaxf(pm[r * WAVES_N + 2 * b], pm[r * WAVES_N + 2 * b + 1]);
       }
     }
   }
@@ -864,9 +893,9 @@ static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
 }
 
 // Tile geometries: "narrow" 128 x 64 (4 waves of 32 x 64 along M, three
-// leaf accumulators) and "wide" 128 x 128 (2 x 2 waves of 64 x 64, two leaf
-// accumulators) -- the wide tile moves a third less data per MFMA but only
-// fits when the tree's live state is small.
+// leaf accumulators; the fallback for few tiles and deep group stacks) and
+// "wide" 128 x 128 (8 waves of 64 x 32, below) -- the wide tile moves a third
+// less data per MFMA.
 template <int GS, int U, int GD, int TD>
 static int launch_narrow(const GemmArgs &a, hipStream_t s) {
   // fragment pipelining only with the compile-time schedules, whose live
@@ -875,29 +904,32 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
                          TBIK_RING_S, TBIK_RING_NX, (TBIK_RING_PIPE != 0 && GS > 0), GS, U, GD, TD>(
       a, s);
 }
-template <int GS, int TD, int U = 0>
-static int launch_wide(const GemmArgs &a, hipStream_t s) {
-  return launch_ring_cfg<4, 4, 2, 2, 4, 2, TBIK_RING_WIDE_PIPE != 0, GS, U, 0, TD>(a, s);
-}
-
-// "Twin" tiles: 128 x 64 like the narrow ones, but compiled for two
-// workgroups per CU (<= 256 registers per wave: two leaf accumulators, no
-// fragment pipelining, a 3-stage ring of 72 KB).  The copy of operands into
-// LDS proceeds at a fixed rate per workgroup whatever the ring depth, so a
-// second resident workgroup nearly doubles it; used where the group's tree
-// state fits the budget (groups of 4, 8 and 11 leaves).
+// "Wide" tiles: 128 x 128 with 8 waves of 64 x 32, two waves per SIMD (so
+// <= 256 registers per wave: two leaf accumulators plus the tree state of
+// 32 outputs per lane) and a 4-stage ring of 128 KB.  Against 4 waves of
+// 64 x 64 with the same tile (one wave per SIMD, ~460 registers) the copy of
+// the operands into LDS runs at nearly twice the rate: the outstanding
+// L1 -> L2 requests per CU grow with the resident waves, and the average L2
+// latency decides the rate at a given count.
 template <int GS, int U = 1>
-static int launch_twin(const GemmArgs &a, hipStream_t s) {
+static int launch_wide(const GemmArgs &a, hipStream_t s) {
   if constexpr (GS == 16 || GS == 32) {
-    // a whole part as one perfect tree (one group per part)
-    if (a.gpp == 1) return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, U, 0, 1, 2>(a, s);
+    if (a.gpp == 1) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1>(a, s);
+    return TBIK_ERR_ARG;
+  } else if constexpr (GS == 28) {
+    // at most 4 groups per part (8 would spill the group stack)
+    switch (a.gpp) {
+      case 1:
+      case 2: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 0, 0, 1, 1>(a, s);
+      case 4: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 0, 0, 2, 1>(a, s);
+    }
     return TBIK_ERR_ARG;
   } else {
     switch (a.gpp) {
       case 1:
-      case 2: return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, 1, 0, 1, 2>(a, s);
-      case 4: return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, 1, 0, 2, 2>(a, s);
-      case 8: return launch_ring_cfg<2, 4, 4, 1, 3, 2, false, GS, 1, 0, 3, 2>(a, s);
+      case 2: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 1, 0, 1, 1>(a, s);
+      case 4: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 1, 0, 2, 1>(a, s);
+      case 8: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 1, 0, 3, 1>(a, s);
     }
     return TBIK_ERR_ARG;
   }
@@ -922,59 +954,25 @@ static bool ring_supported_g(int G) {
 
 static int launch_ring(const GemmArgs &a, hipStream_t s) {
   const int G = a.G;
-#if TBIK_RING_TWIN
-  {
-    const int64_t twin_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 63) / 64) * a.parts;
-    if (twin_tiles >= 512) {
-      if (TBIK_RING_TWIN_PERFECT && (G & (G - 1)) == 0 && a.gpp > 1 && G * a.gpp >= 8 &&
-          G * a.gpp <= 32) {
-        // the part's tree is one perfect tree over G * gpp leaves (as for
-        // the wide tiles below)
-        GemmArgs b = a;
-        b.G = G * a.gpp;
-        b.gpp = 1;
-        return b.G == 32 ? launch_twin<32, 0>(b, s)
-                         : b.G == 16 ? launch_twin<16, 0>(b, s) : launch_twin<8>(b, s);
-      }
-      if (G == 4) return launch_twin<4>(a, s);
-      if (G == 8) return launch_twin<8>(a, s);
-      if (G == 11) return launch_twin<11>(a, s);
-    }
-  }
-#endif
-#if TBIK_RING_WIDE
-  // wide tiles where the live tree state fits (G = 28 with at most two
-  // groups per part, G = 8 with any number) and there are enough of them to
-  // occupy every CU at least twice
   const int64_t wide_tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * a.parts;
-  if (wide_tiles >= 512) {
-  // (a stack depth TD >= log2(groups) is valid; TD = 1 for a single group
-  //  allocates registers better than TD = 0)
-  if (G == 28 && a.gpp <= 2) return launch_wide<28, 1>(a, s);
-  if (G == 11 && a.gpp <= 2) return launch_wide<11, 1>(a, s);
-#if TBIK_RING_PERFECT
-  // G a power of two: the part's tree (PAIR of each group = a perfect tree,
-  // then the perfect top over gpp groups) is one perfect tree over G * gpp
-  // leaves, evaluated as a single compile-time group
-  // (8, 16 and 32 leaves fit the register budget; 64 would spill)
-  if ((G & (G - 1)) == 0 && a.gpp > 1 && G * a.gpp >= 8 && G * a.gpp <= 32) {
-    GemmArgs b = a;
-    b.G = G * a.gpp;
-    b.gpp = 1;
-    return b.G == 32 ? launch_wide<32, 1, 1>(b, s)
-                     : b.G == 16 ? launch_wide<16, 1, 1>(b, s) : launch_wide<8, 1, 1>(b, s);
-  }
-#endif
-  if (G == 8) {
-    switch (a.gpp) {
-      case 1:
-      case 2: return launch_wide<8, 1>(a, s);
-      case 4: return launch_wide<8, 2>(a, s);
-      case 8: return launch_wide<8, 3>(a, s);
+  if (wide_tiles >= 256) {
+    // 128 x 128 tiles, 8 waves: wherever the tree state of a 64 x 32 wave
+    // tile fits 256 registers and there are enough tiles for every CU
+    if ((G & (G - 1)) == 0 && a.gpp > 1 && G * a.gpp >= 8 && G * a.gpp <= 32) {
+      // G a power of two: the part's tree (PAIR of each group = a perfect
+      // tree, then the perfect top over gpp groups) is one perfect tree over
+      // G * gpp leaves, evaluated as a single compile-time group
+      GemmArgs b = a;
+      b.G = G * a.gpp;
+      b.gpp = 1;
+      return b.G == 32 ? launch_wide<32, 0>(b, s)
+                       : b.G == 16 ? launch_wide<16, 0>(b, s) : launch_wide<8>(b, s);
     }
+    if (G == 4) return launch_wide<4>(a, s);
+    if (G == 8) return launch_wide<8>(a, s);
+    if (G == 11) return launch_wide<11>(a, s);
+    if (G == 28 && a.gpp <= 4) return launch_wide<28>(a, s);
   }
-  }
-#endif
   if (G == 28) return launch_narrow_td<28, 1, 0>(a, s);
   if (G == 11) return launch_narrow_td<11, 1, 0>(a, s);
   if (G == 8) return launch_narrow_td<8, 1, 0>(a, s);
@@ -1000,16 +998,23 @@ static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
 }
 
 // Number of aligned tree nodes (1, 2, 4 or 8 parts) into which tbik_gemm
-// splits K when a workspace is given: the smallest split that gives the ring
-// kernel about one 128 x 64 workgroup per CU.  Measured on the M = 33..512,
-// K = 14336, N = 4096 projections, one workgroup per CU beats two (the extra
-// partials cost more HBM traffic than the added occupancy returns).
-// 1 = no split (small M, batched, scalar leaves, or enough tiles).
+// splits K when a workspace is given (the split is at node boundaries, so the
+// bits do not change).  28-leaf groups (K = 14336): the wide tiles hold at
+// most 4 groups per part without spilling, so at least 2 parts, and more
+// until the wide tiles fill every CU.  Otherwise the smallest split that
+// gives the ring kernel about one 128 x 64 workgroup per CU.  1 = no split
+// (small M, batched, scalar leaves, or enough tiles).
 int gemm_split_parts(int M, int N, int K, int batch, int leaf_mode) {
   if (leaf_mode != TBIK_LEAF_MFMA || batch != 1 || M <= 32 || N <= 0 || K <= 0) return 1;
   const int nb = K / 64;
   const int T = tree_T(nb);
   if (!ring_supported_g(nb / T)) return 1;
+  if (nb / T == 28 && T == 8) {
+    const int64_t wide = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    int p = TBIK_SPLIT28_MIN;
+    while (p < T && wide * p < 256) p <<= 1;
+    return p;
+  }
   const int64_t narrow = (int64_t)((M + 127) / 128) * ((N + 63) / 64);
   for (int p = 1; p <= T; p <<= 1)
     if (narrow * p >= 256) return p;
