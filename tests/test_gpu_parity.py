@@ -369,7 +369,7 @@ def _block_max_ref(C):
 
 
 @pytest.mark.parametrize("M,N,K", [(512, 151936, 4096), (100, 1000, 2048), (8, 300, 1024),
-                                   (33, 65, 64 * 28)])
+                                   (33, 65, 64 * 28), (1024, 33000, 2048)])
 def test_gemm_logits_row_maxima(M, N, K):
     """The LM-head GEMM with fused 64-column row maxima: C is bitwise the
     plain GEMM's, pmax is exactly the maximum of each block of C."""
