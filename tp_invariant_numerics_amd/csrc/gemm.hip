@@ -29,6 +29,11 @@
 #define TBIK_SPLIT28_MIN 2
 #endif
 
+// Small-M kernel (M <= 16): each group's tree split over two waves (2) or
+// not (1).
+#ifndef TBIK_SMALL_GSPLIT
+#define TBIK_SMALL_GSPLIT 2
+#endif
 // Small-M kernel: leaves of operand loads in flight ahead of the MFMAs.
 #ifndef TBIK_SMALL_PF
 #define TBIK_SMALL_PF 2
@@ -123,14 +128,16 @@ __device__ __forceinline__ void leaf_mfma(float (&out)[4 * WM * WN], const u32x4
 // GD: stack depth for PAIR inside a group (>= bit length of G-1).
 // TD: stack depth over the groups of one wave group (log2 of their count).
 // PF: leaves whose operand loads are in flight ahead of the MFMAs.
-template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1>
-__global__ void __launch_bounds__(64 * WAVES * KSPLIT)
+template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1, int GSPLIT = 1>
+__global__ void __launch_bounds__(64 * WAVES * KSPLIT * GSPLIT)
 k_gemm_mfma(GemmArgs p) {
   constexpr int R = 4 * WM * WN;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int ks = wave / WAVES;
-  const int wn = wave - ks * WAVES;
+  const int wg = wave / WAVES;                  // (group-split index, k split index)
+  const int ks = wg / GSPLIT;
+  const int gsi = wg - ks * GSPLIT;
+  const int wn = wave - wg * WAVES;
   const int part = blockIdx.z % p.parts;
   const int bat = blockIdx.z / p.parts;
   const int m0 = blockIdx.y * (16 * WM);
@@ -165,8 +172,19 @@ k_gemm_mfma(GemmArgs p) {
   float top[TD > 0 ? TD : 1][R];
   float node[R];
 
-  const int nleaf = gpw * G;
-  int64_t koff = (int64_t)gfirst * G * 64;
+  // GSPLIT = 2 (one group per wave group): the group's PAIR is split at its
+  // binary decomposition -- the perfect tree over the first H leaves (H the
+  // largest power of two below G) and PAIR over the other G - H, whose sum
+  // is PAIR over the group -- and the two halves run on two waves.
+  int Gw = G, lfirst = 0;
+  if constexpr (GSPLIT == 2) {
+    int H = 1;
+    while (2 * H < G) H *= 2;
+    Gw = gsi == 0 ? H : G - H;
+    lfirst = gsi == 0 ? 0 : H;
+  }
+  const int nleaf = gpw * Gw;
+  int64_t koff = ((int64_t)gfirst * G + lfirst) * 64;
   // Slot q of fa / fb holds the leaf l with l % PF == q: the loop is unrolled
   // by PF so that slots are named statically and no in-flight register is
   // copied; leaf l+PF is requested into the slot right after leaf l's MFMAs.
@@ -189,7 +207,7 @@ k_gemm_mfma(GemmArgs p) {
           load_frags<WM>(fa[q], ap, av, koff + 64 * (q + PF));
           load_frags<WN>(fb[q], wp, wv, koff + 64 * (q + PF));
         }
-        if (pair_push<R, GD>(s, node, c, G)) {
+        if (pair_push<R, GD>(s, node, c, Gw)) {
           pair_push<R, TD>(top, node, gi, gpw);
           ++gi;
           c = 0;
@@ -202,17 +220,19 @@ k_gemm_mfma(GemmArgs p) {
   }
   // node = this wave group's node of the tree.
 
-  if constexpr (KSPLIT > 1) {
-    __shared__ float red[KSPLIT][WAVES][R][64];
+  if constexpr (KSPLIT * GSPLIT > 1) {
+    __shared__ float red[KSPLIT * GSPLIT][WAVES][R][64];
 #pragma unroll
-    for (int r = 0; r < R; ++r) red[ks][wn][r][lane] = node[r];
+    for (int r = 0; r < R; ++r) red[wg][wn][r][lane] = node[r];
     __syncthreads();
-    if (ks != 0) return;
+    if (wg != 0) return;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float v[KSPLIT];
 #pragma unroll
-      for (int q = 0; q < KSPLIT; ++q) v[q] = red[q][wn][r][lane];
+      for (int q = 0; q < KSPLIT; ++q)
+        v[q] = GSPLIT == 2 ? red[2 * q][wn][r][lane] + red[2 * q + 1][wn][r][lane]
+                           : red[q][wn][r][lane];
 #pragma unroll
       for (int w = KSPLIT; w > 1; w >>= 1) {
 #pragma unroll
@@ -853,12 +873,12 @@ k_tree_combine4(const float *ws, int64_t mn, int N, float *C, uint16_t *Cb, int6
 // ---------------------------------------------------------------------------
 
 
-template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1>
+template <int WM, int WN, int WAVES, int KSPLIT, int GD, int TD, int PF = 1, int GSPLIT = 1>
 static int launch_cfg(const GemmArgs &a, int batch, hipStream_t s) {
   dim3 grid((unsigned)((a.N + 16 * WN * WAVES - 1) / (16 * WN * WAVES)),
             (unsigned)((a.M + 16 * WM - 1) / (16 * WM)), (unsigned)(batch * a.parts));
-  hipLaunchKernelGGL((k_gemm_mfma<WM, WN, WAVES, KSPLIT, GD, TD, PF>), grid,
-                     dim3(64 * WAVES * KSPLIT), 0, s, a);
+  hipLaunchKernelGGL((k_gemm_mfma<WM, WN, WAVES, KSPLIT, GD, TD, PF, GSPLIT>), grid,
+                     dim3(64 * WAVES * KSPLIT * GSPLIT), 0, s, a);
   return check_launch();
 }
 
@@ -988,6 +1008,17 @@ static int launch_ring(const GemmArgs &a, hipStream_t s) {
 // Small M: one wave per group of the part, combined in LDS.
 template <int WM, int GD>
 static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
+  // the split pays for 16-row tiles (M <= 16: +20% at K = 14336); with
+  // 32-row tiles the second wave's register tile and LDS exchange cost more
+  if (TBIK_SMALL_GSPLIT == 2 && WM == 1 && a.G >= 2) {
+    switch (a.gpp) {
+      case 1: return launch_cfg<WM, 1, 1, 1, GD, 0, TBIK_SMALL_PF, 2>(a, batch, s);
+      case 2: return launch_cfg<WM, 1, 1, 2, GD, 0, TBIK_SMALL_PF, 2>(a, batch, s);
+      case 4: return launch_cfg<WM, 1, 1, 4, GD, 0, TBIK_SMALL_PF, 2>(a, batch, s);
+      case 8: return launch_cfg<WM, 1, 1, 8, GD, 0, TBIK_SMALL_PF, 2>(a, batch, s);
+    }
+    return TBIK_ERR_ARG;
+  }
   switch (a.gpp) {
     case 1: return launch_cfg<WM, 1, 1, 1, GD, 0, TBIK_SMALL_PF>(a, batch, s);
     case 2: return launch_cfg<WM, 1, 1, 2, GD, 0, TBIK_SMALL_PF>(a, batch, s);
