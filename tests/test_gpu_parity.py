@@ -455,6 +455,25 @@ def test_gemm_shard_and_partials_match_tpsim(orc, leaf):
         assert same_bits(parts.cpu().numpy(), refws)
 
 
+@pytest.mark.parametrize("M,N", [(256, 4096), (300, 4000)])
+def test_tp8_partials_of_paired_shards(M, N):
+    """At these sizes the tp = 8 partials kernel streams two consecutive
+    shards per workgroup; each partial must still be exactly that shard's
+    node, as one rank computes it from its own K slice."""
+    K, tp = 14336, 8
+    A = inputs.normal_bf16((M, K), 7300 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 7301 + N, std=0.02, device=DEV)
+    say("tp8 paired partials", M, N, K)
+    ws = tb.tbik_gemm_tp_partials(A, W, tp)
+    ks = K // tp
+    for t in range(tp):
+        node = tb.tbik_gemm_shard(A[:, t * ks:(t + 1) * ks].contiguous(),
+                                  W[:, t * ks:(t + 1) * ks].contiguous(), K, tp)
+        assert np.array_equal(f32_bits_t(ws[t]), f32_bits_t(node)), t
+    ref = f32_bits_t(tb.tbik_gemm(A, W)[0])
+    assert np.array_equal(f32_bits_t(tb.tbik_tree_combine(ws)), ref)
+
+
 # ------------------------------------------------------------------ unaligned strides
 def test_rowops_unaligned_strides(orc):
     rows, H = 6, 4096

@@ -39,6 +39,12 @@
 #define TBIK_SMALL_PF 2
 #endif
 
+// Workgroups at or above which the wide ring kernel pairs parts (one per
+// CU fills the chip)
+#ifndef TBIK_RING_PPW_MIN_WG
+#define TBIK_RING_PPW_MIN_WG 256
+#endif
+
 // Narrow ring geometry: RING_WM x RING_WN 16x16 blocks per wave, 4 waves
 // stacked along M, RING_S stages.
 #ifndef TBIK_RING_WM
@@ -538,8 +544,13 @@ struct Ring {
 // plus a static tail.  GS == 0: runtime G, blocks of U leaves
 // pushed through a binary-counter stack of depth GD.  TD: stack depth over
 // the groups of one part.
+//
+// PPW: consecutive parts (K ranges) per workgroup.  With PPW > 1 a workgroup
+// streams its parts' leaves through one continuous ring and writes each
+// part's node to that part's slot as soon as the part is done, so the next
+// part's first stages are already in flight; each part's tree is unchanged.
 template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
-          int TD, int MINB>
+          int TD, int MINB, int PPW = 1>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, MINB)
 k_gemm_ring(GemmArgs p, TileMap tm) {
   // The body uses buffer-resource builtins that only exist for the device;
@@ -553,11 +564,11 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   __shared__ u32x4 ring[S * RG::SLOT];
 
   // ---- tile of this workgroup
-  const int nblocks = tm.tiles_m * tm.tiles_n * tm.parts;
+  const int nblocks = tm.tiles_m * tm.tiles_n * (tm.parts / PPW);
   int id = xcd_logical(blockIdx.x, nblocks);
   const int per_part = tm.tiles_m * tm.tiles_n;
-  const int part = id / per_part;
-  id -= part * per_part;
+  const int part0 = (id / per_part) * PPW;          // first of this workgroup's parts
+  id -= (id / per_part) * per_part;
   const int span = tm.group_m * tm.tiles_n;
   const int grp = id / span;
   const int first_m = grp * tm.group_m;
@@ -574,8 +585,8 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   const int wm = wave / WAVES_N, wn = wave - (wave / WAVES_N) * WAVES_N;
   const int G = GS > 0 ? GS : p.G;
   const int gpp = p.gpp;
-  rg.nleaf = gpp * G;
-  rg.kbase = (int64_t)part * gpp * G * 64;
+  rg.nleaf = PPW * gpp * G;
+  rg.kbase = (int64_t)part0 * gpp * G * 64;
   rg.l = 0;
 
   // ---- buffer resources over this tile's rows (rows past the end are
@@ -609,8 +620,12 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
 
   rg.prologue();
 
-  float top[TD > 0 ? TD : 1][R];
   float node[R];
+  const int orow = 4 * (lane >> 4);
+#pragma unroll
+  for (int pi = 0; pi < PPW; ++pi) {
+  const int part = part0 + pi;
+  float top[TD > 0 ? TD : 1][R];
   const int ngroups = gpp;
   for (int gi = 0; gi < ngroups; ++gi) {
     if constexpr (GS > 0 && U == 0) {
@@ -648,11 +663,10 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
     }
     pair_push<R, TD>(top, node, gi, gpp);
   }
-  wait_vmcnt<0>();     // no load into LDS may outlive the workgroup
+  if (pi == PPW - 1) wait_vmcnt<0>();     // no load into LDS may outlive the workgroup
 
   float *Cp = p.C ? p.C + (int64_t)part * p.part_stride : nullptr;
   uint16_t *Cbp = p.Cb;
-  const int orow = 4 * (lane >> 4);
 #pragma unroll
   for (int bm = 0; bm < WM; ++bm) {
 #pragma unroll
@@ -669,6 +683,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
         }
       }
     }
+  }
   }
   if constexpr (WN == 4) {
     // Exact row maxima of this wave's 64 columns (max is order-free): the
@@ -897,17 +912,18 @@ static int launch_big(const GemmArgs &a, int batch, hipStream_t s) {
 }
 
 template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
-          int TD, int MINB = 1>
+          int TD, int MINB = 1, int PPW = 1>
 static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
+  if (a.parts % PPW != 0 || (PPW > 1 && a.pmax != nullptr)) return TBIK_ERR_ARG;
   TileMap tm;
   tm.tiles_m = (a.M + MT - 1) / MT;
   tm.tiles_n = (a.N + NT - 1) / NT;
   tm.parts = a.parts;
   tm.group_m = 8;
-  const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * tm.parts;
+  const int64_t nb = (int64_t)tm.tiles_m * tm.tiles_n * (tm.parts / PPW);
   if (nb > 0x7fffffff) return TBIK_ERR_SHAPE;
-  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE, GS, U, GD, TD, MINB>),
+  hipLaunchKernelGGL((k_gemm_ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE, GS, U, GD, TD, MINB, PPW>),
                      dim3((unsigned)nb), dim3(64 * WAVES_M * WAVES_N), 0, s, a, tm);
   return check_launch();
 }
@@ -937,7 +953,12 @@ static int launch_wide(const GemmArgs &a, hipStream_t s) {
     if (a.gpp == 1) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1>(a, s);
     return TBIK_ERR_ARG;
   } else if constexpr (GS == 28) {
-    // at most 4 groups per part (8 would spill the group stack)
+    // at most 4 groups per part (8 would spill the group stack).  One group
+    // per part (the tp = 8 shards of a 224-leaf K): two parts per workgroup
+    // while that still gives every CU a workgroup.
+    if (a.gpp == 1 && a.parts % 2 == 0 && a.pmax == nullptr &&
+        (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * (a.parts / 2) >= TBIK_RING_PPW_MIN_WG)
+      return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 0, 0, 1, 1, 2>(a, s);
     switch (a.gpp) {
       case 1:
       case 2: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 0, 0, 1, 1>(a, s);
