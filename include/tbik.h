@@ -113,8 +113,9 @@ int tbik_tree_groups(int64_t n);
  *          computed by separate workgroups into ws and combined by the top
  *          of the tree (the same bits as without: the split is at tree
  *          nodes; TBIK summary page, "technical framework").  Worth it when
- *          M x N has too few tiles to occupy the GPU.  The contents of ws
- *          are unspecified afterwards.
+ *          M x N has too few tiles to occupy the GPU, and for M <= 32 at
+ *          K = 14336, where each of the 8 parts reads only its own K slice
+ *          of A.  The contents of ws are unspecified afterwards.
  * ---------------------------------------------------------------------- */
 size_t tbik_gemm_workspace_bytes(int M, int N, int K);
 

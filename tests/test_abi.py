@@ -142,6 +142,18 @@ def test_gemm_tpsim_validation(L):
              None) == E_WS
 
 
+def test_gemm_workspace_split_policy(L):
+    """K = 14336 (8 groups of 28 leaves): small M splits K into its 8 groups
+    (thin tiles read only their group's K slice of A); M = 256 into the
+    fewest parts that give every CU a 128 x 128 tile; scalar leaves, batched
+    calls and K without 28-leaf groups never split."""
+    ws = L.tbik_gemm_workspace_bytes
+    for M in (1, 16, 17, 32):
+        assert ws(M, 4096, 14336) == 8 * M * 4096 * 4, M
+    assert ws(256, 4096, 14336) == 4 * 256 * 4096 * 4
+    assert ws(32, 4096, 4096) == 0
+
+
 def test_combine_validation(L):
     assert L.tbik_tree_combine(None, 2, FAKE, 8, None, 1, 8, None) == E_NULL
     assert L.tbik_tree_combine(FAKE, 3, FAKE2, 8, None, 1, 8, None) == E_TP

@@ -177,7 +177,8 @@ def test_gemm_mfma_tp_invariant(M, N, K, tps):
 
 
 @pytest.mark.parametrize("M,N,K", [(33, 4096, 14336), (256, 4096, 14336), (100, 2048, 2048),
-                                   (77, 300, 5632), (130, 520, 4096)])
+                                   (77, 300, 5632), (130, 520, 4096), (32, 4096, 14336),
+                                   (17, 1000, 14336), (16, 4096, 14336), (1, 4000, 14336)])
 def test_gemm_split_k_workspace_same_bits(M, N, K):
     """tbik_gemm with its split-K workspace (nodes of the tree computed by
     separate workgroups, then the top of the tree) equals the one-launch

@@ -45,6 +45,17 @@
 #define TBIK_RING_PPW_MIN_WG 256
 #endif
 
+// 32-row ring tiles for 16 < M <= 32 (1 = on)
+#ifndef TBIK_THIN
+#define TBIK_THIN 1
+#endif
+#ifndef TBIK_THIN_MINB
+#define TBIK_THIN_MINB 2
+#endif
+#ifndef TBIK_THIN_MIN_M
+#define TBIK_THIN_MIN_M 0
+#endif
+
 // Narrow ring geometry: RING_WM x RING_WN 16x16 blocks per wave, 4 waves
 // stacked along M, RING_S stages.
 #ifndef TBIK_RING_WM
@@ -558,8 +569,6 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
 #if defined(__HIP_DEVICE_COMPILE__)
   using RG = Ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE>;
   constexpr int MT = RG::MT, NT = RG::NT, R = RG::R, WAVES = RG::WAVES;
-  static_assert(WN == 4 || (WN == 2 && WAVES_N == 4),
-                "the row-maximum epilogue covers these wave tiles only");
   constexpr int DPW = RG::DPW, DPA = RG::DPA, SEGA = RG::SEGA;
   __shared__ u32x4 ring[S * RG::SLOT];
 
@@ -916,6 +925,9 @@ template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, in
 static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
   if (a.parts % PPW != 0 || (PPW > 1 && a.pmax != nullptr)) return TBIK_ERR_ARG;
+  // the fused row maxima exist for 64-column waves and for 32-column waves
+  // four to a tile row only
+  if (a.pmax != nullptr && !(WN == 4 || (WN == 2 && WAVES_N == 4))) return TBIK_ERR_ARG;
   TileMap tm;
   tm.tiles_m = (a.M + MT - 1) / MT;
   tm.tiles_n = (a.N + NT - 1) / NT;
@@ -974,6 +986,22 @@ static int launch_wide(const GemmArgs &a, hipStream_t s) {
     }
     return TBIK_ERR_ARG;
   }
+}
+
+// "Thin" tiles for M <= 32: 32 x 64 (4 waves of 32 x 16) or, for M <= 16,
+// 16 x 64 (2 waves of 16 x 32), on the LDS ring.  With one or two 28-leaf
+// groups per part (K split at tree nodes into 4 or 8 parts) a workgroup
+// reads only its part's K slice of A, where a small-M kernel over the whole
+// K reads all of A once per 16-column block -- at M = 32 twice the bytes of
+// W.
+#ifndef TBIK_THIN_WN
+#define TBIK_THIN_WN 1
+#endif
+static int launch_thin28(const GemmArgs &a, hipStream_t s) {
+  if (a.gpp > 2) return TBIK_ERR_ARG;
+  if (a.M <= 16)
+    return launch_ring_cfg<1, 2, 1, 2, 4, 2, false, 28, 0, 0, 1, TBIK_THIN_MINB>(a, s);
+  return launch_ring_cfg<2, TBIK_THIN_WN, 1, 4, 4, 2, false, 28, 0, 0, 1, TBIK_THIN_MINB>(a, s);
 }
 
 template <int GS, int U, int GD>
@@ -1057,9 +1085,10 @@ static int launch_small(const GemmArgs &a, int batch, hipStream_t s) {
 // gives the ring kernel about one 128 x 64 workgroup per CU.  1 = no split
 // (small M, batched, scalar leaves, or enough tiles).
 int gemm_split_parts(int M, int N, int K, int batch, int leaf_mode) {
-  if (leaf_mode != TBIK_LEAF_MFMA || batch != 1 || M <= 32 || N <= 0 || K <= 0) return 1;
+  if (leaf_mode != TBIK_LEAF_MFMA || batch != 1 || M <= TBIK_THIN_MIN_M || N <= 0 || K <= 0) return 1;
   const int nb = K / 64;
   const int T = tree_T(nb);
+  if (M <= 32) return (TBIK_THIN && T == 8 && nb / T == 28) ? 8 : 1;   // thin tiles, one group per part
   if (!ring_supported_g(nb / T)) return 1;
   if (nb / T == 28 && T == 8) {
     const int64_t wide = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
@@ -1112,6 +1141,9 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
     return check_launch();
   }
   const int need = bit_length(a.G - 1);
+  if (TBIK_THIN && c.M > TBIK_THIN_MIN_M && c.M <= 32 && c.batch == 1 && a.G == 28 && a.gpp <= 2 &&
+      (int64_t)32 * c.lda * 2 < ((int64_t)1 << 31) && (int64_t)128 * c.ldw * 2 < ((int64_t)1 << 31))
+    return launch_thin28(a, s);
   if (c.M > 32 && c.batch == 1 && ring_supported_g(a.G) &&
       (int64_t)128 * c.lda * 2 < ((int64_t)1 << 31) && (int64_t)128 * c.ldw * 2 < ((int64_t)1 << 31))
     return launch_ring(a, s);
