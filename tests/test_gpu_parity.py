@@ -421,6 +421,38 @@ def test_logsoftmax_bitexact(orc, M, V, tps):
         assert same_bits(got_nodes, nodes), tp
 
 
+@pytest.mark.parametrize("V", [32000, 1000])
+def test_logsoftmax_special_values(orc, V):
+    """Masked vocabulary (-inf), a +inf logit, a NaN logit, targets on masked
+    entries: the same NaN pattern as the oracle and the same bits elsewhere
+    (V = 32000 takes the 16-element chunk path, V = 1000 single elements)."""
+    M = 6
+    rng = np.random.default_rng(V + 1)
+    logits = (rng.standard_normal((M, V)) * 3).astype(np.float32)
+    logits[0, ::3] = -np.inf                  # a third of the vocabulary masked
+    logits[1, 5] = np.inf
+    logits[2, V // 2] = np.nan
+    logits[3, :] = -np.inf
+    logits[3, 7] = 1.0
+    logits[4, -1] = 80.0                      # far above the rest of its row
+    tgt = rng.integers(0, V, M).astype(np.int32)
+    tgt[0] = 3                                # a masked entry: log-probability -inf
+    tgt[3] = 7
+    dev = torch.from_numpy(logits).to(DEV)
+    for tp in (1, 4):
+        say("logsoftmax special values", V, tp)
+        lp, ws = tb.tbik_logsoftmax_gather(dev, torch.from_numpy(tgt).to(DEV), tp)
+        ref, nodes = orc.logsoftmax_gather(logits, tgt, tp)
+        got = lp.cpu().numpy()
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), tp
+        ok = ~np.isnan(ref)
+        assert same_bits(got[ok], ref[ok]), tp
+        gn = tb.logsoftmax_shard_nodes(ws, M, tp).cpu().numpy()
+        okn = ~np.isnan(nodes)
+        assert np.array_equal(np.isnan(gn), np.isnan(nodes)), tp
+        assert same_bits(gn[okn], nodes[okn]), tp
+
+
 # ------------------------------------------------------------------ causal softmax
 @pytest.mark.parametrize("B,Lq,Lk,offset", [(2, 512, 512, 0), (3, 64, 128, 64), (1, 9, 24, 0),
                                             (2, 130, 256, 0), (2, 64, 64, 0), (1, 512, 1024, 512)])

@@ -522,6 +522,17 @@ int launch_swiglu(const uint16_t *g, const uint16_t *u, uint16_t *o, int rows, i
 #define TBIK_LSM_LDS_MIN 0
 #endif
 constexpr int kLsmThreads = TBIK_LSM_THREADS;
+// 16-element chunks read by lane quads (1 = on), with non-temporal loads
+// (NT; a plus only with whole-line accesses) and KB loads in flight per lane
+#ifndef TBIK_LSM_QUAD
+#define TBIK_LSM_QUAD 1
+#endif
+#ifndef TBIK_LSM_NT
+#define TBIK_LSM_NT 1
+#endif
+#ifndef TBIK_LSM_KB
+#define TBIK_LSM_KB 8
+#endif
 
 // PAIR over `groups` groups of m values each, group g at buf[g*m ..): the
 // group's PAIR value is left at buf[g*m].  All threads of the block call it.
@@ -559,6 +570,12 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
     // produced the logits): the logits are then read once
     for (int b = threadIdx.x; b < npmax; b += kLsmThreads)
       m = __builtin_fmaxf(m, pmax[(int64_t)row * ld_pmax + b]);
+  } else if constexpr (CH >= 4) {
+    // the maximum is order-free: consecutive lanes read consecutive 16 bytes
+    for (int i = threadIdx.x; i < nch * (CH / 4); i += kLsmThreads) {
+      const f32x4 u = *reinterpret_cast<const f32x4 *>(xr + 4 * i);
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), __builtin_fmaxf(u[2], u[3])));
+    }
   } else {
     for (int ch = threadIdx.x; ch < nch; ch += kLsmThreads) {
       float v[CH];
@@ -574,12 +591,50 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   m = red[0];
 #pragma unroll
   for (int q = 1; q < kLsmThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
-  for (int ch = nch - 1 - (int)threadIdx.x; ch >= 0; ch -= kLsmThreads) {
-    float v[CH];
-    load_f32<CH>(v, xr + ch * CH);
+  if constexpr (CH == 16 && TBIK_LSM_QUAD) {
+    // A chunk is read by a quad of lanes, lane j of the quad holding its
+    // elements 4j..4j+3, so every load instruction of a wave covers 1 KB
+    // contiguously.  Each lane reduces its four values (the chunk tree's
+    // level of 4), and two quad-permute adds finish the chunk's perfect
+    // tree: (q0 + q1) + (q2 + q3) -- addition is commutative, so every lane
+    // of the quad ends with the same bits.  Blocks of 16*KB chunks per wave,
+    // walked from the row's end, with non-temporal loads (the row is read
+    // once here when its maximum comes from the GEMM).
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int qd = lane >> 2, j = lane & 3;
+    constexpr int NWV = kLsmThreads / 64;
+    constexpr int KB = TBIK_LSM_KB;                       // 16-chunk loads per block
+    const int nblk = (nch + 16 * KB - 1) / (16 * KB);
+    for (int b = nblk - 1 - wave; b >= 0; b -= NWV) {
+      f32x4 u[KB];
+      int c[KB];
 #pragma unroll
-    for (int e = 0; e < CH; ++e) v[e] = exp_f32(v[e] - m);
-    lds[ch] = chunk_tree<CH>(v);
+      for (int k = 0; k < KB; ++k) {
+        c[k] = b * 16 * KB + 16 * k + qd;
+        const int cc = c[k] < nch ? c[k] : nch - 1;      // ragged last block: a valid address
+        u[k] = vload<TBIK_LSM_NT != 0>(reinterpret_cast<const f32x4 *>(xr + cc * 16 + 4 * j));
+      }
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        float e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = exp_f32(u[k][i] - m);
+        float t = (e[0] + e[1]) + (e[2] + e[3]);
+        t = t + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                    0, __builtin_bit_cast(int, t), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+        t = t + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                    0, __builtin_bit_cast(int, t), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+        if (j == 0 && c[k] < nch) lds[c[k]] = t;
+      }
+    }
+  } else {
+    for (int ch = nch - 1 - (int)threadIdx.x; ch >= 0; ch -= kLsmThreads) {
+      float v[CH];
+      load_f32<CH>(v, xr + ch * CH);
+#pragma unroll
+      for (int e = 0; e < CH; ++e) v[e] = exp_f32(v[e] - m);
+      lds[ch] = chunk_tree<CH>(v);
+    }
   }
   __syncthreads();
   lds_pair_inplace<kLsmThreads>(lds, gc, T);

@@ -46,8 +46,11 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 // x = k ln2 + r, k = rint(x log2 e); r via two fma with ln2 split into
 // hi (ln2 rounded to a multiple of 2^-16, so k*hi is exact for |k| < 2^8)
 // and lo; e^r by the degree-7 Taylor polynomial (coefficients 1/n! rounded
-// to fp32) in Horner form with fma; 2^k applied as two power-of-two
-// multiplies so that a subnormal result is rounded once.
+// to fp32) in Horner form with fma; 2^k applied with one rounding.  The
+// definition applies 2^k as two power-of-two multiplies (2^floor(k/2), then
+// 2^(k - floor(k/2))), whose first product is exact; v_ldexp_f32 rounds
+// p * 2^k once as well, and the two agree bit for bit on every fp32 input
+// (checked exhaustively on the GPU), in one instruction instead of six.
 //
 // EXP's special cases (x > 89 -> +inf, x < -104 -> +0) need no branch or
 // select: with x clamped to [-104.5, 89.5] the main path itself overflows
@@ -72,11 +75,7 @@ __device__ __forceinline__ float exp_core(float x) {
   p = __builtin_fmaf(p, r, 0.5f);
   p = __builtin_fmaf(p, r, 1.0f);
   p = __builtin_fmaf(p, r, 1.0f);
-  const int k1 = k >> 1;
-  const int k2 = k - k1;
-  const float s1 = __uint_as_float((uint32_t)(k1 + 127) << 23);
-  const float s2 = __uint_as_float((uint32_t)(k2 + 127) << 23);
-  return (p * s1) * s2;
+  return __builtin_ldexpf(p, k);
 }
 
 // EXP of any fp32 x; a NaN is returned quieted (x + x).
