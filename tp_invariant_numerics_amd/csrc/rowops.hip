@@ -278,6 +278,74 @@ k_rmsnorm_reg(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t 
   }
 }
 
+// Rows of H = 2048 * U elements (U = 1, 2: groups of at most 32 chunks) in
+// 16-element chunks: a chunk is read by two
+// adjacent lanes (8 elements, 16 bytes each), so every load and store
+// instruction of a wave covers 1 KB contiguously (non-temporal accesses
+// measured slower here: TBIK_RMS_NT).  A lane reduces its half chunk (the chunk
+// tree's level of 8), one lane-swap add finishes the chunk's perfect tree
+// (the two lanes get the same bits: addition is commutative), and a
+// butterfly over lane offsets 2, 4, .., gc evaluates each group's PAIR -- a
+// perfect tree, gc being a power of two -- every lane of the group ending
+// with the same bits.  Then as k_rmsnorm_reg.
+#ifndef TBIK_RMS_PAIR
+#define TBIK_RMS_PAIR 1
+#endif
+#ifndef TBIK_RMS_NT
+#define TBIK_RMS_NT 0
+#endif
+template <int U, bool EACH>
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm_pair(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y,
+               uint16_t *r_out, int H, int64_t ld, float eps, int T, int gc) {
+  constexpr bool NT = TBIK_RMS_NT != 0;
+  __shared__ float gsum[8];
+  const int t = threadIdx.x, lane = t & 63;
+  const int64_t rowoff = (int64_t)blockIdx.x * ld;
+  float h[U][8], ww[U][8];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int unit = k * kRowThreads + t;          // elements 8*unit .. 8*unit+7
+    float b[8], sq[8];
+    load_bf16<8, NT>(h[k], x + rowoff + 8 * unit);
+    load_bf16<8, NT>(b, r + rowoff + 8 * unit);
+    load_bf16<8>(ww[k], w + 8 * unit);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h[k][e] = h[k][e] + b[e];
+      if (EACH) h[k][e] = bf_round(h[k][e]);
+      sq[e] = h[k][e] * h[k][e];
+    }
+    if (r_out) store_bf16<8, NT>(r_out + rowoff + 8 * unit, h[k]);
+    float part = chunk_tree<8>(sq);
+    part = part + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                      0, __builtin_bit_cast(int, part), 0xB1, 0xf, 0xf, false));
+    for (int o = 1; o < gc; o <<= 1) part = part + __shfl_xor(part, 2 * o);
+    if ((lane & (2 * gc - 1)) == 0) gsum[(unit >> 1) / gc] = part;
+  }
+  __syncthreads();
+  float g[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) g[q] = q < T ? gsum[q] : 0.0f;
+  for (int wdt = T; wdt > 1; wdt >>= 1)
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (q < wdt / 2) g[q] = g[2 * q] + g[2 * q + 1];
+  const float mean = g[0] / (float)H;
+  const float rstd = 1.0f / __builtin_sqrtf(mean + eps);
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const int unit = k * kRowThreads + t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float n = h[k][e] * rstd;
+      if (EACH) n = bf_round(n);
+      h[k][e] = n * ww[k][e];
+    }
+    store_bf16<8, NT>(y + rowoff + 8 * unit, h[k]);
+  }
+}
+
 template <bool EACH>
 static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t *w,
                             uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
@@ -293,6 +361,14 @@ static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t
   if (nch > 8192) return TBIK_ERR_SHAPE;
   const int gc = nch / T;
   dim3 grid((unsigned)rows), block(kRowThreads);
+  if (TBIK_RMS_PAIR && ch == 16 && H % (8 * kRowThreads) == 0 && (gc & (gc - 1)) == 0 &&
+      gc <= 32) {
+    switch (H / (8 * kRowThreads)) {
+      case 1: hipLaunchKernelGGL((k_rmsnorm_pair<1, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); return check_launch();
+      case 2: hipLaunchKernelGGL((k_rmsnorm_pair<2, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); return check_launch();
+      default: break;
+    }
+  }
   if (nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
     switch (ch) {
       case 16: hipLaunchKernelGGL((k_rmsnorm_reg<16, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
