@@ -107,7 +107,7 @@ def test_gemm_wgrad_integer_exact():
     assert np.array_equal(dW.cpu().numpy().astype(np.float64), exact)
 
 
-@pytest.mark.parametrize("T,heads,d", [(2048, 16, 128), (33, 3, 64)])
+@pytest.mark.parametrize("T,heads,d", [(2048, 16, 128), (33, 3, 64), (17, 6, 32)])
 def test_rope_backward_bitexact(orc, T, heads, d):
     dy = inputs.normal_bf16((T, heads, d), 10600 + T)
     pos = inputs.positions(T, 32768, seed=13)

@@ -398,6 +398,9 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
              : launch_rmsnorm_t<false>(x, r, w, y, r_out, rows, H, ld, eps, s);
 }
 
+#ifndef TBIK_ROPE_HPT
+#define TBIK_ROPE_HPT 2
+#endif
 // =============================================================================
 // RoPE (rotate-half).  One thread = 4 consecutive pairs (i..i+3, i+h..i+h+3);
 // grid.x covers the (head, pair-quad) items of one token, grid.y the tokens.
@@ -406,22 +409,24 @@ int launch_rmsnorm_residual(const uint16_t *x, const uint16_t *r, const uint16_t
 // difference and the sum (rotate_half arithmetic on bf16 tensors).
 // INV: the rotation by -angle, the adjoint used by the backward pass:
 // y[i] = x[i]*c + x[i+h]*s, y[i+h] = x[i+h]*c - x[i]*s.
-template <bool EACH, bool INV = false>
+// HPT: heads per thread.  With HPT > 1 a thread rotates the same 4 pairs of
+// HPT heads (heads hg, hg + heads/HPT, ...), so one load of the token's
+// table entries serves all of them; the lanes of one instruction still read
+// whole 128-byte half rows.
+template <bool EACH, bool INV = false, int HPT = 1>
 __global__ void __launch_bounds__(256)
 k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
        const float *sin_tab, int T, int heads, int half, int64_t ld_token, int max_pos,
        int q4_shift) {
   const int q4 = half / 4;                       // 4-pair items per head
+  const int hstride = heads / HPT;
   const int item = blockIdx.x * blockDim.x + threadIdx.x;
-  if (item >= heads * q4) return;
-  const int hd = q4_shift >= 0 ? item >> q4_shift : item / q4;
-  const int i = (item - hd * q4) * 4;
+  if (item >= hstride * q4) return;
+  const int hd0 = q4_shift >= 0 ? item >> q4_shift : item / q4;
+  const int i = (item - hd0 * q4) * 4;
   for (int t = blockIdx.y; t < T; t += gridDim.y) {
     int p = pos[t];
     p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
-    const int64_t off = (int64_t)t * ld_token + (int64_t)hd * 2 * half + i;
-    const u32x2 ua = vload<true>(reinterpret_cast<const u32x2 *>(x + off));
-    const u32x2 ub = vload<true>(reinterpret_cast<const u32x2 *>(x + off + half));
     f32x4 c = *reinterpret_cast<const f32x4 *>(cos_tab + (int64_t)p * half + i);
     f32x4 sn = *reinterpret_cast<const f32x4 *>(sin_tab + (int64_t)p * half + i);
     if constexpr (EACH) {
@@ -431,10 +436,20 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
         sn[e] = bf_round(sn[e]);
       }
     }
-    const float a[4] = {__uint_as_float(ua[0] << 16), __uint_as_float(ua[0] & 0xffff0000u),
-                        __uint_as_float(ua[1] << 16), __uint_as_float(ua[1] & 0xffff0000u)};
-    const float b[4] = {__uint_as_float(ub[0] << 16), __uint_as_float(ub[0] & 0xffff0000u),
-                        __uint_as_float(ub[1] << 16), __uint_as_float(ub[1] & 0xffff0000u)};
+    u32x2 ua[HPT], ub[HPT];
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+      const int64_t off = (int64_t)t * ld_token + (int64_t)(hd0 + k * hstride) * 2 * half + i;
+      ua[k] = vload<true>(reinterpret_cast<const u32x2 *>(x + off));
+      ub[k] = vload<true>(reinterpret_cast<const u32x2 *>(x + off + half));
+    }
+#pragma unroll
+    for (int k = 0; k < HPT; ++k) {
+    const int64_t off = (int64_t)t * ld_token + (int64_t)(hd0 + k * hstride) * 2 * half + i;
+    const float a[4] = {__uint_as_float(ua[k][0] << 16), __uint_as_float(ua[k][0] & 0xffff0000u),
+                        __uint_as_float(ua[k][1] << 16), __uint_as_float(ua[k][1] & 0xffff0000u)};
+    const float b[4] = {__uint_as_float(ub[k][0] << 16), __uint_as_float(ub[k][0] & 0xffff0000u),
+                        __uint_as_float(ub[k][1] << 16), __uint_as_float(ub[k][1] & 0xffff0000u)};
     float ya[4], yb[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -456,6 +471,7 @@ k_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float *cos_tab,
     ob[1] = pack_bf16(yb[2], yb[3]);
     vstore<true>(reinterpret_cast<u32x2 *>(y + off), oa);
     vstore<true>(reinterpret_cast<u32x2 *>(y + off + half), ob);
+    }
   }
 }
 
@@ -465,12 +481,27 @@ int launch_rope(const uint16_t *x, uint16_t *y, const int32_t *pos, const float 
   if (T == 0) return TBIK_OK;
   const int half = head_dim / 2;
   const int q4 = half / 4;
-  const int items = heads * q4;
   int q4_shift = -1;
   for (int b = 0; b < 31; ++b)
     if ((1 << b) == q4) q4_shift = b;
-  const unsigned gx = (unsigned)((items + 255) / 256);
   const unsigned gy = (unsigned)(T < 65535 ? T : 65535);
+  if (TBIK_ROPE_HPT > 1 && heads % TBIK_ROPE_HPT == 0) {
+    const int ipt = heads / TBIK_ROPE_HPT * q4;          // items per token
+    const int bs = ipt >= 256 ? 256 : (ipt + 63) / 64 * 64;
+    const unsigned gx = (unsigned)((ipt + bs - 1) / bs);
+    if (rounding == kRopeInverse)
+      hipLaunchKernelGGL((k_rope<false, true, TBIK_ROPE_HPT>), dim3(gx, gy), dim3(bs), 0, s, x, y,
+                         pos, cos_tab, sin_tab, T, heads, half, ld_token, max_pos, q4_shift);
+    else if (rounding == TBIK_ROUND_EACH_OP)
+      hipLaunchKernelGGL((k_rope<true, false, TBIK_ROPE_HPT>), dim3(gx, gy), dim3(bs), 0, s, x, y,
+                         pos, cos_tab, sin_tab, T, heads, half, ld_token, max_pos, q4_shift);
+    else
+      hipLaunchKernelGGL((k_rope<false, false, TBIK_ROPE_HPT>), dim3(gx, gy), dim3(bs), 0, s, x, y,
+                         pos, cos_tab, sin_tab, T, heads, half, ld_token, max_pos, q4_shift);
+    return check_launch();
+  }
+  const int items = heads * q4;
+  const unsigned gx = (unsigned)((items + 255) / 256);
   if (rounding == kRopeInverse)
     hipLaunchKernelGGL((k_rope<false, true>), dim3(gx, gy), dim3(256), 0, s, x, y, pos, cos_tab,
                        sin_tab, T, heads, half, ld_token, max_pos, q4_shift);
