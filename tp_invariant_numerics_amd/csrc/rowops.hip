@@ -1257,9 +1257,22 @@ k_colsum_tree(const float *leaves, int nleaf, int H, int T, int dp, float *shard
   if (col < H) {
     float st[20][1];
     float node[1] = {0.0f};
-    for (int i = 0; i < G; ++i) {
-      node[0] = leaves[(int64_t)(q * G + i) * H + col];
-      pair_push<1, 20>(st, node, i, G);
+    // the leaves are requested 8 at a time (independent loads in flight),
+    // then pushed in order
+    for (int i0 = 0; i0 < G; i0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = i0 + k < G ? i0 + k : G - 1;
+        v[k] = leaves[(int64_t)(q * G + i) * H + col];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (i0 + k < G) {
+          node[0] = v[k];
+          pair_push<1, 20>(st, node, i0 + k, G);
+        }
+      }
     }
     gs[q][threadIdx.x] = node[0];
   }
