@@ -736,7 +736,10 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
     // two halves of each 64-column block are combined.
     if (p.pmax) {
       float *pm = reinterpret_cast<float *>(ring);    // [MT rows][WAVES_N]
-      __syncthreads();
+      // LDS-only barriers: every wave has drained its loads into the ring
+      // (vmcnt 0 above); a full __syncthreads would also wait for the C
+      // stores just issued
+      ring_barrier();
 #pragma unroll
       for (int bm = 0; bm < WM; ++bm) {
 #pragma unroll
@@ -762,7 +765,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
           if ((lane & 15) == 15) pm[(wm * 16 * WM + 16 * bm + orow + i) * WAVES_N + wn] = mx;
         }
       }
-      __syncthreads();
+      ring_barrier();
       for (int e = threadIdx.x; e < MT * (WAVES_N / 2); e += 64 * WAVES) {
         const int r = e / (WAVES_N / 2), b = e - r * (WAVES_N / 2);
         const int row = m0 + r, c0 = n0 + 64 * b;
