@@ -85,8 +85,11 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
   __shared__ u32x4 pl[4][16 * PC];
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
-  const int xb = gridDim.x - 1 - blockIdx.x;   // longest row blocks first
-  const int h = blockIdx.y % heads, b = blockIdx.y / heads;
+  // grid (sequence x head, row block): every (sequence, head)'s longest row
+  // block is dispatched before any shorter one -- longest first packs the
+  // causal triangle's unequal workgroups (8:1 at 512 keys) onto the CUs
+  const int xb = gridDim.y - 1 - blockIdx.y;
+  const int h = blockIdx.x % heads, b = blockIdx.x / heads;
   const int r0 = xb * 64 + wave * 16;          // first query row of this wave
   const int nkc = xb + 1;                      // chunks holding a visible key
   const int64_t tok0 = (int64_t)b * LK;
@@ -276,7 +279,7 @@ k_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk, co
 int launch_attn_causal(const uint16_t *Q, int64_t ldq, const uint16_t *K, int64_t ldk,
                        const uint16_t *Vt, int64_t ldvt, uint16_t *O, int64_t ldo, int L, int heads,
                        int batch, float scale, hipStream_t s) {
-  const dim3 grid((unsigned)(L / 64), (unsigned)(heads * batch)), block(256);
+  const dim3 grid((unsigned)(heads * batch), (unsigned)(L / 64)), block(256);
   switch (L) {
     case 64: hipLaunchKernelGGL(k_attn_causal<64>, grid, block, 0, s, Q, ldq, K, ldk, Vt, ldvt, O, ldo, heads, scale); break;
     case 128: hipLaunchKernelGGL(k_attn_causal<128>, grid, block, 0, s, Q, ldq, K, ldk, Vt, ldvt, O, ldo, heads, scale); break;
