@@ -562,6 +562,27 @@ def test_gemm_whole_part_perfect_tree(orc, M, K, N):
     assert np.array_equal(Ci, exact)
 
 
+@pytest.mark.parametrize("M", [1, 32, 256])
+def test_downproj_full_size_sampled_accuracy(orc, M):
+    """The row-parallel down projection at its full size (K = 14336,
+    N = 4096) in the launch configurations the benchmark times: tp = 8
+    simulated shards (paired shards per workgroup at M = 256, thin tiles at
+    M <= 32) and tp = 1 with the split-K workspace.  Both give the same bits;
+    sampled outputs are within 1e-5 normwise of the binary64 product."""
+    K, N = 14336, 4096
+    A = inputs.normal_bf16((M, K), 7400 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 7401, std=0.02, device=DEV)
+    say("down projection full size", M)
+    C8 = f32_bits_t(tb.tbik_gemm_tpsim(A, W, 8)[0])
+    C1 = f32_bits_t(tb.tbik_gemm(A, W)[0])
+    assert np.array_equal(C8, C1)
+    rows = np.arange(0, M, max(1, M // 8))
+    cols = np.arange(3, N, 61)
+    exact = orc.gemm_f64(bits(A[rows]), bits(W[cols]))
+    got = C1.view(np.float32)[np.ix_(rows, cols)].astype(np.float64)
+    assert np.abs(got - exact).max() / np.abs(exact).max() <= 1e-5
+
+
 @pytest.mark.parametrize("M,N", [(4096, 2048), (256, 2048), (40, 520)])
 def test_gemm_group11_schedule(orc, M, N):
     """K = 5632 (88 leaves, groups of 11, the decoder's down projection):
