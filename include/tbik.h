@@ -253,6 +253,25 @@ int tbik_swiglu_ex(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, i
                    void *stream);
 
 /* ------------------------------------------------------------------------
+ * Gate/up projection with the SwiGLU node fused into its epilogue: for the
+ * decoder's FFN ([TBIK] the invariant GEMM; [ROUND] "three nodes").
+ *   G = A W_g^T, U = A W_u^T      the tree GEMM (MFMA leaves), W_gu = [W_g; W_u]
+ *   H = SwiGLU(bf16(G), bf16(U))  as tbik_swiglu_ex with `rounding`
+ * H holds exactly what tbik_gemm (bf16 output over W_gu) followed by
+ * tbik_swiglu_ex on its two column halves returns, without writing G and U.
+ *  A     [M, K] bf16, row stride lda;  W_gu [2F, K] bf16, row stride ldw
+ *        (rows 0..F-1 the gate weights, F..2F-1 the up weights).
+ *  H     [M, F] bf16, row stride ldh >= F (2-byte aligned).
+ *  F     a positive multiple of 16.
+ * Supported where the LDS-ring GEMM kernel runs the whole tree: M > 32, K's
+ * groups of a size that kernel takes (K = 1024 .. 14336 in the decoder and
+ * benchmark shapes), 2F * ldw * 2 bytes < 2^31; otherwise TBIK_ERR_SHAPE and
+ * nothing is launched (compose tbik_gemm and tbik_swiglu_ex instead).
+ * ---------------------------------------------------------------------- */
+int tbik_gemm_swiglu(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W_gu, int64_t ldw,
+                     tbik_bf16 *H, int64_t ldh, int M, int F, int K, int rounding, void *stream);
+
+/* ------------------------------------------------------------------------
  * Log-softmax + target gather ([TBIK] reduction primitives; [ISO] 叁 logprob
  * comparison).  Per row i:
  *   m = max_j x_j (exact);  e_j = EXP(x_j - m);  s = TREE_j(e_j);

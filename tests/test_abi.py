@@ -154,6 +154,15 @@ def test_gemm_workspace_split_policy(L):
     assert ws(32, 4096, 4096) == 0
 
 
+def test_gemm_swiglu_validation(L):
+    g = L.tbik_gemm_swiglu
+    # F not a multiple of 16; H missing; M <= 32 (no fused kernel: nothing launched)
+    assert g(FAKE, 1024, FAKE2, 1024, FAKE3, 24, 64, 24, 1024, 0, None) == E_SHAPE
+    assert g(FAKE, 1024, FAKE2, 1024, None, 32, 64, 32, 1024, 0, None) == E_NULL
+    assert g(FAKE, 1024, FAKE2, 1024, FAKE3, 32, 32, 32, 1024, 0, None) == E_SHAPE
+    assert g(FAKE, 1024, FAKE2, 1024, FAKE3, 32, 64, 32, 1024, 7, None) == E_ARG
+
+
 def test_combine_validation(L):
     assert L.tbik_tree_combine(None, 2, FAKE, 8, None, 1, 8, None) == E_NULL
     assert L.tbik_tree_combine(FAKE, 3, FAKE2, 8, None, 1, 8, None) == E_TP

@@ -562,6 +562,21 @@ def test_gemm_whole_part_perfect_tree(orc, M, K, N):
     assert np.array_equal(Ci, exact)
 
 
+@pytest.mark.parametrize("M,F,K", [(4096, 5632, 2048), (100, 48, 2048), (257, 1040, 5632),
+                                   (33, 16, 1024), (300, 2000, 14336)])
+@pytest.mark.parametrize("rounding", ["once", "each_op"])
+def test_gemm_swiglu_fused_equals_composition(M, F, K, rounding):
+    """The gate/up GEMM with SwiGLU in its epilogue returns what the tree
+    GEMM's bf16 output followed by the SwiGLU node returns, bit for bit."""
+    A = inputs.normal_bf16((M, K), 7500 + M, device=DEV)
+    W = inputs.normal_bf16((2 * F, K), 7501 + F, std=0.05, device=DEV)
+    say("gemm+swiglu fused", M, F, K, rounding)
+    H = tb.tbik_gemm_swiglu(A, W, rounding=rounding)
+    _, gu = tb.tbik_gemm(A, W, want_fp32=False, want_bf16=True)
+    ref = tb.tbik_swiglu(gu[:, :F], gu[:, F:], rounding=rounding)
+    assert torch.equal(H.view(torch.int16), ref.view(torch.int16))
+
+
 @pytest.mark.parametrize("M", [1, 32, 256])
 def test_downproj_full_size_sampled_accuracy(orc, M):
     """The row-parallel down projection at its full size (K = 14336,

@@ -73,6 +73,7 @@ def _sigs():
         "tbik_rmsnorm_residual_ex": (i32, [p, p, p, p, p, i32, i32, i64, f32, i32, p]),
         "tbik_rope_ex": (i32, [p, p, p, p, p, i32, i32, i32, i64, i32, i32, p]),
         "tbik_swiglu_ex": (i32, [p, p, p, i32, i32, i64, i64, i64, i32, p]),
+        "tbik_gemm_swiglu": (i32, [p, i64, p, i64, p, i64, i32, i32, i32, i32, p]),
         "tbik_logsoftmax_workspace_bytes": (sz, [i32, i32, i32]),
         "tbik_logsoftmax_gather": (i32, [p, i64, p, p, i32, i32, i32, p, sz, p]),
         "tbik_softmax_causal": (i32, [p, i64, i64, p, i64, i64, i32, i32, i32, i32, f32, p]),
@@ -311,6 +312,23 @@ def tbik_rope_table(theta, head_dim, max_pos):
     rc = lib().tbik_rope_table(float(theta), head_dim, max_pos, _ptr(c), _ptr(s))
     _chk(rc, "tbik_rope_table")
     return c, s
+
+
+def tbik_gemm_swiglu(A, W_gu, out=None, rounding="once"):
+    """H = SwiGLU(bf16(A W_g^T), bf16(A W_u^T)) with W_gu = [W_g; W_u] [2F, K]:
+    the gate/up GEMM with the SwiGLU node in its epilogue.  Raises TbikError
+    (TBIK_ERR_SHAPE) for shapes the fused kernel does not take."""
+    _bits(A); _bits(W_gu); _need_gpu(A, W_gu)
+    M, K = A.shape
+    F = W_gu.shape[0] // 2
+    if W_gu.shape[1] != K or W_gu.shape[0] != 2 * F:
+        raise ValueError("W_gu must be [2F, K]")
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.bfloat16, device=A.device)
+    rc = lib().tbik_gemm_swiglu(_ptr(A), _ld(A), _ptr(W_gu), _ld(W_gu), _ptr(out), _ld(out),
+                                M, F, K, ROUNDING[rounding], _stream())
+    _chk(rc, "tbik_gemm_swiglu")
+    return out
 
 
 def tbik_swiglu(gate, up, out=None, rounding="once"):

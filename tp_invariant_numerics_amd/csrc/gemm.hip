@@ -103,6 +103,12 @@ struct GemmArgs {
   // Optional (ring kernel, parts == 1): per-row maxima of C over 64-column
   // blocks, pmax[row * ld_pmax + col / 64].
   float *pmax; int64_t ld_pmax;
+  // Optional (ring kernel, parts == 1, no C): glu = 1 (or 2 with the
+  // activation rounded to bf16 before the product) makes the output columns
+  // an interleave of W's two halves, 16 gate columns (W rows j) then their 16
+  // up columns (rows N/2 + j), and the epilogue writes
+  // H[row][j] = bf16(silu(bf16(gate)) * bf16(up)) instead of C.
+  uint16_t *H; int64_t ldh; int glu;
 };
 
 // Load one leaf's operand fragments for WB 16-row blocks (two MFMA halves).
@@ -601,10 +607,14 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   // ---- buffer resources over this tile's rows (rows past the end are
   //      clamped to the last row, so every access stays inside)
   const int arows = min(MT, p.M - m0), brows = min(NT, p.N - n0);
+  const bool glu = p.glu != 0;
   rg.rsa = __builtin_amdgcn_make_buffer_rsrc((void *)(p.A + (int64_t)m0 * p.lda), (short)0,
                                              (int)((int64_t)arows * p.lda * 2), 0x00020000);
-  rg.rsb = __builtin_amdgcn_make_buffer_rsrc((void *)(p.W + (int64_t)n0 * p.ldw), (short)0,
-                                             (int)((int64_t)brows * p.ldw * 2), 0x00020000);
+  // SwiGLU mode: the tile's columns map to rows of both halves of W, so the
+  // resource covers all of W
+  rg.rsb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(glu ? p.W : p.W + (int64_t)n0 * p.ldw), (short)0,
+      (int)((int64_t)(glu ? p.N : brows) * p.ldw * 2), 0x00020000);
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int seg = wave + WAVES * i;
@@ -614,7 +624,11 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
       const int row = min(seg * 8 + rin, arows - 1);
       rg.voff[i] = (unsigned)(((int64_t)row * p.lda + 8 * c) * 2);
     } else {
-      const int row = min((seg - SEGA) * 8 + rin, brows - 1);
+      int row = min((seg - SEGA) * 8 + rin, brows - 1);
+      if (glu) {                                     // interleaved column -> row of W
+        const int ic = n0 + row;
+        row = ((ic & 31) < 16 ? 0 : p.N / 2) + (ic >> 5) * 16 + (ic & 15);
+      }
       rg.voff[i] = (unsigned)(((int64_t)row * p.ldw + 8 * c) * 2);
     }
   }
@@ -674,6 +688,30 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   }
   if (pi == PPW - 1) wait_vmcnt<0>();     // no load into LDS may outlive the workgroup
 
+  if (glu) {
+    // a wave's 16 * WN columns start at a multiple of 32: block pairs
+    // (2q, 2q+1) are the gate and up columns of the same 16 units, held by
+    // the same lane; the arithmetic is the SwiGLU node's on the GEMM's bf16
+    // outputs
+#pragma unroll
+    for (int bm = 0; bm < WM; ++bm) {
+#pragma unroll
+      for (int q = 0; q < WN / 2; ++q) {
+        const int colg = n0 + wn * 16 * WN + 32 * q + (lane & 15);
+        const int unit = (colg >> 5) * 16 + (colg & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + wm * 16 * WM + 16 * bm + orow + i;
+          if (row < p.M && colg < p.N) {
+            float a = silu(bf_round(node[(bm * WN + 2 * q) * 4 + i]));
+            if (p.glu == 2) a = bf_round(a);
+            p.H[(int64_t)row * p.ldh + unit] = f2bf(a * bf_round(node[(bm * WN + 2 * q + 1) * 4 + i]));
+          }
+        }
+      }
+    }
+    continue;
+  }
   float *Cp = p.C ? p.C + (int64_t)part * p.part_stride : nullptr;
   uint16_t *Cbp = p.Cb;
 #pragma unroll
@@ -1116,6 +1154,7 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
   a.G = nb / T;
   a.parts = c.parts;
   a.pmax = nullptr; a.ld_pmax = 0;
+  a.H = c.H; a.ldh = c.ldh; a.glu = c.glu;
   a.gpp = T / (c.shard_of > 0 ? c.shard_of : c.parts);
   if (a.G > kMaxGroupLeaves) return TBIK_ERR_SHAPE;
   if ((int64_t)c.batch * c.parts > 65535) return TBIK_ERR_SHAPE;
@@ -1137,6 +1176,16 @@ int launch_gemm(const GemmCall &c, hipStream_t s) {
     const int rc = launch_gemm(c2, s);
     if (rc) return rc;
     return launch_block_rowmax(c.C, c.ldc, c.M, c.N, c.pmax, c.ld_pmax, s);
+  }
+  if (c.glu) {
+    // SwiGLU epilogue: the ring kernel on the whole tree (one part, one
+    // batch), W addressed through one 32-bit buffer range
+    if (c.leaf_mode != TBIK_LEAF_MFMA || c.M <= 32 || c.batch != 1 || c.parts != 1 ||
+        c.shard_of != 0 || (c.N % 32) != 0 || !ring_supported_g(a.G) ||
+        (int64_t)128 * c.lda * 2 >= ((int64_t)1 << 31) ||
+        (int64_t)c.N * c.ldw * 2 >= ((int64_t)1 << 31))
+      return TBIK_ERR_SHAPE;
+    return launch_ring(a, s);
   }
   if (c.leaf_mode == TBIK_LEAF_SCALAR) {
     dim3 grid((unsigned)((c.N + 63) / 64), (unsigned)c.M, (unsigned)(c.batch * c.parts));

@@ -255,6 +255,23 @@ int tbik_swiglu(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int 
                         stream);
 }
 
+int tbik_gemm_swiglu(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W_gu, int64_t ldw,
+                     tbik_bf16 *H, int64_t ldh, int M, int F, int K, int rounding, void *stream) {
+  if (!H) return TBIK_ERR_NULL;
+  if (F <= 0 || (F % 16) != 0 || F > (1 << 29) || ldh < F) return TBIK_ERR_SHAPE;
+  if (!rounding_ok(rounding)) return TBIK_ERR_ARG;
+  int rc = check_gemm(A, lda, W_gu, ldw, nullptr, 2 * (int64_t)F, H, M, 2 * F, K, TBIK_LEAF_MFMA);
+  if (rc) return rc;
+  if (M == 0) return TBIK_OK;
+  tbik::GemmCall c{};
+  c.A = A; c.lda = lda; c.strideA = 0;
+  c.W = W_gu; c.ldw = ldw; c.strideW = 0;
+  c.C = nullptr; c.Cb = nullptr; c.ldc = 2 * (int64_t)F; c.strideC = 0; c.part_stride = 0;
+  c.M = M; c.N = 2 * F; c.K = K; c.batch = 1; c.parts = 1; c.leaf_mode = TBIK_LEAF_MFMA;
+  c.H = H; c.ldh = ldh; c.glu = rounding == TBIK_ROUND_EACH_OP ? 2 : 1;
+  return tbik::launch_gemm(c, as_stream(stream));
+}
+
 int tbik_swiglu_ex(const tbik_bf16 *gate, const tbik_bf16 *up, tbik_bf16 *out, int rows,
                    int cols, int64_t ld_gate, int64_t ld_up, int64_t ld_out, int rounding,
                    void *stream) {

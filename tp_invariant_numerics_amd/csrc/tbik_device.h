@@ -84,6 +84,58 @@ __device__ __forceinline__ float exp_f32(float x) {
   return (x != x) ? x + x : res;
 }
 
+// --- SiLU ---------------------------------------------------------------------
+// silu(g) = g / (1 + EXP(-g)), the division correctly rounded.
+// Fast path: the quotient from a refined reciprocal plus one exact-remainder
+// correction (Markstein's scheme).  The gate is bf16, so silu has only
+// 2^16 possible arguments: for every finite bf16 g with g >= -87 and
+// |g| >= 2^-20 the fast path returns the IEEE quotient, whatever reciprocal
+// within 3 ulp the hardware's v_rcp_f32 gives (checked exhaustively on the
+// CPU for each such reciprocal; the GPU path is checked against the oracle on
+// all 2^16 gates).  g >= -87 keeps 1 + EXP(-g) below 2^126, so the reciprocal
+// is a normal number.  Every other g (NaN, +-inf, g < -87, tiny |g|) takes
+// the IEEE division in a branch that random activations essentially never
+// enter.
+__device__ __forceinline__ float silu_den(float g) { return 1.0f + exp_core(exp_clamp(-g)); }
+
+__device__ __forceinline__ bool silu_fast_ok(float g) {
+  return g >= -87.0f && __builtin_fabsf(g) >= 0x1p-20f && g <= 0x1.fffffep+127f;
+}
+
+__device__ __forceinline__ float silu_fast(float g, float d) {
+  const float y0 = __builtin_amdgcn_rcpf(d);
+  const float e0 = __builtin_fmaf(-d, y0, 1.0f);
+  const float y1 = __builtin_fmaf(e0, y0, y0);
+  const float q0 = g * y1;
+  const float rm = __builtin_fmaf(-d, q0, g);
+  return __builtin_fmaf(rm, y1, q0);
+}
+
+// n gates at once; the IEEE fallback is one branch for all n.
+template <int n>
+__device__ __forceinline__ void silu_n(float (&g)[n]) {
+  float d[n];
+  bool slow = false;
+#pragma unroll
+  for (int e = 0; e < n; ++e) {
+    d[e] = silu_den(g[e]);
+    slow = slow || !silu_fast_ok(g[e]);
+  }
+  if (slow) {
+#pragma unroll
+    for (int e = 0; e < n; ++e) g[e] = silu_fast_ok(g[e]) ? silu_fast(g[e], d[e]) : g[e] / d[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < n; ++e) g[e] = silu_fast(g[e], d[e]);
+  }
+}
+
+__device__ __forceinline__ float silu(float g) {
+  float v[1] = {g};
+  silu_n<1>(v);
+  return v[0];
+}
+
 // --- LOG ---------------------------------------------------------------------
 // x = 2^k m, m in [sqrt(1/2), sqrt(2)); f = m - 1 (exact); s = f/(2+f);
 // log(1+f) = 2 atanh(s) = f - hfsq + s (hfsq + R(s^2)), hfsq = f^2/2,

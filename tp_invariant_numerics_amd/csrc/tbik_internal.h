@@ -23,6 +23,9 @@ struct GemmCall {
   // Optional: exact row maxima of C over 64-column blocks (needs C, one
   // batch, one part): pmax[row * ld_pmax + col / 64].
   float *pmax; int64_t ld_pmax;
+  // Optional: SwiGLU epilogue instead of C (glu = 1 once, 2 each_op; W's
+  // rows are [gate; up], N = 2F, H [M][F] bf16).  Ring kernel shapes only.
+  uint16_t *H; int64_t ldh; int glu;
 };
 
 // Returns 0 or a TBIK_ERR_* code.

@@ -54,6 +54,9 @@ def _rounding_codes(rounding):
     return {k: ROUNDING[v] for k, v in rd.items()}
 
 
+_ERR_SHAPE = -2          # TBIK_ERR_SHAPE
+
+
 def _p(t, off=0):
     return t.data_ptr() + off * t.element_size()
 
@@ -171,9 +174,16 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA, rounding=No
         else:
             rowpar(attn, lw["w_o"], x, tp)
         norm(x, lw["mlp_norm"])
-        _gemm(h, d, lw["w_gu"], d, None, gu, 2 * f, T, 2 * f, d, leaf_mode)
-        rc = L_.tbik_swiglu_ex(_p(gu), _p(gu, f), _p(a), T, f, 2 * f, 2 * f, f, rc_of["swiglu"], st)
-        _chk(rc, "tbik_swiglu_ex")
+        # gate/up projection and SwiGLU: one fused launch where the library
+        # takes the shape (same bits as the two calls below)
+        rc = (L_.tbik_gemm_swiglu(_p(h), d, _p(lw["w_gu"]), d, _p(a), f, T, f, d,
+                                  rc_of["swiglu"], st)
+              if leaf_mode == LEAF_MFMA else _ERR_SHAPE)
+        if rc == _ERR_SHAPE:
+            _gemm(h, d, lw["w_gu"], d, None, gu, 2 * f, T, 2 * f, d, leaf_mode)
+            rc = L_.tbik_swiglu_ex(_p(gu), _p(gu, f), _p(a), T, f, 2 * f, 2 * f, f,
+                                   rc_of["swiglu"], st)
+        _chk(rc, "tbik_gemm_swiglu / tbik_swiglu_ex")
         if rowpar is None:
             _gemm_rowpar(a, lw["w_down"], x, tp, leaf_mode, ws)
         else:
