@@ -82,12 +82,18 @@
 #ifndef TBIK_RING_NX
 #define TBIK_RING_NX 3
 #endif
-// cache-policy bits of the ring's loads of A and of W (2 = non-temporal)
+// cache-policy bits of the ring's loads of A and of W (2 = non-temporal);
+// W through tiles of at most 32 rows is streamed exactly once (every row
+// tile holds all of M), so those loads are non-temporal (M = 1: 25 -> 22 us;
+// the 128-row tiles share W between row tiles and lose with it)
 #ifndef TBIK_RING_AUX_A
 #define TBIK_RING_AUX_A 0
 #endif
 #ifndef TBIK_RING_AUX_B
 #define TBIK_RING_AUX_B 0
+#endif
+#ifndef TBIK_THIN_AUX_B
+#define TBIK_THIN_AUX_B 2
 #endif
 
 namespace tbik {
@@ -422,7 +428,7 @@ struct Ring {
     for (int i = DPA; i < DPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsb, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
-          TBIK_RING_AUX_B);
+          MT <= 32 ? TBIK_THIN_AUX_B : TBIK_RING_AUX_B);
   }
 
   // fragments of the next leaf (PIPE): read one leaf ahead of their MFMAs
