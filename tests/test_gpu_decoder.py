@@ -147,15 +147,21 @@ def _attention_unfused(q, k, vT, B, L, H, scale):
     return out
 
 
-@pytest.mark.parametrize("B,L,H", [(2, 64, 3), (2, 128, 2), (1, 256, 2), (3, 512, 4)])
-def test_fused_attention_equals_composition(B, L, H):
+@pytest.mark.parametrize("B,L,H,amp", [(2, 64, 3, 1), (2, 128, 2, 1), (1, 256, 2, 1), (3, 512, 4, 1),
+                                        (2, 512, 2, 24), (2, 128, 3, 6)])
+def test_fused_attention_equals_composition(B, L, H, amp):
+    # amp > 1 widens the scores (standard deviation ~amp): rows whose visible
+    # scores span more than 41 take the kernel's IEEE-division branch, the
+    # others its product-and-correction path, often within one wave
     d = H * 128
     T = B * L
     q = inputs.normal_bf16((T, 2 * d), 5100 + L, device=DEV)[:, :d]       # row stride 2d
+    if amp != 1:
+        q = (q.float() * amp).to(torch.bfloat16)
     k = inputs.normal_bf16((T, d), 5101 + L, device=DEV)
     vT = inputs.normal_bf16((d, T), 5102 + L, device=DEV)
     scale = float(torch.tensor(1.0 / 128 ** 0.5, dtype=torch.float32))
-    say("fused attention", B, L, H)
+    say("fused attention", B, L, H, amp)
     ref = _attention_unfused(q, k, vT, B, L, H, scale)
     out = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
     rc = tb.lib().tbik_attention_causal(q.data_ptr(), q.stride(0), k.data_ptr(), k.stride(0),
