@@ -21,6 +21,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -52,8 +53,8 @@ def gemm_source_sha256(root):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--M", type=int, default=256)
     ap.add_argument("--tp", type=int, default=8)
     ap.add_argument("--no-extra", action="store_true", help="headline step only")
@@ -103,19 +104,30 @@ def main():
         log("pmc-calib: copied %d bytes x5" % nbytes)
         return
 
-    def timed(fn, iters, warm=3):
-        """Average ms per call of fn() over iters calls, HIP events on the stream."""
+    def timed(fn, iters, warm=3, min_ms=25.0, max_iters=1000):
+        """Average ms per call of fn() over at least iters calls, HIP events on
+        the stream.  A timed region shorter than min_ms is repeated with more
+        calls (up to max_iters): the first launch after a synchronisation
+        costs extra, which would otherwise weigh on the mean of a short loop."""
         for _ in range(warm):
             fn()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for _ in range(iters):
-            fn()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / iters
+
+        def run(n):
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(n):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        total = run(iters)
+        n = min(max_iters, int(math.ceil(iters * min_ms / max(total, 1e-3))))
+        if n > iters:
+            total, iters = run(n), n
+        return total / iters
 
     # ------------------------------------------------------------------ headline
     M, K, N, tp = args.M, 14336, 4096, args.tp
