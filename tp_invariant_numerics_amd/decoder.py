@@ -145,10 +145,11 @@ def decoder_forward(weights, tokens, cfg, tp=1, leaf_mode=LEAF_MFMA, rounding=No
         norm(x, lw["attn_norm"])
         _gemm(h, d, lw["w_qk"], d, None, qk, 2 * d, T, 2 * d, d, leaf_mode)
         _gemm(lw["w_v"], d, h, d, None, vT, T, d, T, d, leaf_mode)
-        for off in (0, d):                       # q, then k, rotated in place
-            rc = L_.tbik_rope_ex(_p(qk, off), _p(qk, off), _p(pos), _p(c_tab), _p(s_tab), T, H,
-                                 hd, 2 * d, L, rc_of["rope"], st)
-            _chk(rc, "tbik_rope_ex")
+        # q and k rotated in place by one call: a qk row is the H query heads
+        # followed by the H key heads, so it is 2H heads at the same position
+        rc = L_.tbik_rope_ex(_p(qk), _p(qk), _p(pos), _p(c_tab), _p(s_tab), T, 2 * H, hd, 2 * d,
+                             L, rc_of["rope"], st)
+        _chk(rc, "tbik_rope_ex")
         if leaf_mode == LEAF_MFMA and hd == 128 and L in (64, 128, 256, 512):
             # fused kernel: the same bits as the three steps below, without
             # the score matrix in HBM
