@@ -194,7 +194,11 @@ enum { TBIK_ROUND_ONCE = 0, TBIK_ROUND_EACH_OP = 1 };
  *   y = bf16((h * rstd) * w).
  *  x, r, y, r_out  [rows, H] bf16 with row stride ld; r_out may be NULL.
  *  w               [H] bf16.
- *  H               1 .. 65536;  eps >= 0.
+ *  H               1 .. 65536, and H / c <= 8192 for the chunk width c: the
+ *                  largest power of two <= 16 that divides both H / T (T the
+ *                  tree's group count) and the rows' alignment in elements
+ *                  (e.g. H = 65534 has c = 1 and returns TBIK_ERR_SHAPE
+ *                  before any launch);  eps >= 0.
  * ---------------------------------------------------------------------- */
 int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
                           tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,

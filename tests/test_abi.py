@@ -176,6 +176,10 @@ def test_rowop_validation(L):
     assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 64, 32, 1e-6, None) == E_SHAPE
     assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 64, 64, -1.0, None) == E_ARG
     assert r(FAKE, FAKE, FAKE, MISAL, None, 1, 64, 64, 1e-6, None) == E_ALIGN
+    assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 65537, 65537, 1e-6, None) == E_SHAPE
+    # 65534 = 2 x 32767: one-element chunks, 65534 of them, over the limit
+    # (refused by the launcher before it launches anything)
+    assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 65534, 65534, 1e-6, None) == E_SHAPE
     ro = L.tbik_rope
     assert ro(FAKE, FAKE, None, FAKE, FAKE, 1, 1, 128, 128, 16, None) == E_NULL
     assert ro(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 130, 136, 16, None) == E_SHAPE

@@ -284,7 +284,8 @@ def test_gemm_strided_batched_equals_single(orc):
 # ------------------------------------------------------------------ RMSNorm
 @pytest.mark.parametrize("rows,H", [(1, 4096), (7, 4096), (256, 4096), (4096, 4096),
                                     (5, 2048), (3, 5120), (4, 1000), (9, 96), (2, 8), (3, 4104),
-                                    (3, 64), (2, 512), (2, 16384)])
+                                    (3, 64), (2, 512), (2, 16384), (2, 65536), (3, 1),
+                                    (2, 24576)])
 def test_rmsnorm_bitexact(orc, rows, H):
     x = inputs.outlier_bf16((rows, H), 8000 + H)
     r = inputs.outlier_bf16((rows, H), 8001 + H)
