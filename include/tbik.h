@@ -284,7 +284,11 @@ int tbik_gemm_swiglu(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W_gu, int
  * library materialises each shard's partial sum in ws (what vocab-parallel
  * ranks would exchange) and combines them with the top of the tree; the
  * result is bit-identical for every tp.
- *  logits   [M, V] fp32, row stride ld.
+ *  logits   [M, V] fp32, row stride ld.  M <= 65535; V / c <= 40944 for
+ *           the chunk width c, the largest power of two <= 16 dividing both
+ *           V / T and the rows' alignment in fp32 elements (V up to 655104
+ *           when V / T is a multiple of 16); larger V return TBIK_ERR_SHAPE
+ *           before any launch (a row's chunk sums are staged in LDS).
  *  targets  [M] int32 in [0, V) (out-of-range targets: out_lp = NaN).
  *  out_lp   [M] fp32.
  *  ws       at least tbik_logsoftmax_workspace_bytes(M, V, tp) = M*tp*4

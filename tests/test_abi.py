@@ -198,6 +198,10 @@ def test_rowop_validation(L):
                                       None) == OK
     ls = L.tbik_logsoftmax_gather
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 3, FAKE, 1 << 20, None) == E_TP
+    # an odd V has one-element chunks: more than 40944 chunk sums do not fit
+    # the LDS beside the kernel's own 64 bytes (refused by the launcher
+    # before it launches anything)
+    assert ls(FAKE, 40945, FAKE, FAKE, 1, 40945, 1, FAKE, 1 << 20, None) == E_SHAPE
     assert ls(FAKE, 24, FAKE, FAKE, 2, 12, 8, FAKE, 1 << 20, None) == E_TP   # T(12) = 4
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 1, None, 0, None) == E_WS
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 1, FAKE, 4, None) == E_WS

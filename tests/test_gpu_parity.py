@@ -406,7 +406,8 @@ def test_logprob_path_fused_max_bitexact(orc, tp):
 # ------------------------------------------------------------------ log-softmax
 @pytest.mark.parametrize("M,V,tps", [(8, 151936, (1, 2, 4, 8)), (16, 32000, (1, 2, 4, 8)),
                                      (5, 1000, (1, 2, 4, 8)), (3, 12, (1, 2, 4)),
-                                     (4, 7, (1,))])
+                                     (4, 7, (1,)), (2, 655104, (1, 8)), (2, 40943, (1,)),
+                                     (3, 1, (1,))])
 def test_logsoftmax_bitexact(orc, M, V, tps):
     rng = np.random.default_rng(V)
     logits = (rng.standard_normal((M, V)) * 3).astype(np.float32)

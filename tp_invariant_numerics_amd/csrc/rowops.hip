@@ -726,7 +726,9 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
   const int ch = cap_f32(chunk_for(G), elem_align(logits, ld, 4));
   const int nch = V / ch;
   size_t lds = (size_t)nch * sizeof(float);
-  if (lds > 160 * 1024) return TBIK_ERR_SHAPE;
+  // one float per chunk in dynamic LDS, beside the kernel's static per-wave
+  // reduction buffer, within a workgroup's 160 KB
+  if (lds + (size_t)(kLsmThreads / 64) * sizeof(float) > 160 * 1024) return TBIK_ERR_SHAPE;
   if (lds < (size_t)TBIK_LSM_LDS_MIN) lds = TBIK_LSM_LDS_MIN;
   float *shard = ws;
   dim3 grid((unsigned)M), block(kLsmThreads);
