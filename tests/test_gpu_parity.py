@@ -309,7 +309,7 @@ def test_rmsnorm_rows_invariant():
 
 # ------------------------------------------------------------------ RoPE
 @pytest.mark.parametrize("T,heads,d", [(2048, 16, 128), (33, 3, 64), (5, 1, 8), (17, 6, 32),
-                                        (9, 2, 8)])
+                                        (9, 2, 8), (3, 2, 1024), (4, 3, 1016), (2, 64, 128)])
 def test_rope_bitexact(orc, T, heads, d):
     x = inputs.normal_bf16((T, heads, d), 9000 + T)
     pos = inputs.positions(T, 32768, seed=9)
