@@ -230,7 +230,8 @@ def test_gemm_mfma_column_slices_invariant():
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 256, 1024), (64, 256, 14336), (40, 96, 4096),
-                                   (1, 64, 14336), (300, 70, 2048)])
+                                   (1, 64, 14336), (300, 70, 2048), (5, 1, 64), (1, 1, 64),
+                                   (2, 9, 192), (130, 3, 128)])
 def test_gemm_mfma_accuracy(orc, M, N, K):
     A, W = _gen_gemm(M, N, K, 5000 + M, wstd=0.02)
     say("mfma accuracy", M, N, K)
