@@ -146,7 +146,8 @@ def test_gemm_scalar_leaf_probes_golden(orc):
 
 @pytest.mark.parametrize("M,N,K,tps", [(16, 256, 1024, (1, 2, 4, 8)),
                                        (8, 40, 14336, (1, 2, 4, 8)),
-                                       (5, 24, 64 * 28, (1, 2, 4))])
+                                       (5, 24, 64 * 28, (1, 2, 4)), (3, 5, 128, (1, 2)),
+                                       (2, 1, 8 * 64 * 3, (1, 2, 4, 8))])
 def test_gemm_tpsim_scalar_bitexact(orc, M, N, K, tps):
     A, W = _gen_gemm(M, N, K, 2000 + K, wstd=0.02)
     for tp in tps:
@@ -161,7 +162,9 @@ def test_gemm_tpsim_scalar_bitexact(orc, M, N, K, tps):
                                        (1, 4096, 14336, (1, 2, 4, 8)),
                                        (32, 4096, 14336, (1, 2, 4, 8)),
                                        (256, 4096, 14336, (1, 2, 4, 8)),
-                                       (77, 300, 64 * 28, (1, 2, 4))])
+                                       (77, 300, 64 * 28, (1, 2, 4)),
+                                       (3, 5, 128, (1, 2)), (4, 17, 512, (1, 2, 4, 8)),
+                                       (40, 1, 8 * 64 * 3, (1, 2, 4, 8))])
 def test_gemm_mfma_tp_invariant(M, N, K, tps):
     A = inputs.normal_bf16((M, K), 3000 + M, device=DEV)
     W = inputs.normal_bf16((N, K), 3001 + M, std=0.02, device=DEV)
