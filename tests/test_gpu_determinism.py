@@ -1,0 +1,103 @@
+"""Run-to-run determinism: every workload repeated 20 times on the same
+inputs gives outputs with the same SHA-256, stopping at the first change.
+
+The nondeterminism note (section 5) names atomics and scheduling-dependent
+algorithm choices as sources of run-to-run differences; the library's
+fixed trees have neither, and a race in an LDS tree or a missing barrier
+would show here as a changed hash.  Inputs are fingerprinted the same way
+(the note's closing practice), so a failure names exactly what was run.
+"""
+import hashlib
+
+import pytest
+import torch
+
+import tp_invariant_numerics_amd as tb
+from tp_invariant_numerics_amd import inputs
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+REPEATS = 20
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    tb.lib()
+
+
+def sha(*ts):
+    h = hashlib.sha256()
+    for t in ts:
+        h.update(t.detach().contiguous().view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
+def _repeat(name, fn, ins):
+    say(name, "inputs sha256", sha(*ins)[:16])
+    first = sha(*fn())
+    for i in range(1, REPEATS):
+        h = sha(*fn())
+        assert h == first, "%s: run %d output sha256 %s != run 0 %s" % (name, i, h[:16], first[:16])
+    say(name, "output sha256", first[:16], "x%d" % REPEATS)
+
+
+@pytest.mark.parametrize("tp", [1, 2, 4])
+def test_repeat_small_tp_gemm(tp):
+    A = inputs.normal_bf16((16, 1024), 14000, device=DEV)
+    W = inputs.normal_bf16((256, 1024), 14001, device=DEV)
+    _repeat("tpsim 16x1024x256 tp%d" % tp, lambda: tb.tbik_gemm_tpsim(A, W, tp)[::2], (A, W))
+
+
+@pytest.mark.parametrize("M,tp", [(1, 8), (32, 8), (256, 8), (256, 1), (32, 1)])
+def test_repeat_downproj(M, tp):
+    A = inputs.normal_bf16((M, 14336), 14100 + M, device=DEV)
+    W = inputs.normal_bf16((4096, 14336), 14101, std=0.02, device=DEV)
+    if tp == 1:
+        fn = lambda: (tb.tbik_gemm(A, W)[0],)  # noqa: E731
+    else:
+        fn = lambda: tb.tbik_gemm_tpsim(A, W, tp)[::2]  # noqa: E731
+    _repeat("down projection M%d tp%d" % (M, tp), fn, (A, W))
+
+
+def test_repeat_row_kernels():
+    x = inputs.outlier_bf16((4096, 4096), 14200, device=DEV)
+    r = inputs.outlier_bf16((4096, 4096), 14201, device=DEV)
+    w = inputs.normal_bf16((4096,), 14202, std=0.1, mean=1.0, device=DEV)
+    _repeat("rmsnorm 4096x4096", lambda: tb.tbik_rmsnorm_residual(x, r, w, 1e-6), (x, r, w))
+    q = inputs.normal_bf16((8192, 16, 128), 14203, device=DEV)
+    pos = inputs.positions(8192, 32768, seed=14204).to(DEV)
+    c, s = tb.tbik_rope_table(1e6, 128, 32768)
+    c, s = c.to(DEV), s.to(DEV)
+    _repeat("rope 8192x16x128", lambda: (tb.tbik_rope(q, pos, c, s),), (q, pos, c, s))
+    g = inputs.normal_bf16((4096, 14336), 14205, std=3.0, device=DEV)
+    u = inputs.normal_bf16((4096, 14336), 14206, device=DEV)
+    _repeat("swiglu 4096x14336", lambda: (tb.tbik_swiglu(g, u),), (g, u))
+
+
+@pytest.mark.parametrize("tp", [1, 4])
+def test_repeat_logprob_path(tp):
+    M, K, V = 512, 4096, 151936
+    A = inputs.normal_bf16((M, K), 14300, device=DEV)
+    W = inputs.normal_bf16((V, K), 14301, std=0.02, device=DEV)
+    tgt = inputs.uniform_int(M, V, 14302, device=DEV)
+
+    def run():
+        logits, pmax = tb.tbik_gemm_logits(A, W)
+        lp, ws = tb.tbik_logsoftmax_gather_pmax(logits, tgt, pmax, tp)
+        return logits, pmax, lp, tb.logsoftmax_shard_nodes(ws, M, tp)
+
+    _repeat("logprob path tp%d" % tp, run, (A, W, tgt))
+
+
+def test_repeat_decoder():
+    from tp_invariant_numerics_amd.decoder import decoder_forward
+    cfg = inputs.DecoderConfig()
+    w = inputs.decoder_weights(cfg, 14400, device=DEV)
+    tok = inputs.decoder_tokens(8, 512, cfg.vocab, 14401, device=DEV)
+    _repeat("decoder 8L tp4", lambda: (decoder_forward(w, tok, cfg, tp=4),),
+            (tok, w["lm_head"], w["layers"][0]["w_qk"]))

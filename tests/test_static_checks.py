@@ -1,0 +1,96 @@
+"""Static checks of the HIP library's sources and of its compiled device code.
+
+The nondeterminism note (section 5, framework and operator implementation)
+names atomics as a source of run-to-run differences: the order in which
+atomic additions land changes the sum.  The library's reductions are fixed
+trees, so no kernel may contain an atomic operation -- checked in the
+sources (comments removed) and in the gfx950 disassembly of this build's
+own code objects.  The same disassembly shows that EXP and LOG never fall
+back to the hardware transcendental instructions (their results are defined
+by the library's own operation sequences) and that no packed-fp32
+arithmetic was emitted.
+"""
+import glob
+import os
+import re
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "tp_invariant_numerics_amd", "csrc")
+OBJDIR = os.path.join(ROOT, "_build", "tbik")
+LLVM = "/opt/rocm/llvm/bin"
+
+
+def _strip_comments(text):
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return re.sub(r'"(?:\\.|[^"\\])*"', '""', text)
+
+
+def test_no_atomics_in_kernel_sources():
+    files = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h")))
+    assert len(files) >= 5
+    hits = []
+    for f in files:
+        code = _strip_comments(open(f, encoding="utf-8").read())
+        for ln, line in enumerate(code.splitlines(), 1):
+            if re.search(r"atomic", line, re.I):
+                hits.append("%s:%d: %s" % (os.path.basename(f), ln, line.strip()))
+    assert not hits, hits
+
+
+def _device_disassembly():
+    objs = sorted(glob.glob(os.path.join(OBJDIR, "*.o")))
+    if not objs or not os.path.exists(os.path.join(LLVM, "clang-offload-bundler")):
+        pytest.skip("library objects not built (run __graft_entry__.build())")
+    out = {}
+    tmp = tempfile.mkdtemp(prefix="tbik_dis_")
+    try:
+        for o in objs:
+            name = os.path.splitext(os.path.basename(o))[0]
+            fb = os.path.join(tmp, name + ".fb")
+            r = subprocess.run([os.path.join(LLVM, "llvm-objcopy"),
+                                "--dump-section", ".hip_fatbin=" + fb, o],
+                               capture_output=True, text=True)
+            if r.returncode != 0:
+                continue                      # host-only object (the C ABI)
+            co = os.path.join(tmp, name + ".co")
+            subprocess.run([os.path.join(LLVM, "clang-offload-bundler"), "--unbundle",
+                            "--type=o", "--targets=hipv4-amdgcn-amd-amdhsa--gfx950",
+                            "--input=" + fb, "--output=" + co], check=True)
+            dis = subprocess.run([os.path.join(LLVM, "llvm-objdump"), "-d", co],
+                                 capture_output=True, text=True, check=True).stdout
+            out[name] = dis
+    finally:
+        shutil.rmtree(tmp, ignore_errors=True)
+    assert "gemm" in out and "rowops" in out, sorted(out)
+    return out
+
+
+@pytest.fixture(scope="module")
+def disassembly():
+    return _device_disassembly()
+
+
+def _mnemonics(dis):
+    for line in dis.splitlines():
+        m = re.match(r"\s+([a-z_][a-z0-9_]*)\s", line)
+        if m:
+            yield m.group(1)
+
+
+def test_no_atomic_instructions_in_code_objects(disassembly):
+    bad = {n: sorted({m for m in _mnemonics(d) if "atomic" in m}) for n, d in disassembly.items()}
+    assert not any(bad.values()), bad
+
+
+def test_no_hardware_transcendentals_or_packed_fp32(disassembly):
+    pat = re.compile(r"^v_(exp|log|rsq)_|^v_pk_(add|mul|fma)_f32$")
+    bad = {n: sorted({m for m in _mnemonics(d) if pat.search(m)}) for n, d in disassembly.items()}
+    assert not any(bad.values()), bad
+    # the GEMM does run on the matrix cores
+    assert any(m.startswith("v_mfma_f32_16x16x32_bf16") for m in _mnemonics(disassembly["gemm"]))

@@ -76,6 +76,30 @@ def integer_bf16(shape, seed, lo=-8, hi=8):
     return torch.from_numpy(x).to(torch.bfloat16)
 
 
+def one_per_block_bf16(shape, seed, block=64, spread=6, value=None, device="cpu"):
+    """bf16 tensor whose rows hold exactly one nonzero entry in each `block`-wide
+    slice of the last axis, at a uniform position.  Values ~N(0,1) times
+    2^e with e uniform in [-spread, spread], or the constant `value`.  Against
+    any dense second operand, every `block`-wide partial dot product of such a
+    row has a single nonzero term."""
+    shape = tuple(int(s) for s in shape)
+    rows, n = int(np.prod(shape[:-1])), shape[-1]
+    nblk = (n + block - 1) // block
+    g = _gen(seed)
+    x = np.zeros((rows, nblk * block), np.float32)
+    pos = g.integers(0, block, (rows, nblk)) + np.arange(nblk) * block
+    if value is None:
+        v = g.standard_normal((rows, nblk)).astype(np.float32)
+        v = v * np.exp2(g.integers(-spread, spread + 1, (rows, nblk))).astype(np.float32)
+        v[v == 0] = 1.0
+    else:
+        v = np.full((rows, nblk), value, np.float32)
+    np.put_along_axis(x, pos, v, axis=1)
+    # a ragged last block keeps its entry only if it falls inside
+    t = torch.from_numpy(np.ascontiguousarray(x[:, :n]).reshape(shape)).to(torch.bfloat16)
+    return t.to(device)
+
+
 def bits(t):
     """numpy uint16 view of a bf16 tensor's bit patterns (copied to host)."""
     assert t.dtype == torch.bfloat16
