@@ -457,6 +457,32 @@ int tbik_rmsnorm_backward(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf1
                           int rows, int H, int64_t ld, float eps, int dp, float *ws,
                           size_t ws_bytes, void *stream);
 
+/* ------------------------------------------------------------------------
+ * Ceiling microbenchmarks.  Not part of the method: the attainable rates of
+ * this GPU, so that every roofline fraction can be stated against both the
+ * published peak and what the chip sustains (a pure matrix-core loop and
+ * non-temporal HBM streams over buffers far larger than the last-level
+ * cache).  Results are timed by the caller on `stream`.
+ *
+ * tbik_bench_mfma: `blocks` workgroups of 8 waves, each wave running 8
+ *   independent chains of `iters` v_mfma_f32_16x16x32_bf16 from registers.
+ *   seed: >= 2048 bytes of device memory (16-byte aligned) holding the
+ *   operands; out: blocks * 512 floats (one per thread, keeps the chains
+ *   live).  tbik_bench_mfma_flops gives the flops of one launch (0 for
+ *   invalid arguments).
+ * tbik_bench_hbm_read: `blocks` workgroups of 256 threads stream `bytes`
+ *   (a positive multiple of 16) of buf with non-temporal 16-byte loads;
+ *   out: blocks * 256 unsigned (an xor of what each thread read).
+ * tbik_bench_hbm_copy: src -> dst, `bytes` (multiple of 16), non-temporal
+ *   16-byte loads and stores; the buffers must not overlap.
+ * Errors: TBIK_ERR_NULL, TBIK_ERR_SHAPE (sizes out of range),
+ * TBIK_ERR_ALIGN (pointers not 16-byte aligned), TBIK_ERR_LAUNCH.
+ * ---------------------------------------------------------------------- */
+int64_t tbik_bench_mfma_flops(int blocks, int iters);
+int tbik_bench_mfma(const void *seed, float *out, int blocks, int iters, void *stream);
+int tbik_bench_hbm_read(const void *buf, int64_t bytes, unsigned *out, int blocks, void *stream);
+int tbik_bench_hbm_copy(const void *src, void *dst, int64_t bytes, int blocks, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,6 +93,10 @@ def _sigs():
         "tbik_swiglu_backward": (i32, [p, p, p, p, p, i32, i32, i64, i64, i64, i64, i64, p]),
         "tbik_rmsnorm_backward_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "tbik_rmsnorm_backward": (i32, [p, p, p, p, p, p, p, i32, i32, i64, f32, i32, p, sz, p]),
+        "tbik_bench_mfma_flops": (i64, [i32, i32]),
+        "tbik_bench_mfma": (i32, [p, p, i32, i32, p]),
+        "tbik_bench_hbm_read": (i32, [p, i64, p, i32, p]),
+        "tbik_bench_hbm_copy": (i32, [p, p, i64, i32, p]),
     }
 
 
@@ -523,3 +527,34 @@ def tbik_rmsnorm_backward(x, r, w, dy, dr=None, eps=1e-6, dp=1, want_dw=True):
         off = (rows + 63) // 64 * 64 + (rows // 64) * H
         shards = ws[off:off + dp * H].view(dp, H)
     return dh, dw, shards
+
+
+# --- ceiling microbenchmarks --------------------------------------------------
+
+def tbik_bench_mfma(seed, blocks, iters, out=None):
+    """One launch of the matrix-core loop; seed: >= 2048 bytes on the device.
+    Returns (out, flops of the launch)."""
+    _need_gpu(seed)
+    if out is None:
+        out = torch.empty((blocks * 512,), dtype=torch.float32, device=seed.device)
+    _chk(lib().tbik_bench_mfma(_ptr(seed), _ptr(out), blocks, iters, _stream()), "tbik_bench_mfma")
+    return out, lib().tbik_bench_mfma_flops(blocks, iters)
+
+
+def tbik_bench_hbm_read(buf, blocks, out=None):
+    _need_gpu(buf)
+    if out is None:
+        out = torch.empty((blocks * 256,), dtype=torch.int32, device=buf.device)
+    _chk(lib().tbik_bench_hbm_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), blocks,
+                                   _stream()), "tbik_bench_hbm_read")
+    return out
+
+
+def tbik_bench_hbm_copy(src, dst, blocks):
+    _need_gpu(src, dst)
+    n = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() < n:
+        raise ValueError("dst too small")
+    _chk(lib().tbik_bench_hbm_copy(_ptr(src), _ptr(dst), n, blocks, _stream()),
+         "tbik_bench_hbm_copy")
+    return dst

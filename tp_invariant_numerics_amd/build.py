@@ -14,7 +14,8 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libtbik.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["gemm.hip", "rowops.hip", "attention.hip", "training.hip", "tbik_abi.hip"]
+SOURCES = ["gemm.hip", "rowops.hip", "attention.hip", "training.hip", "microbench.hip",
+           "tbik_abi.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,113 @@
+// microbench.hip -- attainable ceilings of the chip, measured by the library's
+// own kernels so that every roofline fraction can be quoted against both the
+// published peak and what this GPU actually sustains.
+//
+//   k_mfma_peak   independent chains of v_mfma_f32_16x16x32_bf16 (the GEMM
+//                 leaf instruction) from registers: no memory traffic in the
+//                 loop, so its rate is the matrix cores' sustained peak.
+//   k_hbm_read    non-temporal 16-byte loads over a buffer much larger than
+//                 the last-level cache, folded by xor (one 4-byte store per
+//                 thread at the end).
+//   k_hbm_copy    non-temporal 16-byte loads and stores, src -> dst.
+//
+// Grids are sized by the caller; every access is bounds-checked against the
+// byte count (a multiple of 16).
+#include "tbik_device.h"
+#include "tbik_internal.h"
+#include "../../include/tbik.h"
+
+namespace tbik {
+
+// CH independent accumulators per wave; `iters` rounds of CH chained MFMAs.
+template <int CH>
+__global__ void __launch_bounds__(512) k_mfma_peak(const u32x4 *seed, float *out, int iters) {
+  const int lane = threadIdx.x & 63;
+  u32x4 a = seed[lane], b = seed[64 + lane];
+  f32x4 acc[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) acc[c] = f32x4{(float)c, 0.0f, 0.0f, 0.0f};   // distinct chains
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), acc[c], 0,
+                                                       0, 0);
+  }
+  f32x4 s = acc[0];
+#pragma unroll
+  for (int c = 1; c < CH; ++c) s = s + acc[c];
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  out[t] = s[0] + s[1] + s[2] + s[3];
+}
+
+__global__ void __launch_bounds__(256) k_hbm_read(const u32x4 *src, int64_t n16, unsigned *out) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  u32x4 x = {0u, 0u, 0u, 0u};
+  int64_t i = t0;
+  // four loads in flight per thread
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const u32x4 v0 = __builtin_nontemporal_load(src + i);
+    const u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
+    const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * stride);
+    const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * stride);
+    x ^= v0 ^ v1 ^ v2 ^ v3;
+  }
+  for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
+  out[t0] = x[0] ^ x[1] ^ x[2] ^ x[3];
+}
+
+__global__ void __launch_bounds__(256) k_hbm_copy(const u32x4 *src, u32x4 *dst, int64_t n16) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; i + stride < n16; i += 2 * stride) {
+    const u32x4 v0 = __builtin_nontemporal_load(src + i);
+    const u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
+    __builtin_nontemporal_store(v0, dst + i);
+    __builtin_nontemporal_store(v1, dst + i + stride);
+  }
+  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+
+static int mb_check() { return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH; }
+
+}  // namespace tbik
+
+using namespace tbik;
+
+extern "C" {
+
+int64_t tbik_bench_mfma_flops(int blocks, int iters) {
+  if (blocks < 1 || iters < 1) return 0;
+  // 8 waves per block, 8 chains each, 2*16*16*32 flops per instruction
+  return (int64_t)blocks * 8 * 8 * (int64_t)iters * 16384;
+}
+
+int tbik_bench_mfma(const void *seed, float *out, int blocks, int iters, void *stream) {
+  if (!seed || !out) return TBIK_ERR_NULL;
+  if (blocks < 1 || blocks > (1 << 20) || iters < 1) return TBIK_ERR_SHAPE;
+  if (((uintptr_t)seed & 15) != 0) return TBIK_ERR_ALIGN;
+  hipLaunchKernelGGL(k_mfma_peak<8>, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream,
+                     (const u32x4 *)seed, out, iters);
+  return mb_check();
+}
+
+int tbik_bench_hbm_read(const void *buf, int64_t bytes, unsigned *out, int blocks, void *stream) {
+  if (!buf || !out) return TBIK_ERR_NULL;
+  if (bytes <= 0 || (bytes & 15) != 0 || blocks < 1 || blocks > (1 << 20)) return TBIK_ERR_SHAPE;
+  if (((uintptr_t)buf & 15) != 0) return TBIK_ERR_ALIGN;
+  hipLaunchKernelGGL(k_hbm_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4 *)buf, bytes / 16, out);
+  return mb_check();
+}
+
+int tbik_bench_hbm_copy(const void *src, void *dst, int64_t bytes, int blocks, void *stream) {
+  if (!src || !dst) return TBIK_ERR_NULL;
+  if (bytes <= 0 || (bytes & 15) != 0 || blocks < 1 || blocks > (1 << 20)) return TBIK_ERR_SHAPE;
+  if ((((uintptr_t)src | (uintptr_t)dst) & 15) != 0) return TBIK_ERR_ALIGN;
+  hipLaunchKernelGGL(k_hbm_copy, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (const u32x4 *)src, (u32x4 *)dst, bytes / 16);
+  return mb_check();
+}
+
+}  // extern "C"
