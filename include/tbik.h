@@ -46,7 +46,8 @@
  *    leading dimensions (in elements) that are multiples of 8; violations
  *    return TBIK_ERR_ALIGN.  Other arrays take any leading dimension >= the
  *    row length; wider memory accesses are used when alignment permits,
- *    which never changes a result bit.
+ *    which never changes a result bit nor the set of accepted shapes
+ *    (size limits below depend on the shape only).
  *  - Outputs must not overlap inputs unless stated otherwise.
  *  - Inputs must be finite; non-finite inputs give unspecified values (but
  *    never out-of-bounds accesses).
@@ -195,10 +196,10 @@ enum { TBIK_ROUND_ONCE = 0, TBIK_ROUND_EACH_OP = 1 };
  *  x, r, y, r_out  [rows, H] bf16 with row stride ld; r_out may be NULL.
  *  w               [H] bf16.
  *  H               1 .. 65536, and H / c <= 8192 for the chunk width c: the
- *                  largest power of two <= 16 that divides both H / T (T the
- *                  tree's group count) and the rows' alignment in elements
- *                  (e.g. H = 65534 has c = 1 and returns TBIK_ERR_SHAPE
- *                  before any launch);  eps >= 0.
+ *                  largest power of two <= 16 dividing H / T (T the tree's
+ *                  group count; e.g. H = 65534 has c = 1 and returns
+ *                  TBIK_ERR_SHAPE before any launch, whatever the
+ *                  alignment);  eps >= 0.
  * ---------------------------------------------------------------------- */
 int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
                           tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,
@@ -285,10 +286,10 @@ int tbik_gemm_swiglu(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W_gu, int
  * ranks would exchange) and combines them with the top of the tree; the
  * result is bit-identical for every tp.
  *  logits   [M, V] fp32, row stride ld.  M <= 65535; V / c <= 40944 for
- *           the chunk width c, the largest power of two <= 16 dividing both
- *           V / T and the rows' alignment in fp32 elements (V up to 655104
- *           when V / T is a multiple of 16); larger V return TBIK_ERR_SHAPE
- *           before any launch (a row's chunk sums are staged in LDS).
+ *           the chunk width c, the largest power of two <= 16 dividing
+ *           V / T (V up to 655104 when V / T is a multiple of 16, at any
+ *           alignment of the rows); larger V return TBIK_ERR_SHAPE before
+ *           any launch (a row's chunk sums are staged in LDS).
  *  targets  [M] int32 in [0, V) (out-of-range targets: out_lp = NaN).
  *  out_lp   [M] fp32.
  *  ws       at least tbik_logsoftmax_workspace_bytes(M, V, tp) = M*tp*4

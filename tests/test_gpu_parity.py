@@ -671,3 +671,72 @@ def test_swiglu_each_op_bitexact(orc, rows, cols):
     say("swiglu each_op", rows, cols)
     y = tb.tbik_swiglu(g.to(DEV), u.to(DEV), rounding="each_op")
     assert np.array_equal(bits(y), orc.swiglu(bits(g), bits(u), rounding="each_op"))
+
+
+# ------------------------------------------------------------------ alignment never changes the shapes
+@pytest.mark.parametrize("V,ld,off", [(151936, 151937, 0), (151936, 151940, 1), (655104, 655105, 3),
+                                      (32000, 32001, 1)])
+def test_logsoftmax_unaligned_rows_accepted_and_bitexact(orc, V, ld, off):
+    """Rows whose starts are not 16-byte aligned take element-wise loads of
+    the same chunks: accepted exactly like aligned rows (the LM-head
+    vocabulary at an odd row stride; V = 655104, the largest vocabulary the
+    LDS staging takes, at an odd offset), with the oracle's bits."""
+    M = 3
+    rng = np.random.default_rng(V + ld)
+    logits = (rng.standard_normal((M, V)) * 3).astype(np.float32)
+    tgt = rng.integers(0, V, M).astype(np.int32)
+    buf = torch.zeros((M * ld + off + 8,), dtype=torch.float32, device=DEV)
+    view = buf[off:off + M * ld].view(M, ld)[:, :V]
+    view.copy_(torch.from_numpy(logits).to(DEV))
+    say("logsoftmax unaligned", V, ld, off)
+    for tp in (1, 4):
+        lp, ws = tb.tbik_logsoftmax_gather(view, torch.from_numpy(tgt).to(DEV), tp)
+        ref, nodes = orc.logsoftmax_gather(logits, tgt, tp)
+        assert same_bits(lp.cpu().numpy(), ref), tp
+        assert same_bits(tb.logsoftmax_shard_nodes(ws, M, tp).cpu().numpy(), nodes), tp
+
+
+@pytest.mark.parametrize("H,off", [(4096, 1), (4104, 3), (4096, 2), (65536, 1), (5120, 5)])
+def test_rmsnorm_unaligned_rows_accepted_and_bitexact(orc, H, off):
+    rows = 3
+    x = inputs.outlier_bf16((rows, H), 8500 + H)
+    r = inputs.outlier_bf16((rows, H), 8501 + H)
+    w = inputs.normal_bf16((H,), 8502 + H, std=0.1, mean=1.0)
+    ld = H + 3
+    say("rmsnorm unaligned", H, off)
+
+    def place(t):
+        buf = torch.zeros((rows * ld + off + 8,), dtype=torch.bfloat16, device=DEV)
+        v = buf[off:off + rows * ld].view(rows, ld)[:, :H]
+        if t is not None:
+            v.copy_(t.to(DEV))
+        return v
+
+    xd, rd, yd, rod = place(x), place(r), place(None), place(None)
+    wbuf = torch.zeros((H + off + 8,), dtype=torch.bfloat16, device=DEV)
+    wd = wbuf[off:off + H]
+    wd.copy_(w.to(DEV))
+    tb.tbik_rmsnorm_residual(xd, rd, wd, 1e-6, y=yd, r_out=rod)
+    ry, rr = orc.rmsnorm_residual(bits(x), bits(r), bits(w), 1e-6)
+    assert np.array_equal(bits(yd), ry)
+    assert np.array_equal(bits(rod), rr)
+    # the backward pass at the same offsets: dh equal to the aligned call
+    gy = inputs.normal_bf16((rows, H), 8503 + H)
+    gyd = place(gy)
+    dh_u, _, _ = tb.tbik_rmsnorm_backward(xd, rd, wd, gyd, want_dw=False)
+    dh_a, _, _ = tb.tbik_rmsnorm_backward(x.to(DEV), r.to(DEV), w.to(DEV), gy.to(DEV), want_dw=False)
+    assert torch.equal(dh_u.view(torch.int16), dh_a.view(torch.int16))
+
+
+@pytest.mark.parametrize("Lq,Lk,lds_pad", [(40, 512, 1), (33, 96, 3), (64, 64, 1)])
+def test_softmax_causal_unaligned_rows_bitexact(orc, Lq, Lk, lds_pad):
+    rng = np.random.default_rng(Lk + lds_pad)
+    S = (rng.standard_normal((1, Lq, Lk)) * 20).astype(np.float32)
+    ld = Lk + lds_pad
+    buf = torch.zeros((Lq * ld + 4,), dtype=torch.float32, device=DEV)
+    Sv = buf[:Lq * ld].view(1, Lq, ld)[:, :, :Lk]
+    Sv.copy_(torch.from_numpy(S).to(DEV))
+    scale = np.float32(1 / math.sqrt(128))
+    say("softmax_causal unaligned", Lq, Lk, lds_pad)
+    P = tb.tbik_softmax_causal(Sv, 0, float(scale))
+    assert np.array_equal(bits(P[0]), orc.softmax_causal(S[0], 0, scale))

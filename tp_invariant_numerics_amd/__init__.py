@@ -142,6 +142,23 @@ def _ld(t):
     return t.stride(0)
 
 
+def _rows_like(t):
+    """An output with t's shape, dtype and leading (row / token) stride: the
+    C ABI takes one row stride for an input and the output beside it."""
+    rows, ld = t.shape[0], t.stride(0)
+    inner = tuple(t.shape[1:])
+    n = 1
+    for v in inner:
+        n *= v
+    buf = torch.empty((rows, max(ld, n)), dtype=t.dtype, device=t.device)[:, :n]
+    return buf.unflatten(1, inner) if len(inner) > 1 else buf
+
+
+def _same_rows(out, t, what):
+    if out.shape != t.shape or out.stride() != t.stride():
+        raise ValueError("%s must have the shape and strides of its input" % what)
+
+
 def _bits(t):
     if t.dtype != torch.bfloat16:
         raise ValueError("expected bfloat16")
@@ -284,10 +301,12 @@ def tbik_rmsnorm_residual(x, r, w, eps=1e-6, y=None, r_out=None, want_r_out=True
     ld = _ld(x)
     if _ld(r) != ld:
         raise ValueError("x and r must share the row stride")
-    if y is None:
-        y = torch.empty_like(x)
+    y = _rows_like(x) if y is None else y
+    _same_rows(y, x, "y")
     if r_out is None and want_r_out:
-        r_out = torch.empty_like(x)
+        r_out = _rows_like(x)
+    if r_out is not None:
+        _same_rows(r_out, x, "r_out")
     rc = lib().tbik_rmsnorm_residual_ex(_ptr(x), _ptr(r), _ptr(w), _ptr(y), _ptr(r_out), rows, H,
                                         ld, float(eps), ROUNDING[rounding], _stream())
     _chk(rc, "tbik_rmsnorm_residual")
@@ -300,8 +319,8 @@ def tbik_rope(x, pos, cos_tab, sin_tab, y=None, rounding="once"):
     T, heads, d = x.shape
     if x.stride(2) != 1 or x.stride(1) != d:
         raise ValueError("heads must be contiguous with stride head_dim")
-    if y is None:
-        y = torch.empty_like(x)
+    y = _rows_like(x) if y is None else y
+    _same_rows(y, x, "y")
     rc = lib().tbik_rope_ex(_ptr(x), _ptr(y), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T, heads,
                             d, x.stride(0), cos_tab.shape[0], ROUNDING[rounding], _stream())
     _chk(rc, "tbik_rope")
@@ -485,8 +504,8 @@ def tbik_rope_backward(dy, pos, cos_tab, sin_tab, dx=None):
     T, heads, d = dy.shape
     if dy.stride(2) != 1 or dy.stride(1) != d:
         raise ValueError("heads must be contiguous with stride head_dim")
-    if dx is None:
-        dx = torch.empty_like(dy)
+    dx = _rows_like(dy) if dx is None else dx
+    _same_rows(dx, dy, "dx")
     rc = lib().tbik_rope_backward(_ptr(dy), _ptr(dx), _ptr(pos), _ptr(cos_tab), _ptr(sin_tab), T,
                                   heads, d, dy.stride(0), cos_tab.shape[0], _stream())
     _chk(rc, "tbik_rope_backward")
@@ -514,7 +533,7 @@ def tbik_rmsnorm_backward(x, r, w, dy, dr=None, eps=1e-6, dp=1, want_dw=True):
     for t in (r, dy) + ((dr,) if dr is not None else ()):
         if _ld(t) != ld:
             raise ValueError("x, r, dy and dr must share the row stride")
-    dh = torch.empty_like(x)
+    dh = _rows_like(x)
     dw = torch.empty((H,), dtype=torch.float32, device=x.device) if want_dw else None
     need = lib().tbik_rmsnorm_backward_workspace_bytes(rows, H, dp, int(want_dw))
     ws = torch.empty((max(1, need // 4),), dtype=torch.float32, device=x.device)

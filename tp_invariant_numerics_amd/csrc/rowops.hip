@@ -82,9 +82,14 @@ __device__ __forceinline__ void vstore(V *p, V v) {
   else *p = v;
 }
 
-template <int CH, bool NT = false>
+// AL = false: element-wise accesses, for rows whose starts are not aligned
+// to the vector width; the chunk (and so the tree) is the same either way.
+template <int CH, bool NT = false, bool AL = true>
 __device__ __forceinline__ void load_bf16(float (&v)[CH], const uint16_t *p) {
-  if constexpr (CH >= 8) {
+  if constexpr (!AL) {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) v[e] = bf2f(p[e]);
+  } else if constexpr (CH >= 8) {
 #pragma unroll
     for (int q = 0; q < CH / 8; ++q) {
       const u32x4 u = vload<NT>(reinterpret_cast<const u32x4 *>(p + 8 * q));
@@ -104,9 +109,12 @@ __device__ __forceinline__ void load_bf16(float (&v)[CH], const uint16_t *p) {
   }
 }
 
-template <int CH, bool NT = false>
+template <int CH, bool NT = false, bool AL = true>
 __device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[CH]) {
-  if constexpr (CH >= 8) {
+  if constexpr (!AL) {
+#pragma unroll
+    for (int e = 0; e < CH; ++e) p[e] = f2bf(v[e]);
+  } else if constexpr (CH >= 8) {
 #pragma unroll
     for (int q = 0; q < CH / 8; ++q) {
       u32x4 u;
@@ -125,9 +133,9 @@ __device__ __forceinline__ void store_bf16(uint16_t *p, const float (&v)[CH]) {
   }
 }
 
-template <int CH, bool NT = false>
+template <int CH, bool NT = false, bool AL = true>
 __device__ __forceinline__ void load_f32(float (&v)[CH], const float *p) {
-  if constexpr (CH >= 4) {
+  if constexpr (AL && CH >= 4) {
 #pragma unroll
     for (int q = 0; q < CH / 4; ++q) {
       const f32x4 u = vload<NT>(reinterpret_cast<const f32x4 *>(p + 4 * q));
@@ -157,20 +165,16 @@ static int elem_align(const void *p, int64_t ld, int elem) {
   return a;
 }
 
-// Chunk width for bf16 rows: 16/8-wide chunks use 16-byte accesses (row
-// starts 8-element aligned), 4-wide use 8-byte accesses.  The tree does not
-// depend on the chunk width, only on which chunk sizes divide the group.
-static int cap_bf16(int ch, int align) {
-  if (ch >= 8 && align < 8) ch = align >= 4 ? 4 : 2;
-  if (ch == 4 && align < 4) ch = 2;
-  return ch;
+// Element alignment that vector accesses of a CH-wide chunk need: 16-byte
+// accesses for 8 or more bf16 (4 or more fp32), 8-byte for 4 bf16; narrower
+// chunks are accessed element by element.  Rows aligned below that take the
+// element-wise instance of the same kernel: the chunk width (and with it the
+// tree, the LDS staging and the set of accepted shapes) depends only on the
+// shape, never on alignment.
+static bool bf16_vec_ok(int ch, int align) {
+  return ch < 4 || align >= (ch >= 8 ? 8 : 4);
 }
-
-// Chunk width for fp32 rows: >= 4 uses 16-byte accesses.
-static int cap_f32(int ch, int align) {
-  if (ch >= 4 && align < 4) ch = 2;
-  return ch;
-}
+static bool f32_vec_ok(int ch, int align) { return ch < 4 || align >= 4; }
 
 // =============================================================================
 // residual-add + RMSNorm: one workgroup per row.
@@ -179,7 +183,7 @@ constexpr int kRowThreads = 256;
 
 // EACH (the misaligned rounding location): h = bf16(x + r) before the norm
 // and n = bf16(h * rstd) before the weight, as eager bf16 arithmetic does.
-template <int CH, bool EACH>
+template <int CH, bool EACH, bool AL>
 __global__ void __launch_bounds__(kRowThreads)
 k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, uint16_t *r_out,
           int H, int64_t ld, float eps, int T) {
@@ -191,15 +195,15 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
   const uint16_t *rr = r + base;
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float a[CH], b[CH], sq[CH];
-    load_bf16<CH>(a, xr + ch * CH);
-    load_bf16<CH>(b, rr + ch * CH);
+    load_bf16<CH, false, AL>(a, xr + ch * CH);
+    load_bf16<CH, false, AL>(b, rr + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       a[e] = a[e] + b[e];          // h
       if (EACH) a[e] = bf_round(a[e]);
       sq[e] = a[e] * a[e];
     }
-    if (r_out) store_bf16<CH>(r_out + base + ch * CH, a);
+    if (r_out) store_bf16<CH, false, AL>(r_out + base + ch * CH, a);
     lds[ch] = chunk_tree<CH>(sq);
   }
   __syncthreads();
@@ -208,9 +212,9 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
   const float rstd = 1.0f / __builtin_sqrtf(mean + eps);
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float a[CH], b[CH], ww[CH];
-    load_bf16<CH>(a, xr + ch * CH);
-    load_bf16<CH>(b, rr + ch * CH);
-    load_bf16<CH>(ww, w + ch * CH);
+    load_bf16<CH, false, AL>(a, xr + ch * CH);
+    load_bf16<CH, false, AL>(b, rr + ch * CH);
+    load_bf16<CH, false, AL>(ww, w + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       float h = a[e] + b[e];
@@ -219,7 +223,7 @@ k_rmsnorm(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y, 
       if (EACH) n = bf_round(n);
       a[e] = n * ww[e];
     }
-    store_bf16<CH>(y + base + ch * CH, a);
+    store_bf16<CH, false, AL>(y + base + ch * CH, a);
   }
 }
 
@@ -356,12 +360,13 @@ static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t
   al = al < elem_align(y, ld, 2) ? al : elem_align(y, ld, 2);
   al = al < elem_align(w, 16, 2) ? al : elem_align(w, 16, 2);
   if (r_out) al = al < elem_align(r_out, ld, 2) ? al : elem_align(r_out, ld, 2);
-  const int ch = cap_bf16(chunk_for(H / T), al);
+  const int ch = chunk_for(H / T);
+  const bool vec = bf16_vec_ok(ch, al);
   const int nch = H / ch;
   if (nch > 8192) return TBIK_ERR_SHAPE;
   const int gc = nch / T;
   dim3 grid((unsigned)rows), block(kRowThreads);
-  if (TBIK_RMS_PAIR && ch == 16 && H % (8 * kRowThreads) == 0 && (gc & (gc - 1)) == 0 &&
+  if (vec && TBIK_RMS_PAIR && ch == 16 && H % (8 * kRowThreads) == 0 && (gc & (gc - 1)) == 0 &&
       gc <= 32) {
     switch (H / (8 * kRowThreads)) {
       case 1: hipLaunchKernelGGL((k_rmsnorm_pair<1, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); return check_launch();
@@ -369,7 +374,7 @@ static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t
       default: break;
     }
   }
-  if (nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
+  if (vec && nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
     switch (ch) {
       case 16: hipLaunchKernelGGL((k_rmsnorm_reg<16, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
       case 8: hipLaunchKernelGGL((k_rmsnorm_reg<8, EACH>), grid, block, 0, s, x, r, w, y, r_out, H, ld, eps, T, gc); break;
@@ -380,12 +385,16 @@ static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t
     return check_launch();
   }
   const size_t lds = 2 * (size_t)nch * sizeof(float);
-  switch (ch) {
-    case 16: hipLaunchKernelGGL((k_rmsnorm<16, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    case 8: hipLaunchKernelGGL((k_rmsnorm<8, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    case 4: hipLaunchKernelGGL((k_rmsnorm<4, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    case 2: hipLaunchKernelGGL((k_rmsnorm<2, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
-    default: hipLaunchKernelGGL((k_rmsnorm<1, EACH>), grid, block, lds, s, x, r, w, y, r_out, H, ld, eps, T); break;
+  switch (ch * 2 + (vec ? 1 : 0)) {
+#define TBIK_RMS_CASE(CW, VEC)                                                                      \
+  case CW * 2 + VEC:                                                                                \
+    hipLaunchKernelGGL((k_rmsnorm<CW, EACH, VEC != 0>), grid, block, lds, s, x, r, w, y, r_out, H, \
+                       ld, eps, T);                                                              \
+    break;
+    TBIK_RMS_CASE(16, 1) TBIK_RMS_CASE(16, 0) TBIK_RMS_CASE(8, 1) TBIK_RMS_CASE(8, 0)
+    TBIK_RMS_CASE(4, 1) TBIK_RMS_CASE(4, 0) TBIK_RMS_CASE(2, 1) TBIK_RMS_CASE(1, 1)
+#undef TBIK_RMS_CASE
+    default: return TBIK_ERR_SHAPE;
   }
   return check_launch();
 }
@@ -612,7 +621,7 @@ __device__ __forceinline__ void lds_pair_inplace(float *buf, int m, int groups) 
   }
 }
 
-template <int CH>
+template <int CH, bool AL>
 __global__ void __launch_bounds__(kLsmThreads)
 k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V, int T, int tp,
                  float *shard, float *out, const float *pmax, int64_t ld_pmax, int npmax) {
@@ -628,7 +637,7 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
     // produced the logits): the logits are then read once
     for (int b = threadIdx.x; b < npmax; b += kLsmThreads)
       m = __builtin_fmaxf(m, pmax[(int64_t)row * ld_pmax + b]);
-  } else if constexpr (CH >= 4) {
+  } else if constexpr (AL && CH >= 4) {
     // the maximum is order-free: consecutive lanes read consecutive 16 bytes
     for (int i = threadIdx.x; i < nch * (CH / 4); i += kLsmThreads) {
       const f32x4 u = *reinterpret_cast<const f32x4 *>(xr + 4 * i);
@@ -637,7 +646,7 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   } else {
     for (int ch = threadIdx.x; ch < nch; ch += kLsmThreads) {
       float v[CH];
-      load_f32<CH>(v, xr + ch * CH);
+      load_f32<CH, false, AL>(v, xr + ch * CH);
 #pragma unroll
       for (int e = 0; e < CH; ++e) m = __builtin_fmaxf(m, v[e]);
     }
@@ -649,7 +658,7 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   m = red[0];
 #pragma unroll
   for (int q = 1; q < kLsmThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
-  if constexpr (CH == 16 && TBIK_LSM_QUAD) {
+  if constexpr (AL && CH == 16 && TBIK_LSM_QUAD) {
     // A chunk is read by a quad of lanes, lane j of the quad holding its
     // elements 4j..4j+3, so every load instruction of a wave covers 1 KB
     // contiguously.  Each lane reduces its four values (the chunk tree's
@@ -688,7 +697,7 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   } else {
     for (int ch = nch - 1 - (int)threadIdx.x; ch >= 0; ch -= kLsmThreads) {
       float v[CH];
-      load_f32<CH>(v, xr + ch * CH);
+      load_f32<CH, false, AL>(v, xr + ch * CH);
 #pragma unroll
       for (int e = 0; e < CH; ++e) v[e] = exp_f32(v[e] - m);
       lds[ch] = chunk_tree<CH>(v);
@@ -723,7 +732,8 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
   if (M == 0) return TBIK_OK;
   const int T = tree_T(V);
   const int G = V / T;
-  const int ch = cap_f32(chunk_for(G), elem_align(logits, ld, 4));
+  const int ch = chunk_for(G);
+  const bool vec = f32_vec_ok(ch, elem_align(logits, ld, 4));
   const int nch = V / ch;
   size_t lds = (size_t)nch * sizeof(float);
   // one float per chunk in dynamic LDS, beside the kernel's static per-wave
@@ -732,20 +742,17 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
   if (lds < (size_t)TBIK_LSM_LDS_MIN) lds = TBIK_LSM_LDS_MIN;
   float *shard = ws;
   dim3 grid((unsigned)M), block(kLsmThreads);
-  switch (ch) {
-#define TBIK_LSM_CASE(C)                                                                       \
-  case C:                                                                                      \
+  switch (ch * 2 + (vec ? 1 : 0)) {
+#define TBIK_LSM_CASE(CW, VEC)                                                                    \
+  case CW * 2 + VEC:                                                                              \
     if (lds > 64 * 1024)                                                                       \
-      (void)hipFuncSetAttribute((const void *)k_logsoftmax_row<C>,                             \
+      (void)hipFuncSetAttribute((const void *)k_logsoftmax_row<CW, VEC != 0>,                     \
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);               \
-    hipLaunchKernelGGL(k_logsoftmax_row<C>, grid, block, lds, s, logits, ld, targets, V, T, tp, \
-                       shard, out, pmax, ld_pmax, npmax);                                      \
+    hipLaunchKernelGGL((k_logsoftmax_row<CW, VEC != 0>), grid, block, lds, s, logits, ld, targets, \
+                       V, T, tp, shard, out, pmax, ld_pmax, npmax);                            \
     break;
-    TBIK_LSM_CASE(16)
-    TBIK_LSM_CASE(8)
-    TBIK_LSM_CASE(4)
-    TBIK_LSM_CASE(2)
-    TBIK_LSM_CASE(1)
+    TBIK_LSM_CASE(16, 1) TBIK_LSM_CASE(16, 0) TBIK_LSM_CASE(8, 1) TBIK_LSM_CASE(8, 0)
+    TBIK_LSM_CASE(4, 1) TBIK_LSM_CASE(4, 0) TBIK_LSM_CASE(2, 1) TBIK_LSM_CASE(1, 1)
 #undef TBIK_LSM_CASE
     default: return TBIK_ERR_SHAPE;
   }
@@ -755,7 +762,7 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
 // =============================================================================
 // causal softmax: one workgroup per (batch, query row).
 // =============================================================================
-template <int CH>
+template <int CH, bool AL>
 __global__ void __launch_bounds__(kRowThreads)
 k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, int64_t ld_p,
                  int64_t stride_p, int Lq, int Lk, int offset, float scale, int T) {
@@ -770,7 +777,7 @@ k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, in
   float m = -__builtin_inff();
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float v[CH];
-    load_f32<CH>(v, srow + ch * CH);
+    load_f32<CH, false, AL>(v, srow + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       const float z = v[e] * scale;
@@ -786,7 +793,7 @@ k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, in
   for (int q = 1; q < kRowThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float v[CH];
-    load_f32<CH>(v, srow + ch * CH);
+    load_f32<CH, false, AL>(v, srow + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) v[e] = (ch * CH + e <= last) ? exp_f32(v[e] * scale - m) : 0.0f;
     lds[ch] = chunk_tree<CH>(v);
@@ -795,11 +802,11 @@ k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, in
   const float ssum = lds_row_tree<kRowThreads>(lds, lds + nch, gc, T);
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float v[CH];
-    load_f32<CH>(v, srow + ch * CH);
+    load_f32<CH, false, AL>(v, srow + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e)
       v[e] = (ch * CH + e <= last) ? exp_f32(v[e] * scale - m) / ssum : 0.0f;
-    store_bf16<CH>(prow + ch * CH, v);
+    store_bf16<CH, false, AL>(prow + ch * CH, v);
   }
 }
 
@@ -871,22 +878,25 @@ int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16
   }
   int ch = chunk_for(Lk / T);
   if (ch > 8) ch = 8;
-  ch = cap_f32(ch, elem_align(S, ld_s, 4) < elem_align(S, stride_s, 4) ? elem_align(S, ld_s, 4)
-                                                                       : elem_align(S, stride_s, 4));
-  {
-    const int ap = elem_align(P, ld_p, 2) < elem_align(P, stride_p, 2) ? elem_align(P, ld_p, 2)
-                                                                       : elem_align(P, stride_p, 2);
-    ch = cap_bf16(ch, ap);
-  }
+  const int as = elem_align(S, ld_s, 4) < elem_align(S, stride_s, 4) ? elem_align(S, ld_s, 4)
+                                                                     : elem_align(S, stride_s, 4);
+  const int ap = elem_align(P, ld_p, 2) < elem_align(P, stride_p, 2) ? elem_align(P, ld_p, 2)
+                                                                     : elem_align(P, stride_p, 2);
+  const bool vec = f32_vec_ok(ch, as) && bf16_vec_ok(ch, ap);
   const int nch = Lk / ch;
   if (nch > 8192) return TBIK_ERR_SHAPE;
   const size_t lds = 2 * (size_t)nch * sizeof(float);
   dim3 grid((unsigned)Lq, (unsigned)batch), block(kRowThreads);
-  switch (ch) {
-    case 8: hipLaunchKernelGGL(k_softmax_causal<8>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
-    case 4: hipLaunchKernelGGL(k_softmax_causal<4>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
-    case 2: hipLaunchKernelGGL(k_softmax_causal<2>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
-    default: hipLaunchKernelGGL(k_softmax_causal<1>, grid, block, lds, s, S, ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T); break;
+  switch (ch * 2 + (vec ? 1 : 0)) {
+#define TBIK_SMC_CASE(CW, VEC)                                                                    \
+  case CW * 2 + VEC:                                                                              \
+    hipLaunchKernelGGL((k_softmax_causal<CW, VEC != 0>), grid, block, lds, s, S, ld_s, stride_s, P, \
+                       ld_p, stride_p, Lq, Lk, offset, scale, T);                              \
+    break;
+    TBIK_SMC_CASE(8, 1) TBIK_SMC_CASE(8, 0) TBIK_SMC_CASE(4, 1) TBIK_SMC_CASE(4, 0)
+    TBIK_SMC_CASE(2, 1) TBIK_SMC_CASE(1, 1)
+#undef TBIK_SMC_CASE
+    default: return TBIK_ERR_SHAPE;
   }
   return check_launch();
 }
@@ -1028,7 +1038,7 @@ int launch_swiglu_backward(const uint16_t *g, const uint16_t *u, const uint16_t 
 // tree (same chunks, same LDS tree, same bits), dot = TREE(g*h) with
 // g = dy*w, c = (dot * ((rstd*rstd)*rstd)) / H, dh = bf16(((rstd*g) - (c*h)) + dr).
 // rstd of the row goes to rstd_out for the weight gradient.
-template <int CH>
+template <int CH, bool AL>
 __global__ void __launch_bounds__(kRowThreads)
 k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uint16_t *dy,
               const uint16_t *dr, uint16_t *dh, float *rstd_out, int H, int64_t ld, float eps,
@@ -1039,8 +1049,8 @@ k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uin
   const int64_t base = (int64_t)blockIdx.x * ld;
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float a[CH], b[CH];
-    load_bf16<CH>(a, x + base + ch * CH);
-    load_bf16<CH>(b, r + base + ch * CH);
+    load_bf16<CH, false, AL>(a, x + base + ch * CH);
+    load_bf16<CH, false, AL>(b, r + base + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       a[e] = a[e] + b[e];
@@ -1054,10 +1064,10 @@ k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uin
   __syncthreads();                       // every thread has read the root
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float a[CH], b[CH], gy[CH], ww[CH];
-    load_bf16<CH>(a, x + base + ch * CH);
-    load_bf16<CH>(b, r + base + ch * CH);
-    load_bf16<CH>(gy, dy + base + ch * CH);
-    load_bf16<CH>(ww, w + ch * CH);
+    load_bf16<CH, false, AL>(a, x + base + ch * CH);
+    load_bf16<CH, false, AL>(b, r + base + ch * CH);
+    load_bf16<CH, false, AL>(gy, dy + base + ch * CH);
+    load_bf16<CH, false, AL>(ww, w + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) a[e] = (gy[e] * ww[e]) * (a[e] + b[e]);
     lds[ch] = chunk_tree<CH>(a);
@@ -1067,11 +1077,11 @@ k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uin
   const float c = (dot * ((rstd * rstd) * rstd)) / (float)H;
   for (int ch = threadIdx.x; ch < nch; ch += kRowThreads) {
     float a[CH], b[CH], gy[CH], ww[CH], gr[CH];
-    load_bf16<CH>(a, x + base + ch * CH);
-    load_bf16<CH>(b, r + base + ch * CH);
-    load_bf16<CH>(gy, dy + base + ch * CH);
-    load_bf16<CH>(ww, w + ch * CH);
-    if (dr) load_bf16<CH>(gr, dr + base + ch * CH);
+    load_bf16<CH, false, AL>(a, x + base + ch * CH);
+    load_bf16<CH, false, AL>(b, r + base + ch * CH);
+    load_bf16<CH, false, AL>(gy, dy + base + ch * CH);
+    load_bf16<CH, false, AL>(ww, w + ch * CH);
+    if (dr) load_bf16<CH, false, AL>(gr, dr + base + ch * CH);
 #pragma unroll
     for (int e = 0; e < CH; ++e) {
       const float h = a[e] + b[e];
@@ -1079,7 +1089,7 @@ k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uin
       if (dr) v = v + gr[e];
       a[e] = v;
     }
-    store_bf16<CH>(dh + base + ch * CH, a);
+    store_bf16<CH, false, AL>(dh + base + ch * CH, a);
   }
   if (threadIdx.x == 0) rstd_out[blockIdx.x] = rstd;
 }
@@ -1260,14 +1270,15 @@ int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t
   al = al < elem_align(dh, ld, 2) ? al : elem_align(dh, ld, 2);
   al = al < elem_align(w, 16, 2) ? al : elem_align(w, 16, 2);
   if (dr) al = al < elem_align(dr, ld, 2) ? al : elem_align(dr, ld, 2);
-  const int ch = cap_bf16(chunk_for(H / T), al);
+  const int ch = chunk_for(H / T);
+  const bool vec = bf16_vec_ok(ch, al);
   const int nch = H / ch;
   if (nch > 8192) return TBIK_ERR_SHAPE;
   const size_t lds = 2 * (size_t)nch * sizeof(float);
   float *rstd = ws;                                 // [rows]
   const dim3 grid((unsigned)rows), block(kRowThreads);
   const int gc = nch / T;
-  if (nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
+  if (vec && nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
     switch (ch) {
       case 16: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<16>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
       case 8: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<8>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
@@ -1275,21 +1286,25 @@ int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t
       case 2: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<2>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
       default: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<1>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
     }
-  } else switch (ch) {
-    case 16: hipLaunchKernelGGL(k_rmsnorm_bwd<16>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
-    case 8: hipLaunchKernelGGL(k_rmsnorm_bwd<8>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
-    case 4: hipLaunchKernelGGL(k_rmsnorm_bwd<4>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
-    case 2: hipLaunchKernelGGL(k_rmsnorm_bwd<2>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
-    default: hipLaunchKernelGGL(k_rmsnorm_bwd<1>, grid, block, lds, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T); break;
+  } else switch (ch * 2 + (vec ? 1 : 0)) {
+#define TBIK_RMSB_CASE(CW, VEC)                                                                   \
+  case CW * 2 + VEC:                                                                              \
+    hipLaunchKernelGGL((k_rmsnorm_bwd<CW, VEC != 0>), grid, block, lds, s, x, r, w, dy, dr, dh,     \
+                       rstd, H, ld, eps, T);                                                   \
+    break;
+    TBIK_RMSB_CASE(16, 1) TBIK_RMSB_CASE(16, 0) TBIK_RMSB_CASE(8, 1) TBIK_RMSB_CASE(8, 0)
+    TBIK_RMSB_CASE(4, 1) TBIK_RMSB_CASE(4, 0) TBIK_RMSB_CASE(2, 1) TBIK_RMSB_CASE(1, 1)
+#undef TBIK_RMSB_CASE
+    default: return TBIK_ERR_SHAPE;
   }
   int rc = check_launch();
   if (rc != TBIK_OK || !dw) return rc;
   const int nleaf = rows / 64;
   float *leaves = ws + rmsnorm_bwd_rstd_floats(rows);
   float *shards = leaves + (int64_t)nleaf * H;
-  const bool vec = (H % 2) == 0 && elem_align(x, ld, 2) >= 2 && elem_align(r, ld, 2) >= 2 &&
-                   elem_align(dy, ld, 2) >= 2;
-  if (vec)
+  const bool pairs = (H % 2) == 0 && elem_align(x, ld, 2) >= 2 && elem_align(r, ld, 2) >= 2 &&
+                     elem_align(dy, ld, 2) >= 2;
+  if (pairs)
     hipLaunchKernelGGL(k_rmsnorm_dw_leaves<2>, dim3((unsigned)((H / 2 + 255) / 256), (unsigned)nleaf),
                        dim3(256), 0, s, x, r, dy, rstd, leaves, H, ld);
   else
