@@ -1,25 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the tree-based invariant kernels on one MI355X.
 
-Headline step (the row-parallel down-projection workload): one pass of the
-simulated tensor-parallel GEMM over a batch of M=256 tokens,
-A [256, 14336] bf16 ~N(0,1), W [4096, 14336] bf16 ~N(0,0.02), K split into
-tp=8 shards: the shard-partials kernel (64-wide K-block MFMA leaves + the
-in-register tree) writes 8 fp32 partials, the combine kernel runs the top
-of the tree.  value = 2*M*N*K / step time (TFLOP/s).  Inputs are resident in
-HBM; W rotates over several copies so every step streams W from HBM rather
-than from the 256 MB last-level cache.
+Headline step (the LM-head logprob workload): one pass of the logprob path
+over a batch of M = 512 tokens -- the LM-head GEMM A [512, 4096] x
+W [151936, 4096]^T (bf16, A ~N(0,1), W ~N(0,0.02); 64-wide K-block MFMA
+leaves and the fixed fp32 tree; exact row maxima of each 64-column block in
+its epilogue), then the tree log-softmax over the vocabulary as tp = 4
+simulated vocabulary shards and the gather of the uniform random targets'
+log-probabilities.  value = 2*M*V*K / step time (TFLOP/s of the invariant
+GEMM, the log-softmax's time included).  Inputs are resident in HBM; W
+(1.24 GB) is far larger than the 256 MB last-level cache.
 
-Also reported: the same GEMM at tp=1 for M in {1,32,256} against torch's
-bf16 GEMM (hipBLASLt) -- the non-invariant baseline and overhead; a
-compute-bound M=4096 prefill and the LM-head GEMM (M=512, K=4096,
-N=151936) as % of the bf16 MFMA peak; the row kernels as % of HBM
-bandwidth; the bitwise mismatch count across tp and M; and the CPU oracle
-timed on a bounded sample.
+The roofline object is for the dominant kernel, the LM-head GEMM (bound by
+the matrix cores: 408 FLOP/B against a ridge of 312), timed back to back
+with HIP events on its launch stream; hipBLASLt (torch's bf16 GEMM with an
+fp32 output) on the same shape gives the non-invariant baseline and the
+overhead.  Also reported: bitwise mismatches across tp and batch size,
+SHA-256 fingerprints of the inputs and outputs, the library's own ceiling
+microbenchmarks, the other workloads (down projection at simulated tp = 8
+and tp = 1, prefill, row kernels, decoder, training side), and the CPU
+oracle timed on bounded samples of every workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
+       python bench.py --profile-gemm      (LM-head GEMM launches only, for rocprofv3)
 """
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -29,20 +35,25 @@ import time
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 METRIC = "invariant GEMM TFLOP/s (% MFMA peak, overhead vs hipBLASLt); 0 bit mismatches"
+M_HEAD, K_HEAD, V_HEAD, TP_HEAD = 512, 4096, 151936, 4
 
-# The headline's shard-partials kernel, as named in a rocprofv3 kernel trace.
-HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 28, 0, 0, 1, 1, 2>"
+# The headline's LM-head GEMM kernel, as named in a rocprofv3 kernel trace.
+HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs (profiles/
+# k_gemm_ring_lmhead_M512_K4096_N151936.md): FETCH_SIZE x its copy factor +
+# WRITE_SIZE x its copy factor, the factors being what a plain 1 GiB device
+# copy reads on the same counters.  Valid only for the GEMM sources the
+# counters were taken on (hash below); None until measured.
+HEAD_TRAFFIC_BYTES = None
+HEAD_TRAFFIC_SRC_SHA256 = None
+# The same for the down projection's tp = 8 shard-partials kernel (profiles/
 # k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64818 KiB x 2.000
-# + WRITE_SIZE 32768 KiB x 1.000, the factors being what a plain 1 GiB device
-# copy reads on the same counters (524303 KiB fetched, 1048576 KiB written).
-# Valid only for the GEMM sources the counters were taken on (hash below).
-HEAD_TRAFFIC_BYTES = (64818 * 2 + 32768) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "b368286dba4f51fbc852b85d1d79d7ec4104168481bb3a3d0859460c35544994"
+# + WRITE_SIZE 32768 KiB x 1.000.
+HEAD_TP8_TRAFFIC_BYTES = (64818 * 2 + 32768) * 1024
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "b368286dba4f51fbc852b85d1d79d7ec4104168481bb3a3d0859460c35544994"
 
 
 def gemm_source_sha256(root):
-    import hashlib
     h = hashlib.sha256()
     for f in ("gemm.hip", "tbik_device.h", "tbik_internal.h"):
         with open(os.path.join(root, "tp_invariant_numerics_amd", "csrc", f), "rb") as fh:
@@ -50,17 +61,27 @@ def gemm_source_sha256(root):
     return h.hexdigest()
 
 
+def sha256_of(*ts):
+    """SHA-256 of the bytes of device or host tensors (the inputs' and
+    outputs' fingerprints)."""
+    import torch
+    h = hashlib.sha256()
+    for t in ts:
+        h.update(t.detach().contiguous().view(-1).view(torch.uint8).cpu().numpy().tobytes())
+    return h.hexdigest()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=100)
-    ap.add_argument("--M", type=int, default=256)
-    ap.add_argument("--tp", type=int, default=8)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline step only")
-    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--pmc-calib", action="store_true",
                     help="run only a plain device copy of known size (counter calibration)")
+    ap.add_argument("--profile-gemm", action="store_true",
+                    help="run only launches of the headline LM-head GEMM (profiling)")
     ap.add_argument("--only", default="", help="run only one extra workload (profiling)")
     return ap.parse_args()
 
@@ -130,140 +151,134 @@ def main():
         return total / iters
 
     # ------------------------------------------------------------------ headline
-    M, K, N, tp = args.M, 14336, 4096, args.tp
-    w_bytes = N * K * 2
-    n_rot = max(2, -(-600_000_000 // w_bytes))       # > 2x the 256 MB last-level cache
-    log("inputs: A [%d,%d], W [%d,%d] x%d rotating copies, tp=%d" % (M, K, N, K, n_rot, tp))
+    M, K, V, tp = M_HEAD, K_HEAD, V_HEAD, TP_HEAD
+    log("inputs: A [%d,%d], W [%d,%d], targets [%d], tp=%d" % (M, K, V, K, M, tp))
     A = inputs.normal_bf16((M, K), 1001, device=dev)
-    Ws = [inputs.normal_bf16((N, K), 2001 + i, std=0.02, device=dev) for i in range(n_rot)]
-    ws = torch.empty((tp, M, N), dtype=torch.float32, device=dev)
-    C = torch.empty((M, N), dtype=torch.float32, device=dev)
-    flops = 2.0 * M * N * K
+    W = inputs.normal_bf16((V, K), 1002, std=0.02, device=dev)
+    tgt = inputs.uniform_int(M, V, 1003, device=dev)
+    logits = torch.empty((M, V), dtype=torch.float32, device=dev)
+    pm = torch.empty((M, (V + 63) // 64), dtype=torch.float32, device=dev)
+    lp = torch.empty((M,), dtype=torch.float32, device=dev)
+    lws = torch.empty((tb.tbik_logsoftmax_workspace_bytes(M, V, tp) // 4 + 1,),
+                      dtype=torch.float32, device=dev)
+    flops = 2.0 * M * V * K
 
-    # One step = the library's simulated-TP call: the shard-partials kernel
-    # writes the tp fp32 partials into ws, the combine kernel runs the top
-    # of the tree into C.  The K timed steps are bracketed by one event pair
-    # and the wall clock; per-kernel events inside the loop would add their
-    # own dispatch gaps to the step.
-    def step(i):
-        tb.tbik_gemm_tpsim(A, Ws[i % n_rot], tp, ws=ws, out=C)
+    def gemm():
+        tb.tbik_gemm_logits(A, W, out=logits, pmax=pm)
 
-    for i in range(args.warmup):
-        step(i)
+    if args.profile_gemm:
+        for _ in range(max(3, args.steps)):
+            gemm()
+        torch.cuda.synchronize()
+        log("profile-gemm: %d launches of the LM-head GEMM" % max(3, args.steps))
+        return
+
+    # One step = the config's logprob path: the LM-head GEMM with its fused
+    # row maxima, then the log-softmax + gather (one read of the logits).
+    # The K timed steps are bracketed by one event pair and the wall clock.
+    def step():
+        gemm()
+        tb.tbik_logsoftmax_gather_pmax(logits, tgt, pm, tp, ws=lws, out=lp)
+
+    for _ in range(args.warmup):
+        step()
     torch.cuda.synchronize()
     e_start = torch.cuda.Event(enable_timing=True)
     e_end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e_start.record(stream)
-    for i in range(args.steps):
-        step(i)
+    for _ in range(args.steps):
+        step()
     e_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     step_ms = e_start.elapsed_time(e_end) / args.steps
     ms_per_step = max(step_ms, wall * 1e3 / args.steps)
     value = flops / (ms_per_step * 1e-3) / 1e12
-    log("step %.4f ms (events), wall %.4f ms/step" % (step_ms, wall * 1e3 / args.steps))
+    log("step %.4f ms (events), wall %.4f ms/step: %.1f TFLOP/s"
+        % (step_ms, wall * 1e3 / args.steps, value))
 
-    # The same step split into its two kernels, in a separately instrumented
-    # pass (an event between the kernels adds a dispatch gap, so the split
-    # sums to more than the step).
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
-        rec = ev[i]
-        rec[0].record(stream)
-        tb.tbik_gemm_tp_partials(A, Ws[i % n_rot], tp, ws=ws)
-        rec[1].record(stream)
-        tb.tbik_tree_combine(ws, out=C)
-        rec[2].record(stream)
+    # the dominant kernel alone: back-to-back launches between two HIP
+    # events on the launch stream
+    kern_ms = timed(gemm, max(10, args.steps), warm=2)
+    lsm_ms = timed(lambda: tb.tbik_logsoftmax_gather_pmax(logits, tgt, pm, tp, ws=lws, out=lp),
+                   max(10, args.steps))
+    log("LM-head GEMM %.4f ms per launch; log-softmax %.4f ms" % (kern_ms, lsm_ms))
+    achieved = flops / (kern_ms * 1e-3) / 1e12
+    gemm_bytes = M * K * 2 + V * K * 2 + M * V * 4 + M * ((V + 63) // 64) * 4
+    traffic = HEAD_TRAFFIC_BYTES if (HEAD_TRAFFIC_SRC_SHA256 is not None and
+                                     gemm_source_sha256(root) == HEAD_TRAFFIC_SRC_SHA256) else None
+    roofline = {"kernel": HEAD_KERNEL + " (LM-head GEMM with fused 64-column row maxima)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic, "algorithmic_flops_per_launch": flops,
+                "algorithmic_bytes_per_launch": gemm_bytes,
+                "arith_intensity_flop_per_byte": round(flops / gemm_bytes, 1),
+                "avg_launch_ms": round(kern_ms, 5)}
+    lsm_bytes = M * V * 4
+    secondary = {"kernel": "k_logsoftmax_row (tree log-softmax + gather, tp=%d, row maxima "
+                           "from the GEMM)" % tp, "bound": "hbm",
+                 "achieved": round(lsm_bytes / lsm_ms / 1e6, 1), "peak": PEAK_HBM_GBS,
+                 "unit": "GB/s", "frac": round(lsm_bytes / lsm_ms / 1e6 / PEAK_HBM_GBS, 4),
+                 "algorithmic_bytes_per_launch": lsm_bytes, "avg_launch_ms": round(lsm_ms, 5)}
+
+    # fingerprints of what this run consumed and produced
+    step()
     torch.cuda.synchronize()
-    part_ms = sum(a.elapsed_time(b) for a, b, c in ev) / args.steps
-    comb_ms = sum(b.elapsed_time(c) for a, b, c in ev) / args.steps
-    log("instrumented split: partials %.4f ms, combine %.4f ms" % (part_ms, comb_ms))
+    fingerprints = {"A": sha256_of(A), "W": sha256_of(W), "targets": sha256_of(tgt),
+                    "logits": sha256_of(logits), "row_maxima": sha256_of(pm),
+                    "logprobs": sha256_of(lp)}
+    lp_head = lp.clone()
 
-    # Average duration of the shard-partials kernel: back-to-back launches on
-    # the launch stream between two HIP events (per-kernel events inside a
-    # step add their own dispatch overhead to the interval).
-    nb2b = max(10, args.steps)
-
-    def part_only(i=[0]):
-        i[0] += 1
-        tb.tbik_gemm_tp_partials(A, Ws[i[0] % n_rot], tp, ws=ws)
-
-    kern_ms = timed(part_only, nb2b)
-    log("partials kernel back-to-back: %.4f ms per launch" % kern_ms)
-
-    # roofline of the dominant kernel (the shard-partials GEMM): by arithmetic
-    # intensity 2MNK / bytes = 190 FLOP/B < 2500e12/8e12 = 312 FLOP/B it is
-    # HBM-bound; its MFMA fraction is reported beside it
-    part_bytes = M * K * 2 + N * K * 2 + tp * M * N * 4
-    achieved_gbs = part_bytes / (kern_ms * 1e-3) / 1e9
-    traffic = HEAD_TRAFFIC_BYTES if gemm_source_sha256(root) == HEAD_TRAFFIC_SRC_SHA256 else None
-    roofline = {"kernel": HEAD_KERNEL + " (tp shard partials)", "bound": "hbm",
-                "achieved": round(achieved_gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved_gbs / PEAK_HBM_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": part_bytes,
-                "avg_launch_ms": round(kern_ms, 5),
-                "in_step_event_ms": round(part_ms, 5),
-                "arith_intensity_flop_per_byte": round(flops / part_bytes, 1),
-                "mfma_frac": round(flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-
-    # bitwise invariance over tp and batch size on this workload
+    # bitwise invariance on this workload: tp 1/2/8 logprobs and sub-batches
     mismatches = 0
-    W0 = Ws[0]
-    ref = tb.tbik_gemm(A, W0)[0]
-    for t in (1, 2, 4, 8):
-        Ct = tb.tbik_gemm_tpsim(A, W0, t)[0]
-        mismatches += int((Ct.view(torch.int32) != ref.view(torch.int32)).sum().item())
-    for m in (1, 32, 255):
-        Cm = tb.tbik_gemm(A[:m], W0)[0]
-        mismatches += int((Cm.view(torch.int32) != ref[:m].view(torch.int32)).sum().item())
-    log("bit mismatches across tp {1,2,4,8} and M {1,32,255,256}: %d" % mismatches)
+    checks = 0
+    for t in (1, 2, 8):
+        o, _ = tb.tbik_logsoftmax_gather_pmax(logits, tgt, pm, t)
+        mismatches += int((o.view(torch.int32) != lp_head.view(torch.int32)).sum().item())
+        checks += M
+    for lo, m in ((0, 1), (511, 1), (100, 17), (0, 256)):
+        lg, p2 = tb.tbik_gemm_logits(A[lo:lo + m], W)
+        mismatches += int((lg.view(torch.int32) != logits[lo:lo + m].view(torch.int32)).sum().item())
+        o, _ = tb.tbik_logsoftmax_gather_pmax(lg, tgt[lo:lo + m], p2, tp)
+        mismatches += int((o.view(torch.int32) != lp_head[lo:lo + m].view(torch.int32)).sum()
+                          .item())
+        checks += m * V + m
+        del lg, p2
+    log("bit mismatches across tp {1,2,4,8} and batch {1,17,256,512}: %d of %d" % (mismatches,
+                                                                                   checks))
 
-    # negative control: the same tp split done the usual way -- each shard's
-    # partial from torch's GEMM, the shards summed in rank order -- is not
-    # tp-invariant (why the tree exists); count its mismatches against tp=1
-    naive_mism = {}
-    one = torch.matmul(A, W0.t()).float()
-    for t in (2, 4, 8):
-        ks = K // t
-        acc = None
-        for r in range(t):
-            part = torch.matmul(A[:, r * ks:(r + 1) * ks], W0[:, r * ks:(r + 1) * ks].t()).float()
-            acc = part if acc is None else acc + part
-        naive_mism["tp%d" % t] = int((acc.view(torch.int32) != one.view(torch.int32)).sum().item())
-    del one
-    log("negative control (hipBLASLt per shard + sequential sum vs tp=1): %s" % naive_mism)
-
-    # non-invariant baseline: torch bf16 GEMM (hipBLASLt), same shape
-    rot = {"i": 0}
-
-    def blas_rot():
-        rot["i"] += 1
-        return torch.matmul(A, Ws[rot["i"] % n_rot].t())
-
-    t_blas = timed(blas_rot, args.steps)
-
-    def tbik_tp1_rot():
-        rot["i"] += 1
-        return tb.tbik_gemm(A, Ws[rot["i"] % n_rot], out=C)
-
-    t_tp1 = timed(tbik_tp1_rot, args.steps)
-    hipblaslt = {"what": "torch.matmul bf16 (hipBLASLt), same shape, not tp-invariant",
+    # non-invariant baseline: hipBLASLt through torch (bf16 inputs, fp32 out
+    # when the backend takes it, else bf16 out)
+    blas_out = "fp32"
+    try:
+        torch.mm(A, W.t(), out_dtype=torch.float32)
+        blas = lambda: torch.mm(A, W.t(), out_dtype=torch.float32)  # noqa: E731
+    except Exception:                                                # noqa: BLE001
+        blas_out = "bf16"
+        blas = lambda: torch.matmul(A, W.t())  # noqa: E731
+    t_blas = timed(blas, max(10, args.steps), warm=2)
+    t_blas_bf16 = timed(lambda: torch.matmul(A, W.t()), max(10, args.steps), warm=2)
+    hipblaslt = {"what": "torch bf16 GEMM (hipBLASLt), same shape, %s output, not tp-invariant"
+                         % blas_out,
                  "ms": round(t_blas, 5), "tflops": round(flops / t_blas / 1e9, 1),
-                 "tbik_tp1_ms": round(t_tp1, 5),
-                 "overhead_tp1_pct": round((t_tp1 / t_blas - 1) * 100, 1),
-                 "overhead_tpsim_pct": round((ms_per_step / t_blas - 1) * 100, 1)}
-    log("hipBLASLt %.4f ms; tbik tp=1 %.4f ms; tpsim step %.4f ms" % (t_blas, t_tp1, ms_per_step))
+                 "ms_bf16_out": round(t_blas_bf16, 5),
+                 "tflops_bf16_out": round(flops / t_blas_bf16 / 1e9, 1),
+                 "tbik_gemm_ms": round(kern_ms, 5),
+                 "overhead_gemm_pct": round((kern_ms / t_blas - 1) * 100, 1),
+                 "overhead_step_pct": round((ms_per_step / t_blas - 1) * 100, 1)}
+    log("hipBLASLt %.4f ms (%s out), %.4f ms (bf16 out); tbik GEMM %.4f ms"
+        % (t_blas, blas_out, t_blas_bf16, kern_ms))
+    del logits, pm, lws
 
     extra = {}
     if not args.no_extra:
         extra = run_extra(tb, inputs, torch, np, dev, timed, log, args)
 
     cpu = None
+    cpu_all = None
     if not args.no_cpu:
-        cpu = cpu_baseline(inputs, np, log, A, Ws[0], tp)
+        cpu, cpu_all = cpu_baselines(inputs, np, torch, log, (A, W, tgt, tp))
 
     out = {
         "metric": METRIC,
@@ -278,25 +293,166 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "row-parallel down-proj GEMM, M=%d K=%d N=%d, simulated TP=%d "
-                               "(shard partials + tree combine)" % (M, K, N, tp),
-                   "M": M, "K": K, "N": N, "tp": tp, "rotating_W_copies": n_rot,
-                   "A": "bf16 ~N(0,1)", "W": "bf16 ~N(0,0.02)", "accumulate": "fp32 tree"},
+        "config": {"workload": "LM-head logprob path: M=%d tokens, K=%d, V=%d vocab; bf16 GEMM "
+                               "(64-wide K-block MFMA leaves, fixed fp32 tree, fused 64-column "
+                               "row maxima) + tree log-softmax over tp=%d simulated vocab shards "
+                               "+ target gather" % (M, K, V, tp),
+                   "M": M, "K": K, "V": V, "tp": tp,
+                   "A": "bf16 ~N(0,1)", "W": "bf16 ~N(0,0.02)", "targets": "uniform int32",
+                   "accumulate": "fp32 tree", "output": "fp32 logits + fp32 logprobs"},
         "pct_mfma_peak": round(value / PEAK_BF16_TFLOPS * 100, 2),
         "bit_mismatches": mismatches,
-        "step_split": {"partials_ms": round(part_ms, 5), "combine_ms": round(comb_ms, 5),
-                       "note": "separately instrumented pass with an event between the two "
-                               "kernels; the timed steps carry no events inside"},
-        "negative_control_mismatches": {
-            "what": "torch bf16 GEMM per K shard, shards summed in rank order, vs the "
-                    "unsplit torch GEMM (not tp-invariant); out of %d outputs" % (M * N),
-            **naive_mism},
+        "bit_checks": checks,
+        "step_split": {"gemm_ms": round(kern_ms, 5), "logsoftmax_ms": round(lsm_ms, 5),
+                       "note": "each kernel back to back on its own; the timed steps run them "
+                               "in sequence with no events between"},
         "roofline": roofline,
+        "roofline_logsoftmax": secondary,
         "hipblaslt": hipblaslt,
+        "fingerprints_sha256": fingerprints,
         "cpu_baseline": cpu,
+        "cpu_oracle_configs": cpu_all,
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def downproj_tp8(tb, inputs, torch, dev, timed, log, args):
+    """The row-parallel down projection (M = 256, K = 14336, N = 4096) as
+    simulated tp = 8: the shard-partials kernel writes 8 fp32 partials, the
+    combine runs the top of the tree.  HBM-bound (190 FLOP/B < 312)."""
+    import time as _t
+    M, K, N, tp = 256, 14336, 4096, 8
+    w_bytes = N * K * 2
+    n_rot = max(2, -(-600_000_000 // w_bytes))       # > 2x the 256 MB last-level cache
+    A = inputs.normal_bf16((M, K), 1001, device=dev)
+    Ws = [inputs.normal_bf16((N, K), 2001 + i, std=0.02, device=dev) for i in range(n_rot)]
+    ws = torch.empty((tp, M, N), dtype=torch.float32, device=dev)
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    flops = 2.0 * M * N * K
+    stream = torch.cuda.current_stream()
+    steps = max(50, args.steps)
+
+    def step(i):
+        tb.tbik_gemm_tpsim(A, Ws[i % n_rot], tp, ws=ws, out=C)
+
+    for i in range(10):
+        step(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = _t.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = _t.perf_counter() - t0
+    ms = max(e0.elapsed_time(e1) / steps, wall * 1e3 / steps)
+
+    k = {"i": 0}
+
+    def part_only():
+        k["i"] += 1
+        tb.tbik_gemm_tp_partials(A, Ws[k["i"] % n_rot], tp, ws=ws)
+
+    kern_ms = timed(part_only, steps)
+    part_bytes = M * K * 2 + N * K * 2 + tp * M * N * 4
+    traffic = HEAD_TP8_TRAFFIC_BYTES if gemm_source_sha256(
+        os.path.dirname(os.path.abspath(__file__))) == HEAD_TP8_TRAFFIC_SRC_SHA256 else None
+
+    # bitwise invariance over tp and batch size on this workload
+    mismatches = 0
+    W0 = Ws[0]
+    ref = tb.tbik_gemm(A, W0)[0]
+    for t in (1, 2, 4, 8):
+        Ct = tb.tbik_gemm_tpsim(A, W0, t)[0]
+        mismatches += int((Ct.view(torch.int32) != ref.view(torch.int32)).sum().item())
+    for m in (1, 32, 255):
+        Cm = tb.tbik_gemm(A[:m], W0)[0]
+        mismatches += int((Cm.view(torch.int32) != ref[:m].view(torch.int32)).sum().item())
+    # negative control: each shard's partial from torch's GEMM, the shards
+    # summed in rank order -- not tp-invariant (why the tree exists)
+    naive = {}
+    one = torch.matmul(A, W0.t()).float()
+    for t in (2, 4, 8):
+        ks = K // t
+        acc = None
+        for r in range(t):
+            part = torch.matmul(A[:, r * ks:(r + 1) * ks], W0[:, r * ks:(r + 1) * ks].t()).float()
+            acc = part if acc is None else acc + part
+        naive["tp%d" % t] = int((acc.view(torch.int32) != one.view(torch.int32)).sum().item())
+    rot = {"i": 0}
+
+    def blas_rot():
+        rot["i"] += 1
+        return torch.matmul(A, Ws[rot["i"] % n_rot].t())
+
+    def tp1_rot():
+        rot["i"] += 1
+        return tb.tbik_gemm(A, Ws[rot["i"] % n_rot], out=C)
+
+    t_blas = timed(blas_rot, steps)
+    t_tp1 = timed(tp1_rot, steps)
+    log("down projection tp8: step %.4f ms, partials %.4f ms, hipBLASLt %.4f, tp1 %.4f"
+        % (ms, kern_ms, t_blas, t_tp1))
+    return {"ms_per_step": round(ms, 5), "tflops": round(flops / ms / 1e9, 1),
+            "roofline": {"kernel": "tp shard partials", "bound": "hbm",
+                         "achieved": round(part_bytes / kern_ms / 1e6, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(part_bytes / kern_ms / 1e6 / PEAK_HBM_GBS, 4),
+                         "traffic": traffic, "algorithmic_bytes_per_launch": part_bytes,
+                         "avg_launch_ms": round(kern_ms, 5),
+                         "mfma_frac": round(flops / kern_ms / 1e9 / PEAK_BF16_TFLOPS, 4)},
+            "bit_mismatches_tp_1_2_4_8_M_1_32_255": mismatches,
+            "negative_control_mismatches": dict(naive, of=M * N),
+            "hipblaslt_ms": round(t_blas, 5), "tbik_tp1_ms": round(t_tp1, 5),
+            "overhead_tp1_pct": round((t_tp1 / t_blas - 1) * 100, 1),
+            "overhead_tpsim_pct": round((ms / t_blas - 1) * 100, 1)}
+
+
+def ceilings(tb, inputs, torch, dev, timed, log):
+    """What this GPU sustains, from the library's own microbenchmarks (a
+    pure matrix-core loop of the leaf instruction; non-temporal HBM read and
+    copy streams over buffers of 4 GiB and 2 GiB), beside a large hipBLASLt
+    GEMM for reference."""
+    ceil = {}
+    seed = inputs.normal_bf16((1024,), 3900, device=dev)          # 2 KB of operands
+    blocks, iters = 2048, 1024
+    out = torch.empty((blocks * 512,), dtype=torch.float32, device=dev)
+    fl = {}
+
+    def mf():
+        _, fl["f"] = tb.tbik_bench_mfma(seed, blocks, iters, out=out)
+
+    t = timed(mf, 5, warm=2)
+    ceil["mfma_bf16_loop_tflops"] = round(fl["f"] / t / 1e9, 1)
+    buf = torch.empty((1 << 32,), dtype=torch.uint8, device=dev)    # 4 GiB
+    buf.fill_(7)
+    red = torch.empty((16384 * 256,), dtype=torch.int32, device=dev)
+    src, dst = buf[:1 << 31], buf[1 << 31:]
+    # the best of a few grid sizes (one to eight workgroups of 256 per CU
+    # and more): the ceiling is what the chip can sustain
+    rd, cp = {}, {}
+    for blocks in (1024, 2048, 4096, 8192, 16384):
+        t = timed(lambda: tb.tbik_bench_hbm_read(buf, blocks, out=red), 5, warm=2)
+        rd[blocks] = round((1 << 32) / t / 1e6, 1)
+        t = timed(lambda: tb.tbik_bench_hbm_copy(src, dst, blocks), 5, warm=2)
+        cp[blocks] = round(2 * (1 << 31) / t / 1e6, 1)
+    ceil["hbm_read_4GiB_gbs"] = max(rd.values())
+    ceil["hbm_copy_2GiB_gbs"] = max(cp.values())
+    ceil["hbm_by_grid"] = {"read": rd, "copy_read_plus_write": cp}
+    del buf, src, dst
+    n = 8192
+    a8 = inputs.normal_bf16((n, n), 3901, device=dev)
+    b8 = inputs.normal_bf16((n, n), 3902, device=dev)
+    t = timed(lambda: torch.matmul(a8, b8), 10)
+    ceil["hipblaslt_bf16_8192cubed_tflops"] = round(2.0 * n ** 3 / t / 1e9, 1)
+    del a8, b8
+    ceil["spec"] = {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
+    log("ceilings: MFMA loop %.0f TFLOP/s, HBM read %.0f GB/s, copy %.0f GB/s, hipBLASLt %.0f"
+        % (ceil["mfma_bf16_loop_tflops"], ceil["hbm_read_4GiB_gbs"], ceil["hbm_copy_2GiB_gbs"],
+           ceil["hipblaslt_bf16_8192cubed_tflops"]))
+    return ceil
 
 
 def run_extra(tb, inputs, torch, np, dev, timed, log, args):
@@ -305,6 +461,13 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
 
     def want(name):
         return not only or only == name
+
+    # --- the row-parallel down projection at simulated tp = 8 (M = 256,
+    #     K = 14336, N = 4096): shard partials + tree combine per step, W
+    #     rotating over copies larger than the last-level cache
+    if want("downproj_tp8"):
+        res["downproj_tp8_M256_K14336_N4096"] = downproj_tp8(tb, inputs, torch, dev, timed, log,
+                                                             args)
 
     # --- tp=1 GEMM at the other batch sizes vs hipBLASLt
     if want("gemm_m"):
@@ -349,49 +512,16 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
         log("prefill: %.3f ms = %.1f TFLOP/s (hipBLASLt %.3f ms)" % (t1, fl / t1 / 1e9, t2))
         del A, W, C
 
-    logits = None
-    if want("lmhead") or want("logsoftmax"):
+    if want("logsoftmax"):
+        # the standalone log-softmax (its own exact row maxima: two reads of
+        # the logits) on the LM head's logits
         M, K, V = 512, 4096, 151936
         A = inputs.normal_bf16((M, K), 3300, device=dev)
         W = inputs.normal_bf16((V, K), 3301, std=0.02, device=dev)
-        logits = torch.empty((M, V), dtype=torch.float32, device=dev)
-        pm = torch.empty((M, (V + 63) // 64), dtype=torch.float32, device=dev)
-        if want("lmhead"):
-            # the tree GEMM with and without the fused row maxima back to back,
-            # then hipBLASLt (whose large launches change the clocks seen next)
-            t1 = timed(lambda: tb.tbik_gemm(A, W, out=logits), 8, warm=2)
-            t_fused = timed(lambda: tb.tbik_gemm_logits(A, W, out=logits, pmax=pm), 8, warm=2)
-            t2 = timed(lambda: torch.matmul(A, W.t()), 8, warm=2)
-            fl = 2.0 * M * V * K
-            res["lmhead_M512_K4096_N151936"] = {
-                "ms": round(t1, 4), "tflops": round(fl / t1 / 1e9, 1),
-                "mfma_frac": round(fl / t1 / 1e9 / 2500, 4), "hipblaslt_ms": round(t2, 4),
-                "hipblaslt_tflops": round(fl / t2 / 1e9, 1),
-                "overhead_pct": round((t1 / t2 - 1) * 100, 1)}
-            log("lmhead: %.3f ms = %.1f TFLOP/s (hipBLASLt %.3f ms)" % (t1, fl / t1 / 1e9, t2))
-        else:
-            tb.tbik_gemm(A, W, out=logits)
+        logits = tb.tbik_gemm(A, W)[0]
+        del A, W
         tgt = inputs.uniform_int(M, V, 3302, device=dev)
         nbytes = M * V * 4
-        # logprob path with the row maximum fused into the LM-head GEMM
-        if want("lmhead"):
-            t1 = t_fused
-            res["lmhead_fused_rowmax_M512_K4096_N151936"] = {
-                "ms": round(t1, 4), "tflops": round(2.0 * M * V * K / t1 / 1e9, 1),
-                "note": "tbik_gemm_logits: LM-head GEMM + 64-column row maxima in its epilogue"}
-        else:
-            tb.tbik_gemm_logits(A, W, out=logits, pmax=pm)
-        for tpv in (1, 4):
-            ws = torch.empty((tb.tbik_logsoftmax_workspace_bytes(M, V, tpv) // 4,),
-                             dtype=torch.float32, device=dev)
-            out = torch.empty((M,), dtype=torch.float32, device=dev)
-            t = timed(lambda: tb.tbik_logsoftmax_gather_pmax(logits, tgt, pm, tpv, ws=ws, out=out),
-                      20)
-            res["logsoftmax_fused_max_M512_V151936_tp%d" % tpv] = {
-                "ms": round(t, 5), "gbs": round(nbytes / t / 1e6, 1),
-                "hbm_frac": round(nbytes / t / 1e6 / 8000, 4),
-                "note": "row maxima from the LM-head GEMM epilogue; one read of the fp32 logits"}
-            log("logsoftmax (fused max) tp=%d: %.4f ms = %.0f GB/s" % (tpv, t, nbytes / t / 1e6))
         for tpv in (1, 4):
             ws = torch.empty((tb.tbik_logsoftmax_workspace_bytes(M, V, tpv) // 4,),
                              dtype=torch.float32, device=dev)
@@ -402,7 +532,7 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
                 "hbm_frac": round(nbytes / t / 1e6 / 8000, 4),
                 "note": "algorithmic bytes = one read of the fp32 logits"}
             log("logsoftmax tp=%d: %.4f ms = %.0f GB/s" % (tpv, t, nbytes / t / 1e6))
-        del A, W, logits
+        del logits
 
     if want("rmsnorm"):
         rows, H = 4096, 4096
@@ -512,28 +642,7 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
         del w
 
     if want("ceilings"):
-        # measured ceilings beside the spec peaks: a large vendor GEMM for the
-        # matrix cores, a 1 GiB device copy and a 2 GiB read for HBM
-        n = 8192
-        a8 = inputs.normal_bf16((n, n), 3900, device=dev)
-        b8 = inputs.normal_bf16((n, n), 3901, device=dev)
-        t = timed(lambda: torch.matmul(a8, b8), 10)
-        ceil = {"hipblaslt_bf16_8192cubed_tflops": round(2.0 * n ** 3 / t / 1e9, 1)}
-        del a8, b8
-        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        t = timed(lambda: dst.copy_(src), 20)
-        ceil["copy_1GiB_gbs"] = round(2 * (1 << 30) / t / 1e6, 1)
-        del src, dst
-        rd = torch.ones((1 << 29,), dtype=torch.float32, device=dev)       # 2 GiB
-        t = timed(lambda: torch.sum(rd), 20)
-        ceil["read_2GiB_sum_gbs"] = round((1 << 31) / t / 1e6, 1)
-        del rd
-        ceil["spec"] = {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
-        res["measured_ceilings"] = ceil
-        log("ceilings: hipBLASLt 8192^3 %.0f TFLOP/s, copy %.0f GB/s, read %.0f GB/s"
-            % (ceil["hipblaslt_bf16_8192cubed_tflops"], ceil["copy_1GiB_gbs"],
-               ceil["read_2GiB_sum_gbs"]))
+        res["measured_ceilings"] = ceilings(tb, inputs, torch, dev, timed, log)
 
     if want("training"):
         # Training side at the down projection's shape: Y = A W^T with
@@ -615,30 +724,134 @@ def _cpu_model():
     return "unknown"
 
 
-def cpu_baseline(inputs, np, log, A, W, tp):
-    """The CPU oracle (scalar C, as it stands) on a bounded sample of the
-    headline workload: all M rows x a block of output columns, simulated tp."""
+def cpu_baselines(inputs, np, torch, log, head):
+    """The CPU oracle (scalar C, as it stands) timed on the host cores.
+
+    Headline (cpu_baseline): the config's logprob path -- oracle GEMM over
+    all V columns plus the oracle log-softmax + gather -- on a bounded
+    number of the same rows (the GPU run's own A, W and targets), sized for
+    about 12 s, scaled to the metric's unit.  cpu_oracle_configs: every
+    other workload at full size where that stays within seconds, otherwise
+    on a stated sample, plus a one-thread time on a row subset scaled up."""
     import oracle
-    nth = min(16, os.cpu_count() or 1)
+    from oracle import decoder as od
+    nproc = os.cpu_count() or 1
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = nproc
+    nth = max(1, min(16, affinity))
+    A, W, tgt, tp = head
+    M, K = A.shape
+    V = W.shape[0]
+    log("cpu oracle: copying the headline inputs to the host")
     Ab = inputs.bits(A)
-    M, K = Ab.shape
-    # a short calibration run, then one run sized for about 12 s of CPU work
-    cols = 8
+    Wb = inputs.bits(W)
+    tg = tgt.cpu().numpy()
+
+    def lp_rows(r0, r):
+        lg = oracle.gemm(Ab[r0:r0 + r], Wb, nthreads=nth)
+        out, _ = oracle.logsoftmax_gather(lg, tg[r0:r0 + r], tp)
+        return out
+
     t0 = time.perf_counter()
-    oracle.gemm_tpsim(Ab, inputs.bits(W[:cols]), tp, nthreads=nth)
+    lp_rows(0, 2)
     dt = time.perf_counter() - t0
-    cols = int(min(W.shape[0], max(8, cols * 12.0 / max(dt, 1e-3))))
-    Wb = inputs.bits(W[:cols])
+    rows = int(max(2, min(M, 2 * 12.0 / max(dt, 1e-3))))
     t0 = time.perf_counter()
-    oracle.gemm_tpsim(Ab, Wb, tp, nthreads=nth)
+    lp_rows(0, rows)
     dt = time.perf_counter() - t0
-    fl = 2.0 * M * cols * K
-    log("cpu oracle: %d x %d outputs, K=%d, tp=%d, %d threads: %.2f s" % (M, cols, K, tp, nth, dt))
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
-            "seconds": round(dt, 2),
-            "cpu_model": _cpu_model(),
-            "sample": "oracle tpsim GEMM (scalar leaves, same tree) on A[%d,%d] x W[:%d] "
-                      "(all rows, first %d output columns), tp=%d" % (M, K, cols, cols, tp)}
+    fl = 2.0 * rows * V * K
+    log("cpu oracle headline: %d of %d rows, %d threads: %.2f s" % (rows, M, nth, dt))
+    head_line = {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": nth, "kind": "oracle",
+                 "nproc": nproc, "affinity_cpus": affinity, "seconds": round(dt, 2),
+                 "cpu_model": _cpu_model(),
+                 "full_step_seconds_estimate": round(dt * M / rows, 1),
+                 "sample": "oracle logprob path (scalar-leaf tree GEMM over all %d vocab columns "
+                           "+ tree log-softmax over tp=%d shards + gather) on the first %d of the "
+                           "%d rows of the benchmark's own inputs; value = GEMM flops of those "
+                           "rows / time" % (V, tp, rows, M)}
+
+    res = {"threads": nth, "nproc": nproc, "affinity_cpus": affinity, "cpu_model": _cpu_model()}
+    # one thread, 4 rows x 4096 vocab columns of the same GEMM, scaled up
+    t0 = time.perf_counter()
+    oracle.gemm(Ab[:4], Wb[:4096], nthreads=1)
+    d1 = time.perf_counter() - t0
+    res["lmhead_gemm_1thread"] = {
+        "sample": "4 rows x 4096 columns, K=%d, one thread" % K, "seconds": round(d1, 3),
+        "gflops": round(2.0 * 4 * 4096 * K / d1 / 1e9, 3),
+        "full_gemm_seconds_scaled": round(d1 * (M * V) / (4 * 4096), 1)}
+    del Wb
+
+    # config 1: the small simulated-TP GEMM at full size
+    a1 = inputs.bits(inputs.normal_bf16((16, 1024), 1))
+    w1 = inputs.bits(inputs.normal_bf16((256, 1024), 2))
+    t0 = time.perf_counter()
+    for t in (1, 2, 4):
+        oracle.gemm_tpsim(a1, w1, t, nthreads=nth)
+    d = (time.perf_counter() - t0) / 3
+    res["tp_gemm_M16_K1024_N256"] = {"seconds_per_call": round(d, 4),
+                                     "gflops": round(2.0 * 16 * 256 * 1024 / d / 1e9, 3),
+                                     "sample": "full size, tp 1/2/4"}
+
+    # config 2: the row-parallel down projection at full size, tp = 8
+    a2 = inputs.bits(inputs.normal_bf16((256, 14336), 3))
+    w2 = inputs.bits(inputs.normal_bf16((4096, 14336), 4, std=0.02))
+    t0 = time.perf_counter()
+    oracle.gemm_tpsim(a2, w2, 8, nthreads=nth)
+    d = time.perf_counter() - t0
+    res["downproj_M256_K14336_N4096_tp8"] = {
+        "seconds": round(d, 2), "gflops": round(2.0 * 256 * 4096 * 14336 / d / 1e9, 3),
+        "sample": "full size"}
+    log("cpu oracle down projection: %.2f s" % d)
+    del a2, w2
+
+    # config 3: the row nodes at full size (the oracle's row nodes are one thread)
+    x = inputs.bits(inputs.outlier_bf16((4096, 4096), 5))
+    r = inputs.bits(inputs.outlier_bf16((4096, 4096), 6))
+    w = inputs.bits(inputs.normal_bf16((4096,), 7, std=0.1, mean=1.0))
+    t0 = time.perf_counter()
+    oracle.rmsnorm_residual(x, r, w, 1e-6)
+    d = time.perf_counter() - t0
+    res["rmsnorm_4096x4096"] = {"seconds": round(d, 3),
+                                "gbs": round((4 * 4096 * 4096 * 2) / d / 1e9, 3), "threads": 1}
+    del x, r
+    xr = inputs.bits(inputs.normal_bf16((32768, 16, 128), 8))
+    pos = inputs.positions(32768, 32768, seed=9).numpy()
+    c, s = oracle.rope_table(1e6, 128, 32768)
+    t0 = time.perf_counter()
+    oracle.rope(xr, pos, c, s)
+    d = time.perf_counter() - t0
+    res["rope_32768x16x128"] = {"seconds": round(d, 3),
+                                "gbs": round((2 * 32768 * 16 * 128 * 2) / d / 1e9, 3),
+                                "threads": 1}
+    del xr
+    g = inputs.bits(inputs.normal_bf16((4096, 14336), 10, std=3.0))
+    u = inputs.bits(inputs.normal_bf16((4096, 14336), 11))
+    t0 = time.perf_counter()
+    oracle.swiglu(g, u)
+    d = time.perf_counter() - t0
+    res["swiglu_4096x14336"] = {"seconds": round(d, 3),
+                                "gbs": round((3 * 4096 * 14336 * 2) / d / 1e9, 3), "threads": 1}
+    del g, u
+    log("cpu oracle row nodes done")
+
+    # config 5: the decoder forward on one sequence of 64 tokens (full width)
+    cfg = inputs.DecoderConfig()
+    wt = inputs.decoder_weights(cfg, 12)
+    w_np = {"emb": inputs.bits(wt["emb"]), "lm_head": inputs.bits(wt["lm_head"]),
+            "final_norm": inputs.bits(wt["final_norm"]),
+            "layers": [{k: inputs.bits(v) for k, v in lw.items()} for lw in wt["layers"]]}
+    del wt
+    tok = inputs.decoder_tokens(1, 64, cfg.vocab, 13).numpy()
+    t0 = time.perf_counter()
+    od.decoder_logprobs(w_np, tok, cfg, tp=4)
+    d = time.perf_counter() - t0
+    res["decoder_8L_d2048_1x64_tokens_tp4"] = {
+        "seconds": round(d, 2), "tokens_per_s": round(64 / d, 2),
+        "sample": "one sequence of 64 tokens, the shortest the 64-key leaves allow (the benchmark runs 8 x 512)"}
+    log("cpu oracle decoder: %.2f s for 64 tokens" % d)
+    return head_line, res
 
 
 if __name__ == "__main__":

@@ -71,7 +71,15 @@ def _c(a, dtype):
 
 
 def _threads(n):
-    return n if n else max(1, os.cpu_count() or 1)
+    """n, or by default the CPUs this process may use, at most 16 (one GPU's
+    share of a host); threads split independent outputs, never a sum."""
+    if n:
+        return n
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count() or 1
+    return max(1, min(16, avail))
 
 
 # --- primitives -------------------------------------------------------------

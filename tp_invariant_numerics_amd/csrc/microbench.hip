@@ -5,10 +5,11 @@
 //   k_mfma_peak   independent chains of v_mfma_f32_16x16x32_bf16 (the GEMM
 //                 leaf instruction) from registers: no memory traffic in the
 //                 loop, so its rate is the matrix cores' sustained peak.
-//   k_hbm_read    non-temporal 16-byte loads over a buffer much larger than
-//                 the last-level cache, folded by xor (one 4-byte store per
-//                 thread at the end).
-//   k_hbm_copy    non-temporal 16-byte loads and stores, src -> dst.
+//   k_hbm_read    non-temporal 16-byte loads (eight in flight per thread)
+//                 over a buffer much larger than the last-level cache, folded
+//                 by xor (one 4-byte store per thread at the end).
+//   k_hbm_copy    non-temporal 16-byte loads and stores (four per thread in
+//                 flight), src -> dst.
 //
 // Grids are sized by the caller; every access is bounds-checked against the
 // byte count (a multiple of 16).
@@ -40,33 +41,41 @@ __global__ void __launch_bounds__(512) k_mfma_peak(const u32x4 *seed, float *out
   out[t] = s[0] + s[1] + s[2] + s[3];
 }
 
+// Each workgroup streams consecutive chunks of 256 * U 16-byte units, U loads
+// in flight per thread, so that every wave instruction covers 1 KB.
+template <int U>
 __global__ void __launch_bounds__(256) k_hbm_read(const u32x4 *src, int64_t n16, unsigned *out) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t chunk = 256 * U;
   u32x4 x = {0u, 0u, 0u, 0u};
-  int64_t i = t0;
-  // four loads in flight per thread
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 v0 = __builtin_nontemporal_load(src + i);
-    const u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
-    const u32x4 v2 = __builtin_nontemporal_load(src + i + 2 * stride);
-    const u32x4 v3 = __builtin_nontemporal_load(src + i + 3 * stride);
-    x ^= v0 ^ v1 ^ v2 ^ v3;
+  for (int64_t base = (int64_t)blockIdx.x * chunk; base < n16; base += (int64_t)gridDim.x * chunk) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      v[u] = i < n16 ? __builtin_nontemporal_load(src + i) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) x ^= v[u];
   }
-  for (; i < n16; i += stride) x ^= __builtin_nontemporal_load(src + i);
-  out[t0] = x[0] ^ x[1] ^ x[2] ^ x[3];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
+template <int U>
 __global__ void __launch_bounds__(256) k_hbm_copy(const u32x4 *src, u32x4 *dst, int64_t n16) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  for (; i + stride < n16; i += 2 * stride) {
-    const u32x4 v0 = __builtin_nontemporal_load(src + i);
-    const u32x4 v1 = __builtin_nontemporal_load(src + i + stride);
-    __builtin_nontemporal_store(v0, dst + i);
-    __builtin_nontemporal_store(v1, dst + i + stride);
+  const int64_t chunk = 256 * U;
+  for (int64_t base = (int64_t)blockIdx.x * chunk; base < n16; base += (int64_t)gridDim.x * chunk) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      if (i < n16) v[u] = __builtin_nontemporal_load(src + i);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * 256 + threadIdx.x;
+      if (i < n16) __builtin_nontemporal_store(v[u], dst + i);
+    }
   }
-  for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
 static int mb_check() { return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH; }
@@ -96,7 +105,7 @@ int tbik_bench_hbm_read(const void *buf, int64_t bytes, unsigned *out, int block
   if (!buf || !out) return TBIK_ERR_NULL;
   if (bytes <= 0 || (bytes & 15) != 0 || blocks < 1 || blocks > (1 << 20)) return TBIK_ERR_SHAPE;
   if (((uintptr_t)buf & 15) != 0) return TBIK_ERR_ALIGN;
-  hipLaunchKernelGGL(k_hbm_read, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(k_hbm_read<8>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4 *)buf, bytes / 16, out);
   return mb_check();
 }
@@ -105,7 +114,7 @@ int tbik_bench_hbm_copy(const void *src, void *dst, int64_t bytes, int blocks, v
   if (!src || !dst) return TBIK_ERR_NULL;
   if (bytes <= 0 || (bytes & 15) != 0 || blocks < 1 || blocks > (1 << 20)) return TBIK_ERR_SHAPE;
   if ((((uintptr_t)src | (uintptr_t)dst) & 15) != 0) return TBIK_ERR_ALIGN;
-  hipLaunchKernelGGL(k_hbm_copy, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+  hipLaunchKernelGGL(k_hbm_copy<4>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4 *)src, (u32x4 *)dst, bytes / 16);
   return mb_check();
 }
