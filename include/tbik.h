@@ -51,7 +51,8 @@
  *  - Outputs must not overlap inputs unless stated otherwise.
  *  - Inputs must be finite; non-finite inputs give unspecified values (but
  *    never out-of-bounds accesses).
- *  - Entry points are thread-safe (no global mutable state).
+ *  - Entry points are thread-safe (the only global state is the per-device
+ *    address of tbik_gemm_noalloc's scratch array, set once under a lock).
  */
 #ifndef TBIK_H
 #define TBIK_H
@@ -457,6 +458,25 @@ int tbik_rmsnorm_backward(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf1
                           const tbik_bf16 *dy, const tbik_bf16 *dr, tbik_bf16 *dh, float *dw,
                           int rows, int H, int64_t ld, float eps, int dp, float *ws,
                           size_t ws_bytes, void *stream);
+
+/* ------------------------------------------------------------------------
+ * tbik_gemm without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts
+ * that forbid hipMalloc).  Same arguments, results and bits as tbik_gemm
+ * given a workspace of tbik_gemm_workspace_bytes(M, N, K): the split-K node
+ * partials go to a file-scope device array of tbik_gemm_noalloc_max_bytes()
+ * = 16 MiB held by every GPU the library runs on until the process ends.
+ * The call allocates nothing.  A shape whose workspace would exceed that
+ * size returns TBIK_ERR_WORKSPACE before any launch (shapes needing no
+ * workspace always run).  Every call on one GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (concurrent streams, or threads
+ * without ordering) race and must not be issued.  The array's device
+ * address is resolved on the first call made with a given device current.
+ * ---------------------------------------------------------------------- */
+size_t tbik_gemm_noalloc_max_bytes(void);
+int tbik_gemm_noalloc(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, float *C,
+                      int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int leaf_mode,
+                      void *stream);
 
 /* ------------------------------------------------------------------------
  * Ceiling microbenchmarks.  Not part of the method: the attainable rates of

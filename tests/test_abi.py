@@ -261,3 +261,18 @@ def test_rope_table_equals_oracle(orc):
         oc, os_ = orc.rope_table(theta, d, maxp)
         assert np.array_equal(c.numpy().view(np.uint32), oc.view(np.uint32))
         assert np.array_equal(s.numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_gemm_noalloc_validation(L):
+    """The allocation-free GEMM validates like tbik_gemm and refuses, before
+    any launch, shapes whose split-K partials exceed its scratch array."""
+    g = L.tbik_gemm_noalloc
+    assert L.tbik_gemm_noalloc_max_bytes() == 16 << 20
+    assert g(None, 64, FAKE, 64, FAKE2, 64, None, 1, 1, 64, 0, None) == E_NULL
+    assert g(FAKE, 64, FAKE, 64, FAKE2, 64, None, 1, 1, 65, 0, None) == E_SHAPE
+    assert g(MISAL, 64, FAKE, 64, FAKE2, 64, None, 1, 1, 64, 0, None) == E_ALIGN
+    assert g(FAKE, 64, FAKE, 64, FAKE2, 64, None, 1, 1, 64, 7, None) == E_ARG
+    # M = 256, N = 16384, K = 14336 splits into two tree nodes: 32 MiB of partials
+    assert L.tbik_gemm_workspace_bytes(256, 16384, 14336) > (16 << 20)
+    assert g(FAKE, 14336, FAKE, 14336, FAKE2, 16384, None, 256, 16384, 14336, 0, None) == E_WS
+    assert g(FAKE, 64, FAKE, 64, FAKE2, 64, None, 0, 5, 64, 0, None) == OK   # empty: no-op

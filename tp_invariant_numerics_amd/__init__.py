@@ -93,6 +93,8 @@ def _sigs():
         "tbik_swiglu_backward": (i32, [p, p, p, p, p, i32, i32, i64, i64, i64, i64, i64, p]),
         "tbik_rmsnorm_backward_workspace_bytes": (sz, [i32, i32, i32, i32]),
         "tbik_rmsnorm_backward": (i32, [p, p, p, p, p, p, p, i32, i32, i64, f32, i32, p, sz, p]),
+        "tbik_gemm_noalloc_max_bytes": (sz, []),
+        "tbik_gemm_noalloc": (i32, [p, i64, p, i64, p, i64, p, i32, i32, i32, i32, p]),
         "tbik_bench_mfma_flops": (i64, [i32, i32]),
         "tbik_bench_mfma": (i32, [p, p, i32, i32, p]),
         "tbik_bench_hbm_read": (i32, [p, i64, p, i32, p]),
@@ -211,6 +213,29 @@ def tbik_gemm(A, W, leaf_mode=LEAF_MFMA, out=None, out_bf16=None, want_fp32=True
     rc = lib().tbik_gemm(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(out), ldc, _ptr(out_bf16),
                          M, N, K, leaf_mode, _ptr(ws), wsb, _stream())
     _chk(rc, "tbik_gemm")
+    return out, out_bf16
+
+
+def tbik_gemm_noalloc(A, W, leaf_mode=LEAF_MFMA, out=None, out_bf16=None, want_fp32=True,
+                      want_bf16=False):
+    """tbik_gemm with the split-K partials in the library's own device
+    scratch (no workspace argument, nothing allocated by the library)."""
+    _bits(A); _bits(W); _need_gpu(A, W)
+    M, K = A.shape
+    N = W.shape[0]
+    if W.shape[1] != K:
+        raise ValueError("K mismatch")
+    if out is None and want_fp32:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    if out_bf16 is None and want_bf16:
+        out_bf16 = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    ref = out if out is not None else out_bf16
+    ldc = _ld(ref) if ref is not None else N
+    if out is not None and out_bf16 is not None and _ld(out_bf16) != ldc:
+        raise ValueError("C and C_bf16 must share the row stride")
+    rc = lib().tbik_gemm_noalloc(_ptr(A), _ld(A), _ptr(W), _ld(W), _ptr(out), ldc, _ptr(out_bf16),
+                                 M, N, K, leaf_mode, _stream())
+    _chk(rc, "tbik_gemm_noalloc")
     return out, out_bf16
 
 

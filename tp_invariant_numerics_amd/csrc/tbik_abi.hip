@@ -2,9 +2,12 @@
 //
 // Host-side validation happens before any HIP call; an invalid call
 // launches nothing and returns a TBIK_ERR_* code.  No entry point allocates
-// memory or keeps state between calls.
+// memory.  The only state kept between calls is the per-device address of
+// tbik_gemm_noalloc's scratch array, resolved once.
 #include <math.h>
 #include <stdint.h>
+
+#include <mutex>
 
 #include "../../include/tbik.h"
 #include "tbik_device.h"
@@ -32,6 +35,40 @@ int check_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw,
   if (leaf_mode != TBIK_LEAF_MFMA && leaf_mode != TBIK_LEAF_SCALAR) return TBIK_ERR_ARG;
   const int nb = K / 64;
   if (nb / tbik::tree_T(nb) > tbik::kMaxGroupLeaves) return TBIK_ERR_SHAPE;
+  return TBIK_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Scratch of tbik_gemm_noalloc: the split-K node partials live in this
+// file-scope device array instead of a caller's workspace.  Each GPU the
+// library runs on holds its own copy until the process ends; in host code
+// the name is only a stand-in, so its device address is resolved once per
+// device with hipGetSymbolAddress and only that address is ever passed on.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;   // 16 MiB
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (resolved on the first
+// call made with that device current).
+int scratch_for_current_device(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return TBIK_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr)
+      return TBIK_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
   return TBIK_OK;
 }
 
@@ -87,6 +124,25 @@ int tbik_gemm(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, 
   }
   return tbik_gemm_strided_batched(A, lda, 0, W, ldw, 0, C, ldc, 0, C_bf16, M, N, K, 1, leaf_mode,
                                    stream);
+}
+
+size_t tbik_gemm_noalloc_max_bytes(void) { return kNoallocScratchBytes; }
+
+int tbik_gemm_noalloc(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64_t ldw, float *C,
+                      int64_t ldc, tbik_bf16 *C_bf16, int M, int N, int K, int leaf_mode,
+                      void *stream) {
+  int rc = check_gemm(A, lda, W, ldw, C, ldc, C_bf16, M, N, K, leaf_mode);
+  if (rc) return rc;
+  if (M == 0 || N == 0) return TBIK_OK;
+  const size_t need = leaf_mode == TBIK_LEAF_MFMA ? tbik_gemm_workspace_bytes(M, N, K) : 0;
+  if (need > kNoallocScratchBytes) return TBIK_ERR_WORKSPACE;
+  void *ws = nullptr;
+  if (need > 0) {
+    rc = scratch_for_current_device(&ws);
+    if (rc) return rc;
+  }
+  return tbik_gemm(A, lda, W, ldw, C, ldc, C_bf16, M, N, K, leaf_mode, static_cast<float *>(ws),
+                   need, stream);
 }
 
 int tbik_gemm_strided_batched(const tbik_bf16 *A, int64_t lda, int64_t strideA,
