@@ -22,7 +22,7 @@ and tp = 1, prefill, row kernels, decoder, training side), and the CPU
 oracle timed on bounded samples of every workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-       python bench.py --profile-gemm      (LM-head GEMM launches only, for rocprofv3)
+       python bench.py --profile lmhead|rows|downproj|calib   (a few launches, for rocprofv3)
 """
 import argparse
 import hashlib
@@ -39,13 +39,14 @@ M_HEAD, K_HEAD, V_HEAD, TP_HEAD = 512, 4096, 151936, 4
 
 # The headline's LM-head GEMM kernel, as named in a rocprofv3 kernel trace.
 HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
-# HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs (profiles/
-# k_gemm_ring_lmhead_M512_K4096_N151936.md): FETCH_SIZE x its copy factor +
-# WRITE_SIZE x its copy factor, the factors being what a plain 1 GiB device
-# copy reads on the same counters.  Valid only for the GEMM sources the
-# counters were taken on (hash below); None until measured.
-HEAD_TRAFFIC_BYTES = None
-HEAD_TRAFFIC_SRC_SHA256 = None
+# HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs of
+# `bench.py --profile lmhead` (profiles/k_gemm_ring_lmhead_M512_K4096_N151936.md):
+# FETCH_SIZE 1050738 KiB x 2.000 + WRITE_SIZE 415757 KiB x 1.000, the factors
+# being what a plain 1 GiB device copy reads on the same counters
+# (`bench.py --profile calib`: 524301 KiB fetched, 1048576 KiB written).  Valid
+# only for the GEMM sources the counters were taken on (hash below).
+HEAD_TRAFFIC_BYTES = (1050738 * 2 + 415757) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "b368286dba4f51fbc852b85d1d79d7ec4104168481bb3a3d0859460c35544994"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
 # k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64818 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000.
@@ -78,10 +79,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
-    ap.add_argument("--pmc-calib", action="store_true",
-                    help="run only a plain device copy of known size (counter calibration)")
-    ap.add_argument("--profile-gemm", action="store_true",
-                    help="run only launches of the headline LM-head GEMM (profiling)")
+    ap.add_argument("--profile", default="", choices=["", "lmhead", "rows", "downproj", "calib"],
+                    help="run only a few launches of one group of kernels, for rocprofv3: "
+                         "lmhead (the headline's GEMM and log-softmax), rows (RMSNorm, RoPE, "
+                         "SwiGLU, standalone log-softmax), downproj (tp = 8 partials + combine), "
+                         "calib (a plain 1 GiB device copy, the counters' byte scale)")
     ap.add_argument("--only", default="", help="run only one extra workload (profiling)")
     return ap.parse_args()
 
@@ -114,7 +116,7 @@ def main():
     def log(*a):
         print(*a, file=sys.stderr, flush=True)
 
-    if args.pmc_calib:
+    if args.profile == "calib":
         # plain copy kernel of known size for FETCH_SIZE / WRITE_SIZE scaling
         nbytes = 1 << 30
         src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
@@ -166,11 +168,10 @@ def main():
     def gemm():
         tb.tbik_gemm_logits(A, W, out=logits, pmax=pm)
 
-    if args.profile_gemm:
-        for _ in range(max(3, args.steps)):
-            gemm()
-        torch.cuda.synchronize()
-        log("profile-gemm: %d launches of the LM-head GEMM" % max(3, args.steps))
+    if args.profile:
+        profile_kernels(args.profile, tb, inputs, torch, dev, log,
+                        (gemm, lambda: tb.tbik_logsoftmax_gather_pmax(logits, tgt, pm, tp, ws=lws,
+                                                                      out=lp)))
         return
 
     # One step = the config's logprob path: the LM-head GEMM with its fused
@@ -315,6 +316,43 @@ def main():
         "extra": extra,
     }
     print(json.dumps(out), flush=True)
+
+
+def profile_kernels(what, tb, inputs, torch, dev, log, head):
+    """A few launches of one group of kernels and nothing else, so that a
+    rocprofv3 run of `bench.py --profile <what>` reads their counters."""
+    reps = 5
+    if what == "lmhead":
+        for f in head:
+            for _ in range(reps):
+                f()
+    elif what == "rows":
+        x = inputs.outlier_bf16((4096, 4096), 3400, device=dev)
+        r = inputs.outlier_bf16((4096, 4096), 3410, device=dev)
+        w = inputs.normal_bf16((4096,), 3420, std=0.1, mean=1.0, device=dev)
+        q = inputs.normal_bf16((32768, 16, 128), 3500, device=dev)
+        pos = inputs.positions(32768, 32768, seed=3501).to(dev)
+        c, s = tb.tbik_rope_table(1e6, 128, 32768)
+        c, s = c.to(dev), s.to(dev)
+        g = inputs.normal_bf16((4096, 14336), 3600, std=3.0, device=dev)
+        u = inputs.normal_bf16((4096, 14336), 3601, device=dev)
+        lg = torch.randn((512, 151936), device=dev) * 3
+        tgt = inputs.uniform_int(512, 151936, 3302, device=dev)
+        for _ in range(reps):
+            tb.tbik_rmsnorm_residual(x, r, w, 1e-6)
+            tb.tbik_rope(q, pos, c, s)
+            tb.tbik_swiglu(g, u)
+            tb.tbik_logsoftmax_gather(lg, tgt, 1)
+    elif what == "downproj":
+        M, K, N, tp = 256, 14336, 4096, 8
+        A = inputs.normal_bf16((M, K), 1001, device=dev)
+        Ws = [inputs.normal_bf16((N, K), 2001 + i, std=0.02, device=dev) for i in range(6)]
+        ws = torch.empty((tp, M, N), dtype=torch.float32, device=dev)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for i in range(reps):
+            tb.tbik_gemm_tpsim(A, Ws[i % 6], tp, ws=ws, out=C)
+    torch.cuda.synchronize()
+    log("profile %s: %d launches of each kernel" % (what, reps))
 
 
 def downproj_tp8(tb, inputs, torch, dev, timed, log, args):
