@@ -479,6 +479,23 @@ def ceilings(tb, inputs, torch, dev, timed, log):
     ceil["hbm_read_4GiB_gbs"] = max(rd.values())
     ceil["hbm_copy_2GiB_gbs"] = max(cp.values())
     ceil["hbm_by_grid"] = {"read": rd, "copy_read_plus_write": cp}
+    # the GEMM ring's operand copy alone (32 KB stages, 4-slot LDS ring,
+    # 8 waves, one workgroup per CU): from a 1 MiB window (resident in every
+    # XCD's 4 MB L2), a 32 MiB one (beyond L2, inside the last-level cache)
+    # and a 1 GiB one (HBM)
+    lds = {}
+    outl = torch.empty((1024 * 512,), dtype=torch.int32, device=dev)
+    for win, name in ((1 << 20, "l2_1MiB"), (32 << 20, "llc_32MiB"), (1 << 30, "hbm_1GiB")):
+        for blocks, stages in ((256, 2048), (1024, 512)):
+            nb = {}
+
+            def cl():
+                _, nb["b"] = tb.tbik_bench_copy_lds(buf, win, stages, blocks, out=outl)
+
+            t = timed(cl, 5, warm=2)
+            lds["%s_wg%d" % (name, blocks)] = round(nb["b"] / t / 1e6, 1)
+    ceil["ring_copy_to_lds_gbs"] = lds
+    ceil["ring_copy_l2_gbs"] = max(v for k, v in lds.items() if k.startswith("l2_"))
     del buf, src, dst
     n = 8192
     a8 = inputs.normal_bf16((n, n), 3901, device=dev)
@@ -487,9 +504,10 @@ def ceilings(tb, inputs, torch, dev, timed, log):
     ceil["hipblaslt_bf16_8192cubed_tflops"] = round(2.0 * n ** 3 / t / 1e9, 1)
     del a8, b8
     ceil["spec"] = {"bf16_mfma_tflops": PEAK_BF16_TFLOPS, "hbm_gbs": PEAK_HBM_GBS}
-    log("ceilings: MFMA loop %.0f TFLOP/s, HBM read %.0f GB/s, copy %.0f GB/s, hipBLASLt %.0f"
+    log("ceilings: MFMA loop %.0f TFLOP/s, HBM read %.0f GB/s, copy %.0f GB/s, ring copy from "
+        "L2 %.0f GB/s, hipBLASLt %.0f"
         % (ceil["mfma_bf16_loop_tflops"], ceil["hbm_read_4GiB_gbs"], ceil["hbm_copy_2GiB_gbs"],
-           ceil["hipblaslt_bf16_8192cubed_tflops"]))
+           ceil["ring_copy_l2_gbs"], ceil["hipblaslt_bf16_8192cubed_tflops"]))
     return ceil
 
 

@@ -496,6 +496,15 @@ int tbik_gemm_noalloc(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W, int64
  *   out: blocks * 256 unsigned (an xor of what each thread read).
  * tbik_bench_hbm_copy: src -> dst, `bytes` (multiple of 16), non-temporal
  *   16-byte loads and stores; the buffers must not overlap.
+ * tbik_bench_copy_lds: the GEMM ring's operand copy without the MFMAs.
+ *   `blocks` workgroups of 8 waves (128 KB of LDS each) each move `stages`
+ *   stages of 32 KB from buf into a 4-slot LDS ring with 16-byte-per-lane
+ *   global->LDS buffer loads, 3 stages ahead, one barrier per stage.  The
+ *   stages are read cyclically from the first `window_bytes` of buf (a
+ *   multiple of 32768, at most 2^31 - 32768), workgroup b starting at stage
+ *   7b.  Bytes moved = blocks * stages * 32768.  A window that fits one XCD's
+ *   L2 (4 MB) measures the L2 -> LDS rate; larger ones, the last-level cache
+ *   or HBM through the same path.  out: blocks * 512 unsigned.
  * Errors: TBIK_ERR_NULL, TBIK_ERR_SHAPE (sizes out of range),
  * TBIK_ERR_ALIGN (pointers not 16-byte aligned), TBIK_ERR_LAUNCH.
  * ---------------------------------------------------------------------- */
@@ -503,6 +512,8 @@ int64_t tbik_bench_mfma_flops(int blocks, int iters);
 int tbik_bench_mfma(const void *seed, float *out, int blocks, int iters, void *stream);
 int tbik_bench_hbm_read(const void *buf, int64_t bytes, unsigned *out, int blocks, void *stream);
 int tbik_bench_hbm_copy(const void *src, void *dst, int64_t bytes, int blocks, void *stream);
+int tbik_bench_copy_lds(const void *buf, int64_t window_bytes, int stages, unsigned *out,
+                        int blocks, void *stream);
 
 #ifdef __cplusplus
 }

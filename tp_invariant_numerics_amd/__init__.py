@@ -99,6 +99,7 @@ def _sigs():
         "tbik_bench_mfma": (i32, [p, p, i32, i32, p]),
         "tbik_bench_hbm_read": (i32, [p, i64, p, i32, p]),
         "tbik_bench_hbm_copy": (i32, [p, p, i64, i32, p]),
+        "tbik_bench_copy_lds": (i32, [p, i64, i32, p, i32, p]),
     }
 
 
@@ -602,3 +603,15 @@ def tbik_bench_hbm_copy(src, dst, blocks):
     _chk(lib().tbik_bench_hbm_copy(_ptr(src), _ptr(dst), n, blocks, _stream()),
          "tbik_bench_hbm_copy")
     return dst
+
+
+def tbik_bench_copy_lds(buf, window_bytes, stages, blocks, out=None):
+    """The GEMM ring's operand copy alone; returns (out, bytes moved)."""
+    _need_gpu(buf)
+    if window_bytes > buf.numel() * buf.element_size():
+        raise ValueError("window larger than the buffer")
+    if out is None:
+        out = torch.empty((blocks * 512,), dtype=torch.int32, device=buf.device)
+    _chk(lib().tbik_bench_copy_lds(_ptr(buf), window_bytes, stages, _ptr(out), blocks, _stream()),
+         "tbik_bench_copy_lds")
+    return out, blocks * stages * 32768

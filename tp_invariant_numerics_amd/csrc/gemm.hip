@@ -408,6 +408,13 @@ struct Ring {
   static constexpr int DPW = SEG / WAVES;                 // loads per wave per stage
   static constexpr int DPA = SEGA / WAVES;                // of which from A
   static constexpr int SLOT = SEG * 64;                   // 16-byte units per slot
+  // Where a leaf issues the copy of the stage that refills the freed slot.
+  // On tiles of 64 rows or more the copies go after the leaf's MFMAs: when
+  // the memory pipeline is backed up a wave stalls at the load instruction,
+  // and issued before the MFMAs that stall held back the matrix core (the
+  // LM-head and prefill GEMMs ran 6% faster with the copies last, bitwise
+  // the same).  The thin tiles keep them first (3% faster there).
+  static constexpr bool LATE = MT >= 64;
 
   u32x4 *ring;
   __amdgpu_buffer_rsrc_t rsa, rsb;
@@ -466,9 +473,10 @@ struct Ring {
     }
   }
 
-  // One leaf: wait for its stage, refill the slot freed by the previous
-  // leaf, then the MFMAs.  `slot_static` >= 0 when the slot is known at
-  // compile time (the block started at a multiple of S).
+  // One leaf: wait for its stage, the MFMAs, and the refill of the slot the
+  // previous leaf freed (before or after the MFMAs, see LATE).
+  // `static_slot`: the slot is known at compile time (the block started at a
+  // multiple of S).
   __device__ __forceinline__ void step(float (&acc)[R], int j, bool static_slot) {
     // keep the scheduler inside one leaf: unbounded interleaving across a
     // fully unrolled group raises register pressure into spills
@@ -480,26 +488,39 @@ struct Ring {
       // in ca/cb): refill it with stage l+j+S, read the next leaf's
       // fragments, then the MFMAs of leaf l+j
       u32x4 na[WM][2], nb[WN][2];
-      if (static_slot) {
-        issue(l + j + S, j % S);
-        read_frags(na, nb, (j + 1) % S);
-      } else {
-        issue(l + j + S, (unsigned)(l + j) % S);
-        read_frags(na, nb, (unsigned)(l + j + 1) % S);
+      if constexpr (!LATE) {
+        if (static_slot) issue(l + j + S, j % S);
+        else issue(l + j + S, (unsigned)(l + j) % S);
       }
+      if (static_slot) read_frags(na, nb, (j + 1) % S);
+      else read_frags(na, nb, (unsigned)(l + j + 1) % S);
       leaf_mfma<WM, WN>(acc, ca, cb);
+      if constexpr (LATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (static_slot) issue(l + j + S, j % S);
+        else issue(l + j + S, (unsigned)(l + j) % S);
+      }
 #pragma unroll
       for (int i = 0; i < WM; ++i) { ca[i][0] = na[i][0]; ca[i][1] = na[i][1]; }
 #pragma unroll
       for (int i = 0; i < WN; ++i) { cb[i][0] = nb[i][0]; cb[i][1] = nb[i][1]; }
     } else if (static_slot) {
-      issue(l + j + S - 1, (j + S - 1) % S);
+      if constexpr (!LATE) issue(l + j + S - 1, (j + S - 1) % S);
       mfma_leaf(acc, j % S);
+      if constexpr (LATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(l + j + S - 1, (j + S - 1) % S);
+      }
     } else {
-      issue(l + j + S - 1, (unsigned)(l + j + S - 1) % S);
+      if constexpr (!LATE) issue(l + j + S - 1, (unsigned)(l + j + S - 1) % S);
       mfma_leaf(acc, (unsigned)(l + j) % S);
+      if constexpr (LATE) {
+        __builtin_amdgcn_sched_barrier(0);
+        issue(l + j + S - 1, (unsigned)(l + j + S - 1) % S);
+      }
     }
   }
+
 
   // Perfect tree over the next U leaves (U in {1,2,4,8}), merges resolved at
   // compile time; with NX == 3 the merge of leaf j-1 follows the MFMAs of

@@ -10,6 +10,13 @@
 //                 by xor (one 4-byte store per thread at the end).
 //   k_hbm_copy    non-temporal 16-byte loads and stores (four per thread in
 //                 flight), src -> dst.
+//   k_copy_lds    the GEMM ring's operand copy alone: 8 waves move 32 KB
+//                 stages with 16-byte-per-lane global->LDS buffer loads into a
+//                 4-slot LDS ring, 3 stages ahead, one barrier per stage, no
+//                 MFMAs.  Over a window small enough to stay in every XCD's
+//                 L2 it measures the L2 -> LDS delivery rate the 128x128 GEMM
+//                 tiles depend on; over larger windows, the last-level cache
+//                 and HBM through the same path.
 //
 // Grids are sized by the caller; every access is bounds-checked against the
 // byte count (a multiple of 16).
@@ -78,6 +85,49 @@ __global__ void __launch_bounds__(256) k_hbm_copy(const u32x4 *src, u32x4 *dst, 
   }
 }
 
+typedef void __attribute__((address_space(3))) *mb_lptr_t;
+
+// One workgroup: `stages` stages of 32 KB (32 segments of 1 KB, four per
+// wave) read from a window of `nst` stages, starting at stage 7*blockIdx.x
+// and wrapping, so concurrent workgroups read different lines.  Stage st goes
+// to ring slot st % 4; after a wave issues stage st+3 it waits for its own
+// loads of stage st (vector-memory counter <= 12) and the workgroup meets at
+// a barrier, exactly the GEMM ring's protocol.  The tail re-reads the last
+// stage, as the GEMM's does.
+__global__ void __launch_bounds__(512) k_copy_lds(const void *src, unsigned nst, int stages,
+                                                  unsigned *out) {
+  constexpr int S = 4, SLOT = 2048;              // 16-byte units per 32 KB slot
+  __shared__ u32x4 ring[S * SLOT];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc((void *)src, (short)0, (int)(nst * 32768u), 0x00020000);
+  const unsigned st0 = (blockIdx.x * 7u) % nst;
+  unsigned voff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (unsigned)((wave + 8 * i) * 1024 + lane * 16);
+  auto issue = [&](int st, int slot) {
+    const int sc = st < stages ? st : stages - 1;
+    const int soff = (int)(((st0 + (unsigned)sc) % nst) * 32768u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (mb_lptr_t)(ring + slot * SLOT + (wave + 8 * i) * 64), 16, voff[i], soff, 0, 0);
+  };
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) issue(s, s);
+  for (int st = 0; st < stages; ++st) {
+    issue(st + S - 1, (st + S - 1) % S);
+    // vmcnt <= 12 (gfx9 encoding: vmcnt [3:0] and [15:14]; expcnt, lgkmcnt unconstrained)
+    __builtin_amdgcn_s_waitcnt((12 & 15) | ((12 >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  }
+  __builtin_amdgcn_s_waitcnt((0 & 15) | (7 << 4) | (15 << 8));
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  const u32x4 v = ring[((stages - 1) % S) * SLOT + threadIdx.x];
+  out[(int64_t)blockIdx.x * 512 + threadIdx.x] = v[0] ^ v[1] ^ v[2] ^ v[3];
+}
+
 static int mb_check() { return hipGetLastError() == hipSuccess ? TBIK_OK : TBIK_ERR_LAUNCH; }
 
 }  // namespace tbik
@@ -116,6 +166,18 @@ int tbik_bench_hbm_copy(const void *src, void *dst, int64_t bytes, int blocks, v
   if ((((uintptr_t)src | (uintptr_t)dst) & 15) != 0) return TBIK_ERR_ALIGN;
   hipLaunchKernelGGL(k_hbm_copy<4>, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4 *)src, (u32x4 *)dst, bytes / 16);
+  return mb_check();
+}
+
+int tbik_bench_copy_lds(const void *buf, int64_t window_bytes, int stages, unsigned *out,
+                        int blocks, void *stream) {
+  if (!buf || !out) return TBIK_ERR_NULL;
+  if (window_bytes < 32768 || (window_bytes & 32767) != 0 || window_bytes > ((int64_t)1 << 31) - 32768 ||
+      stages < 1 || blocks < 1 || blocks > (1 << 20))
+    return TBIK_ERR_SHAPE;
+  if (((uintptr_t)buf & 15) != 0) return TBIK_ERR_ALIGN;
+  hipLaunchKernelGGL(k_copy_lds, dim3((unsigned)blocks), dim3(512), 0, (hipStream_t)stream, buf,
+                     (unsigned)(window_bytes / 32768), stages, out);
   return mb_check();
 }
 
