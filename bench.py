@@ -41,17 +41,17 @@ M_HEAD, K_HEAD, V_HEAD, TP_HEAD = 512, 4096, 151936, 4
 HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs of
 # `bench.py --profile lmhead` (profiles/k_gemm_ring_lmhead_M512_K4096_N151936.md):
-# FETCH_SIZE 1050738 KiB x 2.000 + WRITE_SIZE 415757 KiB x 1.000, the factors
+# FETCH_SIZE 1009371 KiB x 2.000 + WRITE_SIZE 339561 KiB x 1.000, the factors
 # being what a plain 1 GiB device copy reads on the same counters
 # (`bench.py --profile calib`: 524301 KiB fetched, 1048576 KiB written).  Valid
 # only for the GEMM sources the counters were taken on (hash below).
-HEAD_TRAFFIC_BYTES = (1050738 * 2 + 415757) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "b368286dba4f51fbc852b85d1d79d7ec4104168481bb3a3d0859460c35544994"
+HEAD_TRAFFIC_BYTES = (1009371 * 2 + 339561) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "95a77d1f37b961b6c907f2354afb0b91b509f451cf877dd4a97d7c88dc847ea5"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
-# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64818 KiB x 2.000
+# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64822 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000.
-HEAD_TP8_TRAFFIC_BYTES = (64818 * 2 + 32768) * 1024
-HEAD_TP8_TRAFFIC_SRC_SHA256 = "b368286dba4f51fbc852b85d1d79d7ec4104168481bb3a3d0859460c35544994"
+HEAD_TP8_TRAFFIC_BYTES = (64822 * 2 + 32768) * 1024
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "95a77d1f37b961b6c907f2354afb0b91b509f451cf877dd4a97d7c88dc847ea5"
 
 
 def gemm_source_sha256(root):
@@ -79,7 +79,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
-    ap.add_argument("--profile", default="", choices=["", "lmhead", "rows", "downproj", "calib"],
+    ap.add_argument("--profile", default="",
+                    choices=["", "lmhead", "rows", "downproj", "calib", "ringcopy"],
                     help="run only a few launches of one group of kernels, for rocprofv3: "
                          "lmhead (the headline's GEMM and log-softmax), rows (RMSNorm, RoPE, "
                          "SwiGLU, standalone log-softmax), downproj (tp = 8 partials + combine), "
@@ -125,6 +126,16 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("pmc-calib: copied %d bytes x5" % nbytes)
+        return
+    if args.profile == "ringcopy":
+        # the ring-copy microbenchmark from a 1 MiB, a 32 MiB and a 1 GiB
+        # window, one launch each (256 workgroups x 1024 stages of 32 KB)
+        buf = torch.empty((1 << 30,), dtype=torch.uint8, device=dev).fill_(3)
+        out = torch.empty((256 * 512,), dtype=torch.int32, device=dev)
+        for win in (1 << 20, 32 << 20, 1 << 30):
+            tb.tbik_bench_copy_lds(buf, win, 1024, 256, out=out)
+        torch.cuda.synchronize()
+        log("profile ringcopy: 3 launches")
         return
 
     def timed(fn, iters, warm=3, min_ms=25.0, max_iters=1000):
