@@ -276,3 +276,25 @@ def test_gemm_noalloc_validation(L):
     assert L.tbik_gemm_workspace_bytes(256, 16384, 14336) > (16 << 20)
     assert g(FAKE, 14336, FAKE, 14336, FAKE2, 16384, None, 256, 16384, 14336, 0, None) == E_WS
     assert g(FAKE, 64, FAKE, 64, FAKE2, 64, None, 0, 5, 64, 0, None) == OK   # empty: no-op
+
+
+def test_microbench_validation(L):
+    """The ceiling microbenchmarks validate on the host like every other entry
+    point (each case below fails before any launch)."""
+    assert L.tbik_bench_mfma_flops(0, 5) == 0
+    assert L.tbik_bench_mfma_flops(2, 3) == 2 * 8 * 8 * 3 * 16384
+    assert L.tbik_bench_mfma(None, FAKE, 1, 1, None) == E_NULL
+    assert L.tbik_bench_mfma(FAKE, FAKE2, 0, 1, None) == E_SHAPE
+    assert L.tbik_bench_mfma(MISAL, FAKE2, 1, 1, None) == E_ALIGN
+    assert L.tbik_bench_hbm_read(FAKE, 100, FAKE2, 1, None) == E_SHAPE      # not a multiple of 16
+    assert L.tbik_bench_hbm_read(MISAL, 1024, FAKE2, 1, None) == E_ALIGN
+    assert L.tbik_bench_hbm_copy(FAKE, None, 1024, 1, None) == E_NULL
+    assert L.tbik_bench_hbm_copy(FAKE, FAKE2, 1024, 0, None) == E_SHAPE
+    cl = L.tbik_bench_copy_lds
+    assert cl(None, 32768, 1, FAKE2, 1, None) == E_NULL
+    assert cl(FAKE, 32768 + 16, 1, FAKE2, 1, None) == E_SHAPE               # not whole stages
+    assert cl(FAKE, 16384, 1, FAKE2, 1, None) == E_SHAPE                    # below one stage
+    assert cl(FAKE, 1 << 31, 1, FAKE2, 1, None) == E_SHAPE                  # beyond the 32-bit range
+    assert cl(FAKE, 32768, 0, FAKE2, 1, None) == E_SHAPE
+    assert cl(FAKE, 32768, 1, FAKE2, 0, None) == E_SHAPE
+    assert cl(MISAL, 32768, 1, FAKE2, 1, None) == E_ALIGN
