@@ -30,7 +30,7 @@ from tp_invariant_numerics_amd import inputs
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-MS = (1, 16, 17, 32, 33, 255, 256, 512)
+MS = (1, 16, 17, 24, 32, 33, 100, 255, 256, 512)
 KS = (1024, 2048, 4096, 5632, 14336)
 N = 4112                       # 32 x 128 + 16: ragged in every tile width
 
