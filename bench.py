@@ -477,12 +477,12 @@ def ceilings(tb, inputs, torch, dev, timed, log):
     ceil["mfma_bf16_loop_tflops"] = round(fl["f"] / t / 1e9, 1)
     buf = torch.empty((1 << 32,), dtype=torch.uint8, device=dev)    # 4 GiB
     buf.fill_(7)
-    red = torch.empty((16384 * 256,), dtype=torch.int32, device=dev)
+    red = torch.empty((65536 * 256,), dtype=torch.int32, device=dev)
     src, dst = buf[:1 << 31], buf[1 << 31:]
     # the best of a few grid sizes (one to eight workgroups of 256 per CU
     # and more): the ceiling is what the chip can sustain
     rd, cp = {}, {}
-    for blocks in (1024, 2048, 4096, 8192, 16384):
+    for blocks in (1024, 2048, 4096, 8192, 16384, 32768, 65536):
         t = timed(lambda: tb.tbik_bench_hbm_read(buf, blocks, out=red), 5, warm=2)
         rd[blocks] = round((1 << 32) / t / 1e6, 1)
         t = timed(lambda: tb.tbik_bench_hbm_copy(src, dst, blocks), 5, warm=2)

@@ -683,10 +683,21 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
       }
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
+        // EXP's NaN case is taken once per lane's four values: a NaN
+        // argument makes the chunk's sum NaN whichever element it was, and
+        // the clamped main path is harmless for NaN (it gives a finite
+        // value that the select then replaces).  Other values take exactly
+        // exp_f32's main path.
         float e[4];
+        bool nan = false;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) e[i] = exp_f32(u[k][i] - m);
+        for (int i = 0; i < 4; ++i) {
+          const float d = u[k][i] - m;
+          nan = nan || (d != d);
+          e[i] = exp_core(exp_clamp(d));
+        }
         float t = (e[0] + e[1]) + (e[2] + e[3]);
+        if (nan) t = __builtin_nanf("");
         t = t + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                     0, __builtin_bit_cast(int, t), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
         t = t + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
