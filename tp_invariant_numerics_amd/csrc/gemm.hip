@@ -423,18 +423,24 @@ struct Ring {
   int wave, nleaf, l;
   int64_t kbase;
 
+  // Copy stage `st` (this wave's share) into ring slot `slot`.  Past the
+  // last leaf the loads still run, so that every wave's vector-memory count
+  // advances by DPW per stage as the fixed waits expect, but through a
+  // resource of zero size: out of range, they read no memory.
+  __amdgpu_buffer_rsrc_t rs0;
   __device__ __forceinline__ void issue(int st, int slot) {
-    const int sc = st < nleaf ? st : nleaf - 1;
-    const int soff = (int)((kbase + (int64_t)sc * 64) * 2);
+    const bool live = st < nleaf;
+    const int soff = live ? (int)((kbase + (int64_t)st * 64) * 2) : 0;
+    const __amdgpu_buffer_rsrc_t ra = live ? rsa : rs0, rb = live ? rsb : rs0;
 #pragma unroll
     for (int i = 0; i < DPA; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsa, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
+          ra, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
           TBIK_RING_AUX_A);
 #pragma unroll
     for (int i = DPA; i < DPW; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsb, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
+          rb, (lptr_t)(ring + slot * SLOT + (wave + WAVES * i) * 64), 16, voff[i], soff, 0,
           MT <= 32 ? TBIK_THIN_AUX_B : TBIK_RING_AUX_B);
   }
 
@@ -642,6 +648,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   rg.rsb = __builtin_amdgcn_make_buffer_rsrc(
       (void *)(glu ? p.W : p.W + (int64_t)n0 * p.ldw), (short)0,
       (int)((int64_t)(glu ? p.N : brows) * p.ldw * 2), 0x00020000);
+  rg.rs0 = __builtin_amdgcn_make_buffer_rsrc((void *)p.W, (short)0, 0, 0x00020000);
 #pragma unroll
   for (int i = 0; i < DPW; ++i) {
     const int seg = wave + WAVES * i;
