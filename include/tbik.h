@@ -196,11 +196,10 @@ enum { TBIK_ROUND_ONCE = 0, TBIK_ROUND_EACH_OP = 1 };
  *   y = bf16((h * rstd) * w).
  *  x, r, y, r_out  [rows, H] bf16 with row stride ld; r_out may be NULL.
  *  w               [H] bf16.
- *  H               1 .. 65536, and H / c <= 8192 for the chunk width c: the
- *                  largest power of two <= 16 dividing H / T (T the tree's
- *                  group count; e.g. H = 65534 has c = 1 and returns
- *                  TBIK_ERR_SHAPE before any launch, whatever the
- *                  alignment);  eps >= 0.
+ *  H               1 .. 65536, any value, at any alignment of the rows
+ *                  (groups whose size has few factors of two are reduced
+ *                  over 16-leaf chunks plus a tail item, the same tree);
+ *                  eps >= 0.
  * ---------------------------------------------------------------------- */
 int tbik_rmsnorm_residual(const tbik_bf16 *x, const tbik_bf16 *r, const tbik_bf16 *w,
                           tbik_bf16 *y, tbik_bf16 *r_out, int rows, int H, int64_t ld,
@@ -286,11 +285,11 @@ int tbik_gemm_swiglu(const tbik_bf16 *A, int64_t lda, const tbik_bf16 *W_gu, int
  * library materialises each shard's partial sum in ws (what vocab-parallel
  * ranks would exchange) and combines them with the top of the tree; the
  * result is bit-identical for every tp.
- *  logits   [M, V] fp32, row stride ld.  M <= 65535; V / c <= 40944 for
- *           the chunk width c, the largest power of two <= 16 dividing
- *           V / T (V up to 655104 when V / T is a multiple of 16, at any
- *           alignment of the rows); larger V return TBIK_ERR_SHAPE before
- *           any launch (a row's chunk sums are staged in LDS).
+ *  logits   [M, V] fp32, row stride ld.  M <= 65535; a row's chunk sums
+ *           are staged in LDS: T * ceil((V / T) / 16) <= 40944, i.e. any V
+ *           up to about 655000 (655104 when V / T is a multiple of 16), at
+ *           any alignment of the rows; larger V return TBIK_ERR_SHAPE
+ *           before any launch.
  *  targets  [M] int32 in [0, V) (out-of-range targets: out_lp = NaN).
  *  out_lp   [M] fp32.
  *  ws       at least tbik_logsoftmax_workspace_bytes(M, V, tp) = M*tp*4
@@ -450,6 +449,7 @@ int tbik_swiglu_backward(const tbik_bf16 *gate, const tbik_bf16 *up, const tbik_
  *   leaf b of column j = sum over rows 64b..64b+63, in row order from +0, of
  *   dy_ij * (h_ij * rstd_i);  dw_j = TREE over the leaves as dp shards.
  * rows must then be a positive multiple of 64 and dp divide T(rows/64).
+ * H is 1 .. 65536, any value, as for the forward.
  * ws (fp32, >= tbik_rmsnorm_backward_workspace_bytes) holds, in floats:
  * rstd per row (rows rounded up to a multiple of 64), then with dw the
  * (rows/64) x H leaves and the dp x H shard nodes (kept after return). */

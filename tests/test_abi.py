@@ -177,9 +177,8 @@ def test_rowop_validation(L):
     assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 64, 64, -1.0, None) == E_ARG
     assert r(FAKE, FAKE, FAKE, MISAL, None, 1, 64, 64, 1e-6, None) == E_ALIGN
     assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 65537, 65537, 1e-6, None) == E_SHAPE
-    # 65534 = 2 x 32767: one-element chunks, 65534 of them, over the limit
-    # (refused by the launcher before it launches anything)
-    assert r(FAKE, FAKE, FAKE, FAKE2, None, 1, 65534, 65534, 1e-6, None) == E_SHAPE
+    # (every H in 1..65536 is accepted; odd group sizes such as 65534 =
+    # 2 x 32767 are checked against the oracle on the GPU)
     ro = L.tbik_rope
     assert ro(FAKE, FAKE, None, FAKE, FAKE, 1, 1, 128, 128, 16, None) == E_NULL
     assert ro(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 130, 136, 16, None) == E_SHAPE
@@ -198,10 +197,10 @@ def test_rowop_validation(L):
                                       None) == OK
     ls = L.tbik_logsoftmax_gather
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 3, FAKE, 1 << 20, None) == E_TP
-    # an odd V has one-element chunks: more than 40944 chunk sums do not fit
-    # the LDS beside the kernel's own 64 bytes (refused by the launcher
-    # before it launches anything)
-    assert ls(FAKE, 40945, FAKE, FAKE, 1, 40945, 1, FAKE, 1 << 20, None) == E_SHAPE
+    # a row stages T * ceil(G / 16) chunk sums in LDS: with V = 655105 (odd,
+    # one group) that is 40945 values, more than fit beside the kernel's own
+    # 64 bytes (refused by the launcher before it launches anything)
+    assert ls(FAKE, 655105, FAKE, FAKE, 1, 655105, 1, FAKE, 1 << 20, None) == E_SHAPE
     assert ls(FAKE, 24, FAKE, FAKE, 2, 12, 8, FAKE, 1 << 20, None) == E_TP   # T(12) = 4
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 1, None, 0, None) == E_WS
     assert ls(FAKE, 8, FAKE, FAKE, 2, 8, 1, FAKE, 4, None) == E_WS

@@ -289,7 +289,8 @@ def test_gemm_strided_batched_equals_single(orc):
 @pytest.mark.parametrize("rows,H", [(1, 4096), (7, 4096), (256, 4096), (4096, 4096),
                                     (5, 2048), (3, 5120), (4, 1000), (9, 96), (2, 8), (3, 4104),
                                     (3, 64), (2, 512), (2, 16384), (2, 65536), (3, 1),
-                                    (2, 24576)])
+                                    (2, 24576), (2, 65534), (3, 65535), (2, 10001), (2, 8193),
+                                    (2, 49154)])
 def test_rmsnorm_bitexact(orc, rows, H):
     x = inputs.outlier_bf16((rows, H), 8000 + H)
     r = inputs.outlier_bf16((rows, H), 8001 + H)
@@ -411,7 +412,8 @@ def test_logprob_path_fused_max_bitexact(orc, tp):
 @pytest.mark.parametrize("M,V,tps", [(8, 151936, (1, 2, 4, 8)), (16, 32000, (1, 2, 4, 8)),
                                      (5, 1000, (1, 2, 4, 8)), (3, 12, (1, 2, 4)),
                                      (4, 7, (1,)), (2, 655104, (1, 8)), (2, 40943, (1,)),
-                                     (3, 1, (1,))])
+                                     (3, 1, (1,)), (3, 50257, (1,)), (2, 100277, (1,)),
+                                     (2, 71702, (1, 2)), (2, 655100, (1, 4))])
 def test_logsoftmax_bitexact(orc, M, V, tps):
     rng = np.random.default_rng(V)
     logits = (rng.standard_normal((M, V)) * 3).astype(np.float32)
@@ -462,7 +464,9 @@ def test_logsoftmax_special_values(orc, V):
 
 # ------------------------------------------------------------------ causal softmax
 @pytest.mark.parametrize("B,Lq,Lk,offset", [(2, 512, 512, 0), (3, 64, 128, 64), (1, 9, 24, 0),
-                                            (2, 130, 256, 0), (2, 64, 64, 0), (1, 512, 1024, 512)])
+                                            (2, 130, 256, 0), (2, 64, 64, 0), (1, 512, 1024, 512),
+                                            (1, 5, 10001, 9990), (1, 3, 65535, 65530),
+                                            (1, 4, 16386, 16380)])
 def test_softmax_causal_bitexact(orc, B, Lq, Lk, offset):
     rng = np.random.default_rng(Lk + offset)
     S = (rng.standard_normal((B, Lq, Lk)) * 30).astype(np.float32)

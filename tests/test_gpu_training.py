@@ -146,7 +146,9 @@ def test_swiglu_backward_all_bf16_gates(orc):
 
 @pytest.mark.parametrize("rows,H,with_dr", [(64, 4096, True), (512, 4096, False),
                                             (4096, 4096, True), (128, 5120, True),
-                                            (192, 1000, True), (64, 64, False)])
+                                            (192, 1000, True), (64, 64, False),
+                                            (64, 65534, True), (64, 10001, False),
+                                            (128, 65535, True)])
 def test_rmsnorm_backward_bitexact(orc, rows, H, with_dr):
     x = inputs.outlier_bf16((rows, H), 10900 + H)
     r = inputs.outlier_bf16((rows, H), 10901 + H)

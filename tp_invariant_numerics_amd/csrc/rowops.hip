@@ -64,6 +64,50 @@ __device__ __forceinline__ float lds_row_tree(float *buf_a, float *buf_b, int gc
   return root[0];
 }
 
+// ---- rows whose groups are not whole chunks -----------------------------------
+// A group of G = 16q + r leaves (r < 16): PAIR over it is the right fold of
+// perfect trees over the binary decomposition of G, whose blocks of 16 and
+// more are perfect trees over aligned 16-leaf chunks.  So it equals PAIR
+// over the sequence of q + (r > 0) items -- the q chunk trees, then PAIR over
+// the r tail leaves -- appending the tail's value carries through the low
+// blocks exactly as the low bits of G do.  This lets a row whose G has few
+// factors of two (so that whole-group chunks would be 1 or 2 leaves wide)
+// stage about G/16 values per group.
+struct TailRows {
+  int G, q, r, gs;
+  __device__ __forceinline__ TailRows(int n, int T)
+      : G(n / T), q((n / T) >> 4), r((n / T) & 15), gs(((n / T) >> 4) + (((n / T) & 15) ? 1 : 0)) {}
+  // item `it` (group it / gs): first leaf and leaf count
+  __device__ __forceinline__ void item(int it, int &start, int &len) const {
+    const int g = it / gs, k = it - g * gs;
+    start = g * G + 16 * k;
+    len = k < q ? 16 : r;
+  }
+};
+
+// PAIR over v[0..n), 1 <= n <= 16: neighbours added level by level, an odd
+// last element carried up unchanged (for n = 16 the perfect tree).
+__device__ __forceinline__ float pair16(float (&v)[16], int n) {
+  if (n == 16) return chunk_tree<16>(v);
+#pragma unroll
+  for (int lev = 0; lev < 4; ++lev) {
+    if (n > 1) {
+      float last = 0.0f;                         // v[n - 1], read by static indices
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        if (e == n - 1) last = v[e];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < n / 2) v[i] = v[2 * i] + v[2 * i + 1];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if ((n & 1) && i == n / 2) v[i] = last;
+      n = (n + 1) >> 1;
+    }
+  }
+  return v[0];
+}
+
 // ---- chunk loads and stores ---------------------------------------------------
 // NT = true: non-temporal access, for data touched once by a layout in which
 // each load or store instruction covers whole cache lines (consecutive lanes,
@@ -350,6 +394,46 @@ k_rmsnorm_pair(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t
   }
 }
 
+// Rows whose group size has too few factors of two for whole-group chunks
+// (H / c > 8192 chunk sums): the sum of squares over 16-leaf chunks plus one
+// tail item per group (TailRows), element-wise accesses; the output pass is
+// element by element.
+template <bool EACH>
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm_tail(const uint16_t *x, const uint16_t *r, const uint16_t *w, uint16_t *y,
+               uint16_t *r_out, int H, int64_t ld, float eps, int T) {
+  extern __shared__ float lds[];
+  const TailRows L(H, T);
+  const int n_it = T * L.gs;
+  const int64_t base = (int64_t)blockIdx.x * ld;
+  for (int it = threadIdx.x; it < n_it; it += kRowThreads) {
+    int start, len;
+    L.item(it, start, len);
+    float sq[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      sq[e] = 0.0f;
+      if (e < len) {
+        float h = bf2f(x[base + start + e]) + bf2f(r[base + start + e]);
+        if (EACH) h = bf_round(h);
+        if (r_out) r_out[base + start + e] = f2bf(h);
+        sq[e] = h * h;
+      }
+    }
+    lds[it] = pair16(sq, len);
+  }
+  __syncthreads();
+  const float ss = lds_row_tree<kRowThreads>(lds, lds + n_it, L.gs, T);
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)H + eps);
+  for (int i = threadIdx.x; i < H; i += kRowThreads) {
+    float h = bf2f(x[base + i]) + bf2f(r[base + i]);
+    if (EACH) h = bf_round(h);
+    float n = h * rstd;
+    if (EACH) n = bf_round(n);
+    y[base + i] = f2bf(n * bf2f(w[i]));
+  }
+}
+
 template <bool EACH>
 static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t *w,
                             uint16_t *y, uint16_t *r_out, int rows, int H, int64_t ld,
@@ -363,9 +447,16 @@ static int launch_rmsnorm_t(const uint16_t *x, const uint16_t *r, const uint16_t
   const int ch = chunk_for(H / T);
   const bool vec = bf16_vec_ok(ch, al);
   const int nch = H / ch;
-  if (nch > 8192) return TBIK_ERR_SHAPE;
-  const int gc = nch / T;
   dim3 grid((unsigned)rows), block(kRowThreads);
+  if (nch > 8192) {
+    // chunk sums and their ping-pong copy within 64 KB of LDS
+    const int n_it = T * ((H / T) / 16 + ((H / T) % 16 ? 1 : 0));
+    if (n_it > 8192) return TBIK_ERR_SHAPE;
+    hipLaunchKernelGGL((k_rmsnorm_tail<EACH>), grid, block, 2 * (size_t)n_it * sizeof(float), s, x,
+                       r, w, y, r_out, H, ld, eps, T);
+    return check_launch();
+  }
+  const int gc = nch / T;
   if (vec && TBIK_RMS_PAIR && ch == 16 && H % (8 * kRowThreads) == 0 && (gc & (gc - 1)) == 0 &&
       gc <= 32) {
     switch (H / (8 * kRowThreads)) {
@@ -621,6 +712,81 @@ __device__ __forceinline__ void lds_pair_inplace(float *buf, int m, int groups) 
   }
 }
 
+// The last steps of a row, by one thread: the group PAIR values (lds[g*gs]
+// after the in-place PAIR levels) form the tp shard nodes by the perfect
+// tree over T/tp groups each, the nodes their perfect tree; then LOG and the
+// target's logprob.
+__device__ __forceinline__ void lsm_finish(const float *lds, int gs, int T, int tp, int row,
+                                           float *shard, float *out, const float *xr, float m,
+                                           const int32_t *targets, int V) {
+  const int per = T / tp;
+  float nodes[8];
+  for (int t = 0; t < tp; ++t) {
+    float u[8];
+    for (int q = 0; q < per; ++q) u[q] = lds[(t * per + q) * gs];
+    for (int w = per; w > 1; w >>= 1)
+      for (int q = 0; q < w / 2; ++q) u[q] = u[2 * q] + u[2 * q + 1];
+    nodes[t] = u[0];
+    shard[(int64_t)row * tp + t] = u[0];
+  }
+  for (int w = tp; w > 1; w >>= 1)
+    for (int q = 0; q < w / 2; ++q) nodes[q] = nodes[2 * q] + nodes[2 * q + 1];
+  const int tgt = targets[row];
+  if (tgt < 0 || tgt >= V) {
+    out[row] = __builtin_nanf("");
+    return;
+  }
+  out[row] = (xr[tgt] - m) - log_f32(nodes[0]);
+}
+
+// Row maximum (order-free): from partial maxima when given, else from the
+// logits element by element.  Every thread returns the row's maximum.
+__device__ __forceinline__ float lsm_row_max(const float *xr, int V, const float *pmax,
+                                             int64_t ld_pmax, int npmax, int row, float *red) {
+  float m = -__builtin_inff();
+  if (pmax) {
+    for (int b = threadIdx.x; b < npmax; b += kLsmThreads)
+      m = __builtin_fmaxf(m, pmax[(int64_t)row * ld_pmax + b]);
+  } else {
+    for (int i = threadIdx.x; i < V; i += kLsmThreads) m = __builtin_fmaxf(m, xr[i]);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int q = 1; q < kLsmThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
+  return m;
+}
+
+// Rows whose group size has too few factors of two for whole-group chunks to
+// fit LDS (G = V / T odd, say): 16-leaf chunks plus one tail item per group
+// (TailRows), element-wise loads (group starts need not be aligned); the
+// maximum and the rest of the row as in the main kernel.
+__global__ void __launch_bounds__(kLsmThreads)
+k_logsoftmax_row_tail(const float *logits, int64_t ld, const int32_t *targets, int V, int T,
+                      int tp, float *shard, float *out, const float *pmax, int64_t ld_pmax,
+                      int npmax) {
+  extern __shared__ float lds[];
+  __shared__ float red[kLsmThreads / 64];
+  const int row = blockIdx.x;
+  const float *xr = logits + (int64_t)row * ld;
+  const TailRows L(V, T);
+  const float m = lsm_row_max(xr, V, pmax, ld_pmax, npmax, row, red);
+  for (int it = threadIdx.x; it < T * L.gs; it += kLsmThreads) {
+    int start, len;
+    L.item(it, start, len);
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = e < len ? exp_f32(xr[start + e] - m) : 0.0f;
+    lds[it] = pair16(v, len);
+  }
+  __syncthreads();
+  lds_pair_inplace<kLsmThreads>(lds, L.gs, T);
+  if (threadIdx.x == 0) lsm_finish(lds, L.gs, T, tp, row, shard, out, xr, m, targets, V);
+}
+
 template <int CH, bool AL>
 __global__ void __launch_bounds__(kLsmThreads)
 k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V, int T, int tp,
@@ -716,25 +882,7 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   }
   __syncthreads();
   lds_pair_inplace<kLsmThreads>(lds, gc, T);
-  if (threadIdx.x != 0) return;
-  const int per = T / tp;
-  float nodes[8];
-  for (int t = 0; t < tp; ++t) {
-    float u[8];
-    for (int q = 0; q < per; ++q) u[q] = lds[(t * per + q) * gc];
-    for (int w = per; w > 1; w >>= 1)
-      for (int q = 0; q < w / 2; ++q) u[q] = u[2 * q] + u[2 * q + 1];
-    nodes[t] = u[0];
-    shard[(int64_t)row * tp + t] = u[0];
-  }
-  for (int w = tp; w > 1; w >>= 1)
-    for (int q = 0; q < w / 2; ++q) nodes[q] = nodes[2 * q] + nodes[2 * q + 1];
-  const int tgt = targets[row];
-  if (tgt < 0 || tgt >= V) {
-    out[row] = __builtin_nanf("");
-    return;
-  }
-  out[row] = (xr[tgt] - m) - log_f32(nodes[0]);
+  if (threadIdx.x == 0) lsm_finish(lds, gc, T, tp, row, shard, out, xr, m, targets, V);
 }
 
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out, int M,
@@ -749,7 +897,17 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
   size_t lds = (size_t)nch * sizeof(float);
   // one float per chunk in dynamic LDS, beside the kernel's static per-wave
   // reduction buffer, within a workgroup's 160 KB
-  if (lds + (size_t)(kLsmThreads / 64) * sizeof(float) > 160 * 1024) return TBIK_ERR_SHAPE;
+  constexpr size_t kLdsCap = 160 * 1024 - (size_t)(kLsmThreads / 64) * sizeof(float);
+  if (lds > kLdsCap) {
+    // G with few factors of two: 16-leaf chunks plus one tail value per group
+    const size_t lt = (size_t)T * (G / 16 + (G % 16 ? 1 : 0)) * sizeof(float);
+    if (lt > kLdsCap) return TBIK_ERR_SHAPE;
+    (void)hipFuncSetAttribute((const void *)k_logsoftmax_row_tail,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lt);
+    hipLaunchKernelGGL(k_logsoftmax_row_tail, dim3((unsigned)M), dim3(kLsmThreads), lt, s, logits,
+                       ld, targets, V, T, tp, ws, out, pmax, ld_pmax, npmax);
+    return check_launch();
+  }
   if (lds < (size_t)TBIK_LSM_LDS_MIN) lds = TBIK_LSM_LDS_MIN;
   float *shard = ws;
   dim3 grid((unsigned)M), block(kLsmThreads);
@@ -773,6 +931,45 @@ int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, f
 // =============================================================================
 // causal softmax: one workgroup per (batch, query row).
 // =============================================================================
+// Rows whose group size has too few factors of two for whole-group chunks
+// (Lk / c > 8192 chunk sums): 16-leaf chunks plus one tail item per group
+// (TailRows), element-wise accesses; otherwise as k_softmax_causal.
+__global__ void __launch_bounds__(kRowThreads)
+k_softmax_causal_tail(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, int64_t ld_p,
+                      int64_t stride_p, int Lq, int Lk, int offset, float scale, int T) {
+  extern __shared__ float lds[];
+  __shared__ float red[kRowThreads / 64];
+  const int i = blockIdx.x, b = blockIdx.y;
+  const float *srow = S + (int64_t)b * stride_s + (int64_t)i * ld_s;
+  uint16_t *prow = P + (int64_t)b * stride_p + (int64_t)i * ld_p;
+  const int last = i + offset;
+  const TailRows L(Lk, T);
+  const int n_it = T * L.gs;
+  float m = -__builtin_inff();
+  for (int k = threadIdx.x; k < Lk; k += kRowThreads)
+    if (k <= last) m = __builtin_fmaxf(m, srow[k] * scale);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int q = 1; q < kRowThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
+  for (int it = threadIdx.x; it < n_it; it += kRowThreads) {
+    int start, len;
+    L.item(it, start, len);
+    float v[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      v[e] = (e < len && start + e <= last) ? exp_f32(srow[start + e] * scale - m) : 0.0f;
+    lds[it] = pair16(v, len);
+  }
+  __syncthreads();
+  const float ssum = lds_row_tree<kRowThreads>(lds, lds + n_it, L.gs, T);
+  for (int k = threadIdx.x; k < Lk; k += kRowThreads)
+    prow[k] = f2bf(k <= last ? exp_f32(srow[k] * scale - m) / ssum : 0.0f);
+}
+
 template <int CH, bool AL>
 __global__ void __launch_bounds__(kRowThreads)
 k_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16_t *P, int64_t ld_p,
@@ -895,9 +1092,15 @@ int launch_softmax_causal(const float *S, int64_t ld_s, int64_t stride_s, uint16
                                                                      : elem_align(P, stride_p, 2);
   const bool vec = f32_vec_ok(ch, as) && bf16_vec_ok(ch, ap);
   const int nch = Lk / ch;
-  if (nch > 8192) return TBIK_ERR_SHAPE;
   const size_t lds = 2 * (size_t)nch * sizeof(float);
   dim3 grid((unsigned)Lq, (unsigned)batch), block(kRowThreads);
+  if (nch > 8192) {
+    const int n_it = T * ((Lk / T) / 16 + ((Lk / T) % 16 ? 1 : 0));
+    if (n_it > 8192) return TBIK_ERR_SHAPE;
+    hipLaunchKernelGGL(k_softmax_causal_tail, grid, block, 2 * (size_t)n_it * sizeof(float), s, S,
+                       ld_s, stride_s, P, ld_p, stride_p, Lq, Lk, offset, scale, T);
+    return check_launch();
+  }
   switch (ch * 2 + (vec ? 1 : 0)) {
 #define TBIK_SMC_CASE(CW, VEC)                                                                    \
   case CW * 2 + VEC:                                                                              \
@@ -1049,6 +1252,63 @@ int launch_swiglu_backward(const uint16_t *g, const uint16_t *u, const uint16_t 
 // tree (same chunks, same LDS tree, same bits), dot = TREE(g*h) with
 // g = dy*w, c = (dot * ((rstd*rstd)*rstd)) / H, dh = bf16(((rstd*g) - (c*h)) + dr).
 // rstd of the row goes to rstd_out for the weight gradient.
+// Rows whose group size has too few factors of two for whole-group chunks
+// (H / c > 8192 chunk sums): both row trees over 16-leaf chunks plus one tail
+// item per group (TailRows), element-wise accesses; otherwise as
+// k_rmsnorm_bwd.
+__global__ void __launch_bounds__(kRowThreads)
+k_rmsnorm_bwd_tail(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uint16_t *dy,
+                   const uint16_t *dr, uint16_t *dh, float *rstd_out, int H, int64_t ld,
+                   float eps, int T) {
+  extern __shared__ float lds[];
+  const TailRows L(H, T);
+  const int n_it = T * L.gs;
+  const int64_t base = (int64_t)blockIdx.x * ld;
+  for (int it = threadIdx.x; it < n_it; it += kRowThreads) {
+    int start, len;
+    L.item(it, start, len);
+    float a[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      a[e] = 0.0f;
+      if (e < len) {
+        const float h = bf2f(x[base + start + e]) + bf2f(r[base + start + e]);
+        a[e] = h * h;
+      }
+    }
+    lds[it] = pair16(a, len);
+  }
+  __syncthreads();
+  const float ss = lds_row_tree<kRowThreads>(lds, lds + n_it, L.gs, T);
+  const float rstd = 1.0f / __builtin_sqrtf(ss / (float)H + eps);
+  __syncthreads();                       // every thread has read the root
+  for (int it = threadIdx.x; it < n_it; it += kRowThreads) {
+    int start, len;
+    L.item(it, start, len);
+    float a[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      a[e] = 0.0f;
+      if (e < len) {
+        const int64_t o = base + start + e;
+        a[e] = (bf2f(dy[o]) * bf2f(w[start + e])) * (bf2f(x[o]) + bf2f(r[o]));
+      }
+    }
+    lds[it] = pair16(a, len);
+  }
+  __syncthreads();
+  const float dot = lds_row_tree<kRowThreads>(lds, lds + n_it, L.gs, T);
+  const float c = (dot * ((rstd * rstd) * rstd)) / (float)H;
+  for (int k = threadIdx.x; k < H; k += kRowThreads) {
+    const int64_t o = base + k;
+    const float h = bf2f(x[o]) + bf2f(r[o]);
+    float v = (rstd * (bf2f(dy[o]) * bf2f(w[k]))) - (c * h);
+    if (dr) v = v + bf2f(dr[o]);
+    dh[o] = f2bf(v);
+  }
+  if (threadIdx.x == 0) rstd_out[blockIdx.x] = rstd;
+}
+
 template <int CH, bool AL>
 __global__ void __launch_bounds__(kRowThreads)
 k_rmsnorm_bwd(const uint16_t *x, const uint16_t *r, const uint16_t *w, const uint16_t *dy,
@@ -1284,12 +1544,16 @@ int launch_rmsnorm_backward(const uint16_t *x, const uint16_t *r, const uint16_t
   const int ch = chunk_for(H / T);
   const bool vec = bf16_vec_ok(ch, al);
   const int nch = H / ch;
-  if (nch > 8192) return TBIK_ERR_SHAPE;
   const size_t lds = 2 * (size_t)nch * sizeof(float);
   float *rstd = ws;                                 // [rows]
   const dim3 grid((unsigned)rows), block(kRowThreads);
   const int gc = nch / T;
-  if (vec && nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
+  if (nch > 8192) {
+    const int n_it = T * ((H / T) / 16 + ((H / T) % 16 ? 1 : 0));
+    if (n_it > 8192) return TBIK_ERR_SHAPE;
+    hipLaunchKernelGGL(k_rmsnorm_bwd_tail, grid, block, 2 * (size_t)n_it * sizeof(float), s, x, r,
+                       w, dy, dr, dh, rstd, H, ld, eps, T);
+  } else if (vec && nch <= kRowThreads && (gc & (gc - 1)) == 0 && 64 % gc == 0) {
     switch (ch) {
       case 16: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<16>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
       case 8: hipLaunchKernelGGL(k_rmsnorm_bwd_reg<8>, grid, block, 0, s, x, r, w, dy, dr, dh, rstd, H, ld, eps, T, gc); break;
