@@ -79,6 +79,22 @@ def test_repeat_row_kernels():
     _repeat("swiglu 4096x14336", lambda: (tb.tbik_swiglu(g, u),), (g, u))
 
 
+def test_repeat_tail_row_kernels():
+    """The kernels for groups that are not whole chunks (odd group sizes)."""
+    x = inputs.outlier_bf16((64, 65534), 14250, device=DEV)
+    r = inputs.outlier_bf16((64, 65534), 14251, device=DEV)
+    w = inputs.normal_bf16((65534,), 14252, std=0.1, mean=1.0, device=DEV)
+    dy = inputs.normal_bf16((64, 65534), 14253, device=DEV)
+    _repeat("rmsnorm H 65534", lambda: tb.tbik_rmsnorm_residual(x, r, w, 1e-6), (x, r, w))
+    _repeat("rmsnorm backward H 65534",
+            lambda: tb.tbik_rmsnorm_backward(x, r, w, dy, None, 1e-6, dp=1)[:2], (x, r, w, dy))
+    lg = inputs.normal_bf16((64, 50257), 14254, std=3.0, device=DEV).float()
+    tgt = inputs.uniform_int(64, 50257, 14255, device=DEV)
+    _repeat("logsoftmax V 50257", lambda: tb.tbik_logsoftmax_gather(lg, tgt, 1)[:1], (lg, tgt))
+    S = inputs.normal_bf16((1, 32, 10001), 14256, std=30.0, device=DEV).float()
+    _repeat("softmax causal Lk 10001", lambda: (tb.tbik_softmax_causal(S, 9970, 0.0884),), (S,))
+
+
 @pytest.mark.parametrize("tp", [1, 4])
 def test_repeat_logprob_path(tp):
     M, K, V = 512, 4096, 151936
