@@ -12,7 +12,10 @@
 // (2^c divides the group size, so PAIR's first c levels are perfect trees
 // over exactly these chunks); (2) PAIR's remaining levels run level by level
 // in LDS (ping-pong buffers, one barrier per level, odd last element carried);
-// (3) the perfect tree over the T group sums.  No atomics.
+// (3) the perfect tree over the T group sums.  When the group size has too
+// few factors of two for such chunks to fit LDS, the *_tail kernels use
+// 16-leaf chunks plus one tail item per group (TailRows), the same tree.
+// No atomics.
 #include "tbik_device.h"
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
