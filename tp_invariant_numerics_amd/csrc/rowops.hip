@@ -695,18 +695,22 @@ constexpr int kLsmThreads = TBIK_LSM_THREADS;
 #define TBIK_LSM_KB 8
 #endif
 
-// PAIR over `groups` groups of m values each, group g at buf[g*m ..): the
-// group's PAIR value is left at buf[g*m].  All threads of the block call it.
+// PAIR over each of `groups` groups of m values, group g at buf[g*m ..), in
+// place, level by level (node i of a level sits at i * 2^level, so the
+// carried odd element never moves); the group's PAIR value is left at
+// buf[g*m].  groups is a power of two dividing NT: each group gets NT/groups
+// threads (no division in the index arithmetic).  All threads of the block
+// call it; every level ends with a block barrier.
 template <int NT>
 __device__ __forceinline__ void lds_pair_inplace(float *buf, int m, int groups) {
-  const int m0 = m;
+  const int sh = __builtin_ctz((unsigned)(NT / groups));
+  float *gb = buf + (threadIdx.x >> sh) * m;
+  const int r = threadIdx.x & ((1 << sh) - 1);
   int s = 1;
   while (m > 1) {
     const int half = m >> 1;
-    for (int idx = threadIdx.x; idx < groups * half; idx += NT) {
-      const int g = idx / half;
-      const int i = idx - g * half;
-      float *b = buf + g * m0 + 2 * i * s;
+    for (int i = r; i < half; i += 1 << sh) {
+      float *b = gb + 2 * i * s;
       b[0] = b[0] + b[s];
     }
     __syncthreads();
@@ -716,12 +720,14 @@ __device__ __forceinline__ void lds_pair_inplace(float *buf, int m, int groups) 
 }
 
 // The last steps of a row, by one thread: the group PAIR values (lds[g*gs]
-// after the in-place PAIR levels) form the tp shard nodes by the perfect
+// after lds_pair_inplace) form the tp shard nodes by the perfect
 // tree over T/tp groups each, the nodes their perfect tree; then LOG and the
-// target's logprob.
+// target's logprob.  The caller has read the target index tgt and its logit
+// xt (any value when tgt is out of range) before the row's sum, so that
+// neither read waits at the end of the row.
 __device__ __forceinline__ void lsm_finish(const float *lds, int gs, int T, int tp, int row,
-                                           float *shard, float *out, const float *xr, float m,
-                                           const int32_t *targets, int V) {
+                                           float *shard, float *out, float xt, float m, int tgt,
+                                           int V) {
   const int per = T / tp;
   float nodes[8];
   for (int t = 0; t < tp; ++t) {
@@ -734,12 +740,33 @@ __device__ __forceinline__ void lsm_finish(const float *lds, int gs, int T, int 
   }
   for (int w = tp; w > 1; w >>= 1)
     for (int q = 0; q < w / 2; ++q) nodes[q] = nodes[2 * q] + nodes[2 * q + 1];
-  const int tgt = targets[row];
   if (tgt < 0 || tgt >= V) {
     out[row] = __builtin_nanf("");
     return;
   }
-  out[row] = (xr[tgt] - m) - log_f32(nodes[0]);
+  out[row] = (xt - m) - log_f32(nodes[0]);
+}
+
+// The target's logit, for thread 0 (the one that finishes the row).
+__device__ __forceinline__ float lsm_target_logit(const float *xr, int tgt, int V) {
+  return (threadIdx.x == 0 && tgt >= 0 && tgt < V) ? xr[tgt] : 0.0f;
+}
+
+// This thread's share of a row's partial maxima: four loads in flight per
+// round (one round up to 4 x kLsmThreads values).
+__device__ __forceinline__ float lsm_pmax_part(const float *pm, int npmax) {
+  float m = -__builtin_inff();
+  for (int b0 = threadIdx.x; b0 < npmax; b0 += 4 * kLsmThreads) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = b0 + i * kLsmThreads;
+      v[i] = b < npmax ? pm[b] : -__builtin_inff();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = __builtin_fmaxf(m, v[i]);
+  }
+  return m;
 }
 
 // Row maximum (order-free): from partial maxima when given, else from the
@@ -748,8 +775,7 @@ __device__ __forceinline__ float lsm_row_max(const float *xr, int V, const float
                                              int64_t ld_pmax, int npmax, int row, float *red) {
   float m = -__builtin_inff();
   if (pmax) {
-    for (int b = threadIdx.x; b < npmax; b += kLsmThreads)
-      m = __builtin_fmaxf(m, pmax[(int64_t)row * ld_pmax + b]);
+    m = lsm_pmax_part(pmax + (int64_t)row * ld_pmax, npmax);
   } else {
     for (int i = threadIdx.x; i < V; i += kLsmThreads) m = __builtin_fmaxf(m, xr[i]);
   }
@@ -776,7 +802,9 @@ k_logsoftmax_row_tail(const float *logits, int64_t ld, const int32_t *targets, i
   const int row = blockIdx.x;
   const float *xr = logits + (int64_t)row * ld;
   const TailRows L(V, T);
+  const int tgt = threadIdx.x == 0 ? targets[row] : 0;
   const float m = lsm_row_max(xr, V, pmax, ld_pmax, npmax, row, red);
+  const float xt = lsm_target_logit(xr, tgt, V);
   for (int it = threadIdx.x; it < T * L.gs; it += kLsmThreads) {
     int start, len;
     L.item(it, start, len);
@@ -787,7 +815,7 @@ k_logsoftmax_row_tail(const float *logits, int64_t ld, const int32_t *targets, i
   }
   __syncthreads();
   lds_pair_inplace<kLsmThreads>(lds, L.gs, T);
-  if (threadIdx.x == 0) lsm_finish(lds, L.gs, T, tp, row, shard, out, xr, m, targets, V);
+  if (threadIdx.x == 0) lsm_finish(lds, L.gs, T, tp, row, shard, out, xt, m, tgt, V);
 }
 
 template <int CH, bool AL>
@@ -800,17 +828,57 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   const float *xr = logits + (int64_t)row * ld;
   const int nch = V / CH;
   const int gc = nch / T;
+  const int tgt = threadIdx.x == 0 ? targets[row] : 0;
+  // Quad path (16-element chunks, aligned rows).  A chunk is read by a quad
+  // of lanes, lane j of the quad holding its elements 4j..4j+3, so every load
+  // instruction of a wave covers 1 KB contiguously.  Each lane reduces its
+  // four values (the chunk tree's level of 4), and two quad-permute adds
+  // finish the chunk's perfect tree: (q0 + q1) + (q2 + q3) -- addition is
+  // commutative, so every lane of the quad ends with the same bits.
+  // A unit is 16 chunks (1 KB, one load of a wave).  Wave w takes units w,
+  // w + NWV, w + 2 NWV, ... counted from the row's end, so the waves' shares
+  // differ by at most one unit, KB units per step.  Buffer loads from a
+  // resource of the row's size: a partial last unit reads zeros past the
+  // row (those chunks are not stored); in a wave's last step the units past
+  // its share get an offset beyond the resource, which reads nothing, so
+  // that every step issues its KB loads together.  Non-temporal loads: the row is read once
+  // here when its maximum comes from the GEMM.  The first step's loads go
+  // out before the row maximum is formed (they do not depend on it).
+  constexpr bool QUAD = AL && CH == 16 && TBIK_LSM_QUAD;
+  constexpr int NWV = kLsmThreads / 64;
+  constexpr int KB = TBIK_LSM_KB;
+  const int lane = threadIdx.x & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);   // wave-uniform
+  const int qd = lane >> 2, j = lane & 3;
+  const int nunit = (nch + 15) / 16;
+  const int cnt = wv < nunit ? (nunit - 1 - wv) / NWV + 1 : 0;
+  f32x4 ua[KB];
+  __amdgpu_buffer_rsrc_t rs;
+  // the chunk index of step i0's k-th unit for this lane
+  auto chunk = [&](int i0, int k) { return (nunit - 1 - wv - NWV * (i0 + k)) * 16 + qd; };
+  auto issue = [&](f32x4 (&u)[KB], int i0) {
+    const int n = cnt - i0 < KB ? cnt - i0 : KB;
+#pragma unroll
+    for (int k = 0; k < KB; ++k) {
+      const int off = k < n ? chunk(i0, k) * 64 + 16 * j : 0x40000000;
+      u[k] = __builtin_bit_cast(
+          f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, TBIK_LSM_NT ? 2 : 0));
+    }
+  };
+  if constexpr (QUAD) {
+    rs = __builtin_amdgcn_make_buffer_rsrc((void *)xr, (short)0, nch * 64, 0x00020000);
+    issue(ua, 0);
+  }
   float m = -__builtin_inff();
   if (pmax) {
     // the row maximum from partial maxima (e.g. fused into the GEMM that
     // produced the logits): the logits are then read once
-    for (int b = threadIdx.x; b < npmax; b += kLsmThreads)
-      m = __builtin_fmaxf(m, pmax[(int64_t)row * ld_pmax + b]);
+    m = lsm_pmax_part(pmax + (int64_t)row * ld_pmax, npmax);
   } else if constexpr (AL && CH >= 4) {
     // the maximum is order-free: consecutive lanes read consecutive 16 bytes
     for (int i = threadIdx.x; i < nch * (CH / 4); i += kLsmThreads) {
-      const f32x4 u = *reinterpret_cast<const f32x4 *>(xr + 4 * i);
-      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(u[0], u[1]), __builtin_fmaxf(u[2], u[3])));
+      const f32x4 v = *reinterpret_cast<const f32x4 *>(xr + 4 * i);
+      m = __builtin_fmaxf(m, __builtin_fmaxf(__builtin_fmaxf(v[0], v[1]), __builtin_fmaxf(v[2], v[3])));
     }
   } else {
     for (int ch = threadIdx.x; ch < nch; ch += kLsmThreads) {
@@ -827,36 +895,17 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   m = red[0];
 #pragma unroll
   for (int q = 1; q < kLsmThreads / 64; ++q) m = __builtin_fmaxf(m, red[q]);
-  if constexpr (AL && CH == 16 && TBIK_LSM_QUAD) {
-    // A chunk is read by a quad of lanes, lane j of the quad holding its
-    // elements 4j..4j+3, so every load instruction of a wave covers 1 KB
-    // contiguously.  Each lane reduces its four values (the chunk tree's
-    // level of 4), and two quad-permute adds finish the chunk's perfect
-    // tree: (q0 + q1) + (q2 + q3) -- addition is commutative, so every lane
-    // of the quad ends with the same bits.  Blocks of 16*KB chunks per wave,
-    // walked from the row's end, with non-temporal loads (the row is read
-    // once here when its maximum comes from the GEMM).
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int qd = lane >> 2, j = lane & 3;
-    constexpr int NWV = kLsmThreads / 64;
-    constexpr int KB = TBIK_LSM_KB;                       // 16-chunk loads per block
-    const int nblk = (nch + 16 * KB - 1) / (16 * KB);
-    for (int b = nblk - 1 - wave; b >= 0; b -= NWV) {
-      f32x4 u[KB];
-      int c[KB];
+  const float xt = lsm_target_logit(xr, tgt, V);
+  if constexpr (QUAD) {
+    // EXP's NaN case is taken once per lane's four values: a NaN argument
+    // makes the chunk's sum NaN whichever element it was, and the clamped
+    // main path is harmless for NaN (it gives a finite value that the select
+    // then replaces).  Other values take exactly exp_f32's main path.
+    auto consume = [&](const f32x4 (&u)[KB], int i0) {
+      const int n = cnt - i0 < KB ? cnt - i0 : KB;
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
-        c[k] = b * 16 * KB + 16 * k + qd;
-        const int cc = c[k] < nch ? c[k] : nch - 1;      // ragged last block: a valid address
-        u[k] = vload<TBIK_LSM_NT != 0>(reinterpret_cast<const f32x4 *>(xr + cc * 16 + 4 * j));
-      }
-#pragma unroll
-      for (int k = 0; k < KB; ++k) {
-        // EXP's NaN case is taken once per lane's four values: a NaN
-        // argument makes the chunk's sum NaN whichever element it was, and
-        // the clamped main path is harmless for NaN (it gives a finite
-        // value that the select then replaces).  Other values take exactly
-        // exp_f32's main path.
+        if (k >= n) break;
         float e[4];
         bool nan = false;
 #pragma unroll
@@ -871,8 +920,15 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
                     0, __builtin_bit_cast(int, t), 0xB1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
         t = t + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
                     0, __builtin_bit_cast(int, t), 0x4E, 0xf, 0xf, false));   // quad_perm 2,3,0,1
-        if (j == 0 && c[k] < nch) lds[c[k]] = t;
+        const int c = chunk(i0, k);
+        if (j == 0 && c < nch) lds[c] = t;
       }
+    };
+    for (int i0 = 0;;) {
+      consume(ua, i0);
+      i0 += KB;
+      if (i0 >= cnt) break;
+      issue(ua, i0);
     }
   } else {
     for (int ch = nch - 1 - (int)threadIdx.x; ch >= 0; ch -= kLsmThreads) {
@@ -885,7 +941,7 @@ k_logsoftmax_row(const float *logits, int64_t ld, const int32_t *targets, int V,
   }
   __syncthreads();
   lds_pair_inplace<kLsmThreads>(lds, gc, T);
-  if (threadIdx.x == 0) lsm_finish(lds, gc, T, tp, row, shard, out, xr, m, targets, V);
+  if (threadIdx.x == 0) lsm_finish(lds, gc, T, tp, row, shard, out, xt, m, tgt, V);
 }
 
 int launch_logsoftmax(const float *logits, int64_t ld, const int32_t *targets, float *out, int M,
