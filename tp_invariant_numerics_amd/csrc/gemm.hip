@@ -20,6 +20,8 @@
 // `parts` aligned nodes written to a workspace (simulated tensor
 // parallelism, TBIK "technical framework"); k_tree_combine finishes the tree.
 // No atomics; no data-dependent reduction order.
+#include <type_traits>
+
 #include "tbik_device.h"
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
@@ -748,6 +750,68 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   }
   float *Cp = p.C ? p.C + (int64_t)part * p.part_stride : nullptr;
   uint16_t *Cbp = p.Cb;
+  bool staged = false;
+  // fp32 output of a workgroup's only part: the tile goes through LDS (the
+  // ring is free: every copy has landed, vmcnt 0 above) and out as whole
+  // rows, 16 bytes per lane, so every store instruction writes full lines
+  // (the MFMA layout alone gives 64-byte row pieces).  The stores are
+  // non-temporal, except for logits whose row maxima are produced here: the
+  // log-softmax reads those next.  (Full-line non-temporal stores: prefill
+  // and 8192^2 GEMMs 12-14% faster; the LM head with its row maxima 1%
+  // faster with plain full-line stores; bitwise the same.)
+  constexpr int LDO = NT + 4;                         // padded row (conflict-free writes)
+  constexpr int LPR = NT / 4;                         // lanes per tile row
+  constexpr int RPI = 64 / LPR;                       // rows per store instruction
+  constexpr int RPW = MT / WAVES;                     // rows per wave
+  if constexpr (PPW == 1 && MT >= 64 && RPW % RPI == 0 &&
+                MT * LDO * 4 <= S * RG::SLOT * 16) {
+    if (Cp && !Cbp && (p.ldc & 3) == 0 && ((uintptr_t)Cp & 15) == 0) {
+      staged = true;
+      float *st = reinterpret_cast<float *>(ring);
+      ring_barrier();                                 // every wave is past its last fragment read
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < WN; ++bn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            st[(wm * 16 * WM + 16 * bm + orow + i) * LDO + wn * 16 * WN + 16 * bn + (lane & 15)] =
+                node[(bm * WN + bn) * 4 + i];
+      ring_barrier();
+      const int cl = 4 * (lane % LPR);
+      const int col = n0 + cl;
+      auto store_rows = [&](auto nt) {
+#pragma unroll
+        for (int r0 = 0; r0 < RPW; r0 += RPI) {
+          const int rl = wave * RPW + r0 + lane / LPR;
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(st + rl * LDO + cl);
+          const int row = m0 + rl;
+          if (row < p.M) {
+            float *dst = Cp + (int64_t)row * p.ldc + col;
+            if (col + 3 < p.N) {
+              if constexpr (decltype(nt)::value)
+                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
+              else
+                *reinterpret_cast<f32x4 *>(dst) = v;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < p.N) dst[e] = v[e];
+            }
+          }
+        }
+      };
+      if (p.pmax == nullptr) {
+        store_rows(std::true_type{});
+      } else {
+        store_rows(std::false_type{});
+        // keeps the two store sequences apart: merged, the compiler would
+        // drop the non-temporal hint from both
+        asm volatile("" ::: "memory");
+      }
+    }
+  }
+  if (!staged) {
 #pragma unroll
   for (int bm = 0; bm < WM; ++bm) {
 #pragma unroll
@@ -764,6 +828,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
         }
       }
     }
+  }
   }
   }
   if constexpr (WN == 4) {
