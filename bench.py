@@ -41,17 +41,17 @@ M_HEAD, K_HEAD, V_HEAD, TP_HEAD = 512, 4096, 151936, 4
 HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs of
 # `bench.py --profile lmhead` (profiles/k_gemm_ring_lmhead_M512_K4096_N151936.md):
-# FETCH_SIZE 1016115 KiB x 2.000 + WRITE_SIZE 339509 KiB x 1.000, the factors
+# FETCH_SIZE 1016386 KiB x 2.000 + WRITE_SIZE 339457 KiB x 1.000, the factors
 # being what a plain 1 GiB device copy reads on the same counters
 # (`bench.py --profile calib`: 524301 KiB fetched, 1048576 KiB written).  Valid
 # only for the GEMM sources the counters were taken on (hash below).
-HEAD_TRAFFIC_BYTES = (1016115 * 2 + 339509) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "e91cf5d7a7b2caacf583c80f3f0a06e39948bf6b90a80acf1553286d0a359241"
+HEAD_TRAFFIC_BYTES = (1016386 * 2 + 339457) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "25a77ea8e4c3adbee6bfe24163a03614b4600c934841154e0d1d7d07bae3e08d"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
-# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64830 KiB x 2.000
-# + WRITE_SIZE 32768 KiB x 1.000.
-HEAD_TP8_TRAFFIC_BYTES = (64830 * 2 + 32768) * 1024
-HEAD_TP8_TRAFFIC_SRC_SHA256 = "e91cf5d7a7b2caacf583c80f3f0a06e39948bf6b90a80acf1553286d0a359241"
+# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64843 KiB x 2.000
+# + WRITE_SIZE 32771 KiB x 1.000.
+HEAD_TP8_TRAFFIC_BYTES = (64843 * 2 + 32771) * 1024
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "25a77ea8e4c3adbee6bfe24163a03614b4600c934841154e0d1d7d07bae3e08d"
 
 
 def gemm_source_sha256(root):
