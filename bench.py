@@ -41,17 +41,17 @@ M_HEAD, K_HEAD, V_HEAD, TP_HEAD = 512, 4096, 151936, 4
 HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs of
 # `bench.py --profile lmhead` (profiles/k_gemm_ring_lmhead_M512_K4096_N151936.md):
-# FETCH_SIZE 1016386 KiB x 2.000 + WRITE_SIZE 339457 KiB x 1.000, the factors
+# FETCH_SIZE 1022236 KiB x 2.000 + WRITE_SIZE 339632 KiB x 1.000, the factors
 # being what a plain 1 GiB device copy reads on the same counters
 # (`bench.py --profile calib`: 524301 KiB fetched, 1048576 KiB written).  Valid
 # only for the GEMM sources the counters were taken on (hash below).
-HEAD_TRAFFIC_BYTES = (1016386 * 2 + 339457) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "25a77ea8e4c3adbee6bfe24163a03614b4600c934841154e0d1d7d07bae3e08d"
+HEAD_TRAFFIC_BYTES = (1022236 * 2 + 339632) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "f964f0c3224de667373da7e7bad6c6ad05d3c64065a630036470d9e1499d648d"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
-# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64843 KiB x 2.000
-# + WRITE_SIZE 32771 KiB x 1.000.
-HEAD_TP8_TRAFFIC_BYTES = (64843 * 2 + 32771) * 1024
-HEAD_TP8_TRAFFIC_SRC_SHA256 = "25a77ea8e4c3adbee6bfe24163a03614b4600c934841154e0d1d7d07bae3e08d"
+# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64839 KiB x 2.000
+# + WRITE_SIZE 32768 KiB x 1.000.
+HEAD_TP8_TRAFFIC_BYTES = (64839 * 2 + 32768) * 1024
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "f964f0c3224de667373da7e7bad6c6ad05d3c64065a630036470d9e1499d648d"
 
 
 def gemm_source_sha256(root):
@@ -566,10 +566,21 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
     if want("prefill"):
         M, K, N = 4096, 14336, 4096
         A = inputs.normal_bf16((M, K), 3200, device=dev)
-        W = inputs.normal_bf16((N, K), 3201, std=0.02, device=dev)
+        # W (117 MB) rotates over 4 copies, so A and W together exceed twice
+        # the 256 MB last-level cache and are read from HBM, not kept there
+        Wr = [inputs.normal_bf16((N, K), 3201 + i, std=0.02, device=dev) for i in range(4)]
         C = torch.empty((M, N), dtype=torch.float32, device=dev)
-        t1 = timed(lambda: tb.tbik_gemm(A, W, out=C), 10)
-        t2 = timed(lambda: torch.matmul(A, W.t()), 10)
+        kr = {"i": 0}
+
+        def tb_rot():
+            kr["i"] += 1
+            tb.tbik_gemm(A, Wr[kr["i"] % 4], out=C)
+
+        def blas_rot():
+            kr["i"] += 1
+            return torch.matmul(A, Wr[kr["i"] % 4].t())
+        t1 = timed(tb_rot, 10)
+        t2 = timed(blas_rot, 10)
         fl = 2.0 * M * N * K
         res["prefill_M4096_K14336_N4096"] = {
             "ms": round(t1, 4), "tflops": round(fl / t1 / 1e9, 1),
@@ -577,7 +588,7 @@ def run_extra(tb, inputs, torch, np, dev, timed, log, args):
             "hipblaslt_tflops": round(fl / t2 / 1e9, 1),
             "overhead_pct": round((t1 / t2 - 1) * 100, 1)}
         log("prefill: %.3f ms = %.1f TFLOP/s (hipBLASLt %.3f ms)" % (t1, fl / t1 / 1e9, t2))
-        del A, W, C
+        del A, Wr, C
 
     if want("logsoftmax"):
         # the standalone log-softmax (its own exact row maxima: two reads of

@@ -755,10 +755,12 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   // ring is free: every copy has landed, vmcnt 0 above) and out as whole
   // rows, 16 bytes per lane, so every store instruction writes full lines
   // (the MFMA layout alone gives 64-byte row pieces).  The stores are
-  // non-temporal, except for logits whose row maxima are produced here: the
-  // log-softmax reads those next.  (Full-line non-temporal stores: prefill
-  // and 8192^2 GEMMs 12-14% faster; the LM head with its row maxima 1%
-  // faster with plain full-line stores; bitwise the same.)
+  // non-temporal, except for logits whose row maxima are produced here.
+  // (Measured with operands beyond the last-level cache, bitwise the same:
+  // non-temporal full lines made an 8192^2 x 1024 GEMM 30% faster and the
+  // other shapes 2-10%; on the 512-row LM head with its row maxima they
+  // raised the HBM reads by 8% and gained nothing, so logits keep plain
+  // stores.)
   constexpr int LDO = NT + 4;                         // padded row (conflict-free writes)
   constexpr int LPR = NT / 4;                         // lanes per tile row
   constexpr int RPI = 64 / LPR;                       // rows per store instruction
