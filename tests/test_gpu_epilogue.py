@@ -1,0 +1,58 @@
+"""The GEMM's output stores through the C ABI: the full-line path (16-byte
+aligned rows: the tile staged in LDS and written as whole rows) and the direct
+path (any other output) write exactly the M x N outputs of a strided, offset
+output view, bit for bit what a contiguous output receives, and nothing
+outside it (the rest of the buffer holds NaN sentinels)."""
+import pytest
+import torch
+
+import tp_invariant_numerics_amd as tb
+from tp_invariant_numerics_amd import inputs
+
+DEV = "cuda"
+pytestmark = pytest.mark.gpu
+
+# (M, N, K, element offset of C in its buffer, extra row pitch)
+CASES = [(512, 4112, 4096, 0, 8),      # aligned rows: full-line path
+         (300, 4111, 1024, 0, 9),      # aligned pitch, ragged N
+         (257, 130, 2048, 1, 4),       # misaligned base: direct path
+         (4096, 1000, 1024, 0, 0),     # contiguous, many row tiles
+         (129, 4096, 14336, 3, 12),    # split K and the combine kernel, misaligned
+         (64, 256, 64, 0, 4)]          # one leaf
+
+
+def _strided(M, N, off, pad):
+    ldc = N + pad
+    buf = torch.full(((M + 2) * ldc + off + 64,), float("nan"), device=DEV)
+    C = buf[off: off + M * ldc].view(M, ldc)[:, :N]
+    mask = torch.ones(buf.shape, dtype=torch.bool, device=DEV)
+    mask[off: off + M * ldc].view(M, ldc)[:, :N] = False
+    return buf, C, mask
+
+
+@pytest.mark.parametrize("M,N,K,off,pad", CASES)
+def test_gemm_strided_output(M, N, K, off, pad):
+    print("case", M, N, K, off, pad, flush=True)
+    A = inputs.normal_bf16((M, K), 900 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 901 + N, std=0.02, device=DEV)
+    ref = tb.tbik_gemm(A, W)[0]
+    buf, C, mask = _strided(M, N, off, pad)
+    tb.tbik_gemm(A, W, out=C)
+    torch.cuda.synchronize()
+    assert torch.equal(C.contiguous().view(torch.int32), ref.view(torch.int32))
+    assert bool(torch.isnan(buf[mask]).all()), "a store landed outside the output view"
+
+
+@pytest.mark.parametrize("M,N,K,off,pad", [(512, 4112, 4096, 0, 8), (200, 1000, 2048, 0, 12),
+                                           (77, 2050, 1024, 2, 4)])
+def test_logits_strided_output(M, N, K, off, pad):
+    print("case", M, N, K, off, pad, flush=True)
+    A = inputs.normal_bf16((M, K), 700 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 701 + N, std=0.02, device=DEV)
+    ref, pref = tb.tbik_gemm_logits(A, W)
+    buf, C, mask = _strided(M, N, off, pad)
+    _, pm = tb.tbik_gemm_logits(A, W, out=C)
+    torch.cuda.synchronize()
+    assert torch.equal(C.contiguous().view(torch.int32), ref.view(torch.int32))
+    assert torch.equal(pm.view(torch.int32), pref.view(torch.int32))
+    assert bool(torch.isnan(buf[mask]).all()), "a store landed outside the output view"
