@@ -38,18 +38,19 @@ __device__ __forceinline__ float chunk_tree(float (&v)[CH]) {
 
 // PAIR levels over `groups` independent groups of m values each, stored
 // compactly (group g at src[g*m .. g*m+m)).  Leaves each group's PAIR value
-// at src'[g] (returned pointer).  Must be called by all threads of the block.
+// at src'[g] (returned pointer).  groups is a power of two dividing NT: each
+// group gets NT/groups threads (no division in the index arithmetic).  Must
+// be called by all threads of the block.
 template <int NT>
 __device__ __forceinline__ float *lds_pair(float *src, float *dst, int m, int groups) {
+  const int sh = __builtin_ctz((unsigned)(NT / groups));
+  const int g = threadIdx.x >> sh, r = threadIdx.x & ((1 << sh) - 1);
   while (m > 1) {
     const int half = m >> 1;
     const int nm = half + (m & 1);
-    for (int idx = threadIdx.x; idx < groups * nm; idx += NT) {
-      const int g = idx / nm;
-      const int i = idx - g * nm;
-      const float *sg = src + g * m;
-      dst[idx] = (i < half) ? sg[2 * i] + sg[2 * i + 1] : sg[m - 1];
-    }
+    const float *sg = src + g * m;
+    for (int i = r; i < nm; i += 1 << sh)
+      dst[g * nm + i] = (i < half) ? sg[2 * i] + sg[2 * i + 1] : sg[m - 1];
     __syncthreads();
     float *t = src; src = dst; dst = t;
     m = nm;
