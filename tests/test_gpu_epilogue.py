@@ -56,3 +56,24 @@ def test_logits_strided_output(M, N, K, off, pad):
     assert torch.equal(C.contiguous().view(torch.int32), ref.view(torch.int32))
     assert torch.equal(pm.view(torch.int32), pref.view(torch.int32))
     assert bool(torch.isnan(buf[mask]).all()), "a store landed outside the output view"
+
+
+@pytest.mark.parametrize("M,N,K,off,pad", [(512, 4112, 4096, 0, 8), (300, 4111, 1024, 0, 9),
+                                           (257, 130, 2048, 1, 6), (4096, 2048, 2048, 0, 0),
+                                           (129, 4096, 14336, 3, 16)])
+def test_gemm_bf16_strided_output(M, N, K, off, pad):
+    """bf16-only output (full-line path when rows are 16-byte aligned): the
+    round-to-nearest-even of the fp32 result, in a strided, offset view."""
+    print("case", M, N, K, off, pad, flush=True)
+    A = inputs.normal_bf16((M, K), 500 + M, device=DEV)
+    W = inputs.normal_bf16((N, K), 501 + N, std=0.02, device=DEV)
+    ref = tb.tbik_gemm(A, W)[0].to(torch.bfloat16)
+    ldc = N + pad
+    buf = torch.full(((M + 2) * ldc + off + 64,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    Cb = buf[off: off + M * ldc].view(M, ldc)[:, :N]
+    mask = torch.ones(buf.shape, dtype=torch.bool, device=DEV)
+    mask[off: off + M * ldc].view(M, ldc)[:, :N] = False
+    tb.tbik_gemm(A, W, out_bf16=Cb, want_fp32=False)
+    torch.cuda.synchronize()
+    assert torch.equal(Cb.contiguous().view(torch.int16), ref.view(torch.int16))
+    assert bool(torch.isnan(buf[mask]).all()), "a store landed outside the output view"

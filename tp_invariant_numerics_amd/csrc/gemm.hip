@@ -751,10 +751,11 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   float *Cp = p.C ? p.C + (int64_t)part * p.part_stride : nullptr;
   uint16_t *Cbp = p.Cb;
   bool staged = false;
-  // fp32 output of a workgroup's only part: the tile goes through LDS (the
-  // ring is free: every copy has landed, vmcnt 0 above) and out as whole
-  // rows, 16 bytes per lane, so every store instruction writes full lines
-  // (the MFMA layout alone gives 64-byte row pieces).  The stores are
+  // fp32 or bf16 output of a workgroup's only part: the tile goes through
+  // LDS (the ring is free: every copy has landed, vmcnt 0 above) and out as
+  // whole rows, 16 bytes per lane, so every store instruction writes full
+  // lines (the MFMA layout alone gives 64-byte fp32 or 32-byte bf16 row
+  // pieces).  The stores are
   // non-temporal, except for logits whose row maxima are produced here.
   // (Measured with operands beyond the last-level cache, bitwise the same:
   // non-temporal full lines made an 8192^2 x 1024 GEMM 30% faster and the
@@ -810,6 +811,44 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
         // keeps the two store sequences apart: merged, the compiler would
         // drop the non-temporal hint from both
         asm volatile("" ::: "memory");
+      }
+    } else if (!Cp && Cbp && (p.ldc & 7) == 0 && ((uintptr_t)Cbp & 15) == 0) {
+      // bf16-only output (the decoder's projections): the same, rounded to
+      // bf16 on the way into LDS, 8 values (16 bytes) per lane, non-temporal
+      constexpr int LDB = NT + 8;                     // padded row, in bf16 elements
+      constexpr int LPB = NT / 8;                     // lanes per tile row
+      constexpr int RPB = 64 / LPB;                   // rows per store instruction
+      static_assert(RPW % RPB == 0 && MT * LDB * 2 <= S * RG::SLOT * 16, "bf16 staging");
+      staged = true;
+      uint16_t *sb = reinterpret_cast<uint16_t *>(ring);
+      ring_barrier();                                 // every wave is past its last fragment read
+#pragma unroll
+      for (int bm = 0; bm < WM; ++bm)
+#pragma unroll
+        for (int bn = 0; bn < WN; ++bn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            sb[(wm * 16 * WM + 16 * bm + orow + i) * LDB + wn * 16 * WN + 16 * bn + (lane & 15)] =
+                f2bf(node[(bm * WN + bn) * 4 + i]);
+      ring_barrier();
+      const int cl = 8 * (lane % LPB);
+      const int col = n0 + cl;
+#pragma unroll
+      for (int r0 = 0; r0 < RPW; r0 += RPB) {
+        const int rl = wave * RPW + r0 + lane / LPB;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(sb + rl * LDB + cl);
+        const int row = m0 + rl;
+        if (row < p.M) {
+          uint16_t *dst = Cbp + (int64_t)row * p.ldc + col;
+          if (col + 7 < p.N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(dst));
+          } else {
+            const uint16_t *e16 = sb + rl * LDB + cl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (col + e < p.N) dst[e] = e16[e];
+          }
+        }
       }
     }
   }
