@@ -1,8 +1,9 @@
-"""The GEMM's output stores through the C ABI: the full-line path (16-byte
-aligned rows: the tile staged in LDS and written as whole rows) and the direct
-path (any other output) write exactly the M x N outputs of a strided, offset
-output view, bit for bit what a contiguous output receives, and nothing
-outside it (the rest of the buffer holds NaN sentinels)."""
+"""The GEMM's output stores through the C ABI (fp32, bf16 and the SwiGLU
+epilogue's H): the full-line path (16-byte aligned rows: the tile staged in
+LDS and written as whole rows) and the direct path (any other output) write
+exactly the outputs of a strided, offset output view, bit for bit what a
+contiguous output receives, and nothing outside it (the rest of the buffer
+holds NaN sentinels)."""
 import pytest
 import torch
 
@@ -76,4 +77,27 @@ def test_gemm_bf16_strided_output(M, N, K, off, pad):
     tb.tbik_gemm(A, W, out_bf16=Cb, want_fp32=False)
     torch.cuda.synchronize()
     assert torch.equal(Cb.contiguous().view(torch.int16), ref.view(torch.int16))
+    assert bool(torch.isnan(buf[mask]).all()), "a store landed outside the output view"
+
+
+@pytest.mark.parametrize("M,F,K,off,pad", [(512, 2816, 2048, 0, 8), (300, 1040, 1024, 0, 16),
+                                           (257, 208, 2048, 3, 5), (4096, 1024, 1024, 0, 0)])
+def test_gemm_swiglu_strided_output(M, F, K, off, pad):
+    """The gate/up GEMM with the SwiGLU node in its epilogue, H written into a
+    strided, offset view (full-line path when its rows are 16-byte aligned):
+    bit for bit the composition GEMM -> bf16 gate and up -> SwiGLU."""
+    print("case", M, F, K, off, pad, flush=True)
+    A = inputs.normal_bf16((M, K), 300 + M, device=DEV)
+    Wgu = inputs.normal_bf16((2 * F, K), 301 + F, std=0.02, device=DEV)
+    g = tb.tbik_gemm(A, Wgu[:F], want_fp32=False, want_bf16=True)[1]
+    u = tb.tbik_gemm(A, Wgu[F:], want_fp32=False, want_bf16=True)[1]
+    ref = tb.tbik_swiglu(g, u)
+    ldh = F + pad
+    buf = torch.full(((M + 2) * ldh + off + 64,), float("nan"), dtype=torch.bfloat16, device=DEV)
+    H = buf[off: off + M * ldh].view(M, ldh)[:, :F]
+    mask = torch.ones(buf.shape, dtype=torch.bool, device=DEV)
+    mask[off: off + M * ldh].view(M, ldh)[:, :F] = False
+    tb.tbik_gemm_swiglu(A, Wgu, out=H)
+    torch.cuda.synchronize()
+    assert torch.equal(H.contiguous().view(torch.int16), ref.view(torch.int16))
     assert bool(torch.isnan(buf[mask]).all()), "a store landed outside the output view"
