@@ -1,9 +1,9 @@
 """The GEMM's output stores through the C ABI (fp32, bf16 and the SwiGLU
-epilogue's H): the full-line path (16-byte aligned rows: the tile staged in
-LDS and written as whole rows) and the direct path (any other output) write
-exactly the outputs of a strided, offset output view, bit for bit what a
-contiguous output receives, and nothing outside it (the rest of the buffer
-holds NaN sentinels)."""
+epilogue's H): the full-line path (fp32 or bf16 outputs with 16-byte aligned
+rows: the tile staged in LDS and written as whole rows) and the direct path
+(any other output) write exactly the outputs of a strided, offset output
+view, bit for bit what a contiguous output receives, and nothing outside it
+(the rest of the buffer holds NaN sentinels)."""
 import pytest
 import torch
 
@@ -84,8 +84,8 @@ def test_gemm_bf16_strided_output(M, N, K, off, pad):
                                            (257, 208, 2048, 3, 5), (4096, 1024, 1024, 0, 0)])
 def test_gemm_swiglu_strided_output(M, F, K, off, pad):
     """The gate/up GEMM with the SwiGLU node in its epilogue, H written into a
-    strided, offset view (full-line path when its rows are 16-byte aligned):
-    bit for bit the composition GEMM -> bf16 gate and up -> SwiGLU."""
+    strided, offset view: bit for bit the composition GEMM -> bf16 gate and
+    up -> SwiGLU."""
     print("case", M, F, K, off, pad, flush=True)
     A = inputs.normal_bf16((M, K), 300 + M, device=DEV)
     Wgu = inputs.normal_bf16((2 * F, K), 301 + F, std=0.02, device=DEV)

@@ -728,67 +728,20 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
     // a wave's 16 * WN columns start at a multiple of 32: block pairs
     // (2q, 2q+1) are the gate and up columns of the same 16 units, held by
     // the same lane; the arithmetic is the SwiGLU node's on the GEMM's bf16
-    // outputs.  The tile's NT/2 units of each row are contiguous in H: with
-    // 16-byte aligned rows they go through LDS and out as whole rows, 8
-    // units per lane, non-temporal (as the plain outputs below).
-    auto hval = [&](int bm, int q, int i) {
-      float a = silu(bf_round(node[(bm * WN + 2 * q) * 4 + i]));
-      if (p.glu == 2) a = bf_round(a);
-      return f2bf(a * bf_round(node[(bm * WN + 2 * q + 1) * 4 + i]));
-    };
-    constexpr int NU = NT / 2;                        // units per tile row
-    constexpr int LDH = NU + 8;                       // padded row, in bf16 elements
-    constexpr int LPH = NU / 8;                       // lanes per tile row
-    constexpr int RPH = 64 / LPH;                     // rows per store instruction
-    constexpr int RPWH = MT / WAVES;                  // rows per wave
-    bool hstaged = false;
-    if constexpr (MT >= 64 && RPWH % RPH == 0 && MT * LDH * 2 <= S * RG::SLOT * 16) {
-      if ((p.ldh & 7) == 0 && ((uintptr_t)p.H & 15) == 0) {
-        hstaged = true;
-        uint16_t *sb = reinterpret_cast<uint16_t *>(ring);
-        ring_barrier();                               // every wave is past its last fragment read
+    // outputs
 #pragma unroll
-        for (int bm = 0; bm < WM; ++bm)
+    for (int bm = 0; bm < WM; ++bm) {
 #pragma unroll
-          for (int q = 0; q < WN / 2; ++q)
+      for (int q = 0; q < WN / 2; ++q) {
+        const int colg = n0 + wn * 16 * WN + 32 * q + (lane & 15);
+        const int unit = (colg >> 5) * 16 + (colg & 15);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-              sb[(wm * 16 * WM + 16 * bm + orow + i) * LDH + (wn * 16 * WN) / 2 + 16 * q +
-                 (lane & 15)] = hval(bm, q, i);
-        ring_barrier();
-        const int nu = p.N / 2;                       // units of H
-        const int cl = 8 * (lane % LPH);
-        const int u0 = n0 / 2 + cl;
-#pragma unroll
-        for (int r0 = 0; r0 < RPWH; r0 += RPH) {
-          const int rl = wave * RPWH + r0 + lane / LPH;
-          const int row = m0 + rl;
-          if (row < p.M) {
-            uint16_t *dst = p.H + (int64_t)row * p.ldh + u0;
-            const uint16_t *src = sb + rl * LDH + cl;
-            if (u0 + 7 < nu) {
-              __builtin_nontemporal_store(*reinterpret_cast<const u32x4 *>(src),
-                                          reinterpret_cast<u32x4 *>(dst));
-            } else {
-#pragma unroll
-              for (int e = 0; e < 8; ++e)
-                if (u0 + e < nu) dst[e] = src[e];
-            }
-          }
-        }
-      }
-    }
-    if (!hstaged) {
-#pragma unroll
-      for (int bm = 0; bm < WM; ++bm) {
-#pragma unroll
-        for (int q = 0; q < WN / 2; ++q) {
-          const int colg = n0 + wn * 16 * WN + 32 * q + (lane & 15);
-          const int unit = (colg >> 5) * 16 + (colg & 15);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = m0 + wm * 16 * WM + 16 * bm + orow + i;
-            if (row < p.M && colg < p.N) p.H[(int64_t)row * p.ldh + unit] = hval(bm, q, i);
+        for (int i = 0; i < 4; ++i) {
+          const int row = m0 + wm * 16 * WM + 16 * bm + orow + i;
+          if (row < p.M && colg < p.N) {
+            float a = silu(bf_round(node[(bm * WN + 2 * q) * 4 + i]));
+            if (p.glu == 2) a = bf_round(a);
+            p.H[(int64_t)row * p.ldh + unit] = f2bf(a * bf_round(node[(bm * WN + 2 * q + 1) * 4 + i]));
           }
         }
       }
