@@ -20,8 +20,6 @@
 // `parts` aligned nodes written to a workspace (simulated tensor
 // parallelism, TBIK "technical framework"); k_tree_combine finishes the tree.
 // No atomics; no data-dependent reduction order.
-#include <type_traits>
-
 #include "tbik_device.h"
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
@@ -681,6 +679,7 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
 
   float node[R];
   const int orow = 4 * (lane >> 4);
+  bool staged = false;                  // the last part's output went out through LDS
 #pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
   const int part = part0 + pi;
@@ -750,18 +749,14 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   }
   float *Cp = p.C ? p.C + (int64_t)part * p.part_stride : nullptr;
   uint16_t *Cbp = p.Cb;
-  bool staged = false;
+  staged = false;
   // fp32 or bf16 output of a workgroup's only part: the tile goes through
   // LDS (the ring is free: every copy has landed, vmcnt 0 above) and out as
-  // whole rows, 16 bytes per lane, so every store instruction writes full
-  // lines (the MFMA layout alone gives 64-byte fp32 or 32-byte bf16 row
-  // pieces).  The stores are
-  // non-temporal, except for logits whose row maxima are produced here.
-  // (Measured with operands beyond the last-level cache, bitwise the same:
-  // non-temporal full lines made an 8192^2 x 1024 GEMM 30% faster and the
-  // other shapes 2-10%; on the 512-row LM head with its row maxima they
-  // raised the HBM reads by 8% and gained nothing, so logits keep plain
-  // stores.)
+  // whole rows, 16 bytes per lane, non-temporal, so every store instruction
+  // writes full lines (the MFMA layout alone gives 64-byte fp32 or 32-byte
+  // bf16 row pieces).  With 128-column tiles the 64-column row maxima are
+  // formed from the same LDS rows as they are stored (16 lanes hold one
+  // row's 64 columns), with no separate phase.
   constexpr int LDO = NT + 4;                         // padded row (conflict-free writes)
   constexpr int LPR = NT / 4;                         // lanes per tile row
   constexpr int RPI = 64 / LPR;                       // rows per store instruction
@@ -783,34 +778,49 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
       ring_barrier();
       const int cl = 4 * (lane % LPR);
       const int col = n0 + cl;
-      auto store_rows = [&](auto nt) {
 #pragma unroll
-        for (int r0 = 0; r0 < RPW; r0 += RPI) {
-          const int rl = wave * RPW + r0 + lane / LPR;
-          const f32x4 v = *reinterpret_cast<const f32x4 *>(st + rl * LDO + cl);
-          const int row = m0 + rl;
-          if (row < p.M) {
-            float *dst = Cp + (int64_t)row * p.ldc + col;
-            if (col + 3 < p.N) {
-              if constexpr (decltype(nt)::value)
-                __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
-              else
-                *reinterpret_cast<f32x4 *>(dst) = v;
-            } else {
+      for (int r0 = 0; r0 < RPW; r0 += RPI) {
+        const int rl = wave * RPW + r0 + lane / LPR;
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(st + rl * LDO + cl);
+        const int row = m0 + rl;
+        if (row < p.M) {
+          float *dst = Cp + (int64_t)row * p.ldc + col;
+          if (col + 3 < p.N) {
+            __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(dst));
+          } else {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (col + e < p.N) dst[e] = v[e];
-            }
+            for (int e = 0; e < 4; ++e)
+              if (col + e < p.N) dst[e] = v[e];
           }
         }
-      };
-      if (p.pmax == nullptr) {
-        store_rows(std::true_type{});
-      } else {
-        store_rows(std::false_type{});
-        // keeps the two store sequences apart: merged, the compiler would
-        // drop the non-temporal hint from both
-        asm volatile("" ::: "memory");
+        if constexpr (NT == 128) {
+          if (p.pmax) {
+            // lanes 16k .. 16k+15 hold one row's 64-column block; every lane
+            // takes part in the DPP steps (a lane past M or N contributes
+            // -inf), the block's last lane stores the maximum
+            float mx = -__builtin_inff();
+            if (row < p.M) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (col + e < p.N) mx = __builtin_fmaxf(mx, v[e]);
+            }
+            mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                         0x111, 0xf, 0xf, false)));
+            mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                         0x112, 0xf, 0xf, false)));
+            mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                         0x114, 0xf, 0xf, false)));
+            mx = __builtin_fmaxf(mx, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+                                         __builtin_bit_cast(int, mx), __builtin_bit_cast(int, mx),
+                                         0x118, 0xf, 0xf, false)));
+            const int cb = n0 + 64 * ((lane >> 4) & 1);
+            if ((lane & 15) == 15 && row < p.M && cb < p.N)
+              p.pmax[(int64_t)row * p.ld_pmax + cb / 64] = mx;
+          }
+        }
       }
     } else if (!Cp && Cbp && (p.ldc & 7) == 0 && ((uintptr_t)Cbp & 15) == 0) {
       // bf16-only output (the decoder's projections): the same, rounded to
@@ -909,10 +919,11 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
       }
     }
   } else if constexpr (WN == 2 && WAVES_N == 4) {
-    // 32-column waves: each wave's row maxima over its 32 columns go to LDS
-    // (the ring is free once every wave is past its last leaf), then the
-    // two halves of each 64-column block are combined.
-    if (p.pmax) {
+    // 32-column waves, output not staged (the staged path forms the row
+    // maxima as it stores): each wave's row maxima over its 32 columns go to
+    // LDS (the ring is free once every wave is past its last leaf), then
+    // the two halves of each 64-column block are combined.
+    if (p.pmax && !staged) {
       float *pm = reinterpret_cast<float *>(ring);    // [MT rows][WAVES_N]
       // LDS-only barriers: every wave has drained its loads into the ring
       // (vmcnt 0 above); a full __syncthreads would also wait for the C
