@@ -22,7 +22,7 @@ and tp = 1, prefill, row kernels, decoder, training side), and the CPU
 oracle timed on bounded samples of every workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extra] [--no-cpu]
-       python bench.py --profile lmhead|rows|downproj|calib   (a few launches, for rocprofv3)
+       python bench.py --profile lmhead|rows|downproj|decode|calib   (a few launches, for rocprofv3)
 """
 import argparse
 import hashlib
@@ -80,10 +80,11 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="headline step only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baselines")
     ap.add_argument("--profile", default="",
-                    choices=["", "lmhead", "rows", "downproj", "calib", "ringcopy"],
+                    choices=["", "lmhead", "rows", "downproj", "decode", "calib", "ringcopy"],
                     help="run only a few launches of one group of kernels, for rocprofv3: "
                          "lmhead (the headline's GEMM and log-softmax), rows (RMSNorm, RoPE, "
                          "SwiGLU, standalone log-softmax), downproj (tp = 8 partials + combine), "
+                         "decode (tp = 1 down projection at M = 1 and M = 32), "
                          "calib (a plain 1 GiB device copy, the counters' byte scale)")
     ap.add_argument("--only", default="", help="run only one extra workload (profiling)")
     return ap.parse_args()
@@ -362,6 +363,19 @@ def profile_kernels(what, tb, inputs, torch, dev, log, head):
         C = torch.empty((M, N), dtype=torch.float32, device=dev)
         for i in range(reps):
             tb.tbik_gemm_tpsim(A, Ws[i % 6], tp, ws=ws, out=C)
+    elif what == "decode":
+        # the tp = 1 down projection at decode batch sizes, W rotating over 5
+        # copies as in the timed workload; M = 1 first, then M = 32
+        K, N = 14336, 4096
+        Ws = [inputs.normal_bf16((N, K), 3001 + i, std=0.02, device=dev) for i in range(5)]
+        for M in (1, 32):
+            A = inputs.normal_bf16((M, K), 3100 + M, device=dev)
+            C = torch.empty((M, N), dtype=torch.float32, device=dev)
+            nb = tb.tbik_gemm_workspace_bytes(M, N, K)
+            ws = torch.empty((nb // 4,), dtype=torch.float32, device=dev)
+            for i in range(reps):
+                tb.tbik_gemm(A, Ws[i % 5], out=C, ws=ws)
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     log("profile %s: %d launches of each kernel" % (what, reps))
 
