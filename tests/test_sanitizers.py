@@ -46,8 +46,9 @@ def test_oracle_driver_under_asan_ubsan():
 
 @pytest.mark.parametrize("mode", ["exp", "log", "prod", "rne"])
 def test_pins_under_asan_ubsan(mode):
-    lib = os.path.join(OUT, "liboracle_tbik_san.so")
-    exe = os.path.join(OUT, "pins_san")
+    # one build per process: parallel test workers must not race on the files
+    lib = os.path.join(OUT, "liboracle_tbik_san_%d.so" % os.getpid())
+    exe = os.path.join(OUT, "pins_san_%d" % os.getpid())
     if not (os.path.exists(lib) and os.path.exists(exe)):
         _gcc(["-fPIC", "-shared", os.path.join(ROOT, "oracle", "tbik_oracle.c"), "-o", lib,
               "-lm"])
