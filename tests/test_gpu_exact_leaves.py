@@ -16,7 +16,8 @@ Shapes reach every launch path of tbik_gemm: the thin 16- and 32-row ring
 tiles (K = 14336, M <= 32, K split into its 8 groups or tp = 4 / 8 shards),
 the small-M kernel (other K, tp = 2), the narrow and wide ring tiles with
 the perfect-tree, 4-, 8-, 11- and 28-leaf group schedules, paired shards
-(tp = 8 at K = 14336 with many tiles), split-K at tree nodes, the
+(tp = 8 at K = 14336 with many tiles), all shards of a tile in one
+workgroup (one group per shard, 256 to 512 tiles), split-K at tree nodes, the
 strided-batched kernel and the LM-head GEMM with fused row maxima.
 """
 import os
@@ -134,3 +135,34 @@ def test_mfma_exact_leaves_golden_tree_probes():
             say("golden tree probe", n, big, "M", M)
             C, _ = tb.tbik_gemm(A.to(DEV), W)
             assert torch.all(C == float(expected)), (n, big, M, C.unique().tolist()[:4])
+
+
+@pytest.mark.parametrize("K", (2048, 4096, 8192))
+def test_mfma_exact_leaves_all_shards_per_workgroup(orc, K):
+    """Shapes with at least 256 wide tiles and one tree group per shard,
+    where a workgroup streams every shard of its tile through one ring and
+    writes each shard's node as it completes: K = 2048 (tp 2, 4, 8 give
+    shards of 16, 8 and 4 leaves), K = 4096 (32, 16, 8) and K = 8192 (tp 4:
+    32).  The shard partials and C are bit-exact against the oracle's
+    simulated tensor parallelism on sampled columns; M = 4096 rows of A are
+    the same 512 rows repeated, so rows 512 apart must agree bit for bit."""
+    M, Nw = 4096, 1040                 # 32 x 9 = 288 tiles of 128 x 128, ragged N
+    A512 = inputs.one_per_block_bf16((512, K), 11400 + K, spread=12)
+    A = A512.repeat(M // 512, 1)
+    W = inputs.normal_bf16((Nw, K), 11401 + K, device=DEV)
+    cols = _cols(Nw, K + 1)
+    ci = torch.from_numpy(cols).to(DEV)
+    rows = np.unique(np.concatenate([np.arange(0, 512, 37), [0, 127, 128, 511]]))
+    ri = torch.from_numpy(rows).to(DEV)
+    Ad = A.to(DEV)
+    for tp in ((2, 4, 8) if K < 8192 else (4,)):
+        say("exact leaves, all shards per workgroup: K", K, "tp", tp)
+        refC, refP = orc.gemm_tpsim(inputs.bits(A512[rows]),
+                                    inputs.bits(W.index_select(0, ci)), tp)
+        C, _, ws = tb.tbik_gemm_tpsim(Ad, W, tp)
+        for blk in range(M // 512):
+            got = _u32(C[blk * 512:(blk + 1) * 512].index_select(0, ri).index_select(1, ci))
+            assert np.array_equal(got, refC.view(np.uint32)), ("C", K, tp, blk)
+        for t in range(tp):
+            got = _u32(ws[t].index_select(0, ri).index_select(1, ci))
+            assert np.array_equal(got, refP[t].view(np.uint32)), ("partial", K, tp, t)

@@ -45,6 +45,12 @@
 #define TBIK_RING_PPW_MIN_WG 256
 #endif
 
+// Wide ring tiles with one group per part: all parts of a tile in one
+// workgroup (1 = on)
+#ifndef TBIK_RING_ALL_PARTS
+#define TBIK_RING_ALL_PARTS 1
+#endif
+
 // 32-row ring tiles for 16 < M <= 32 (1 = on)
 #ifndef TBIK_THIN
 #define TBIK_THIN 1
@@ -680,7 +686,10 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   float node[R];
   const int orow = 4 * (lane >> 4);
   bool staged = false;                  // the last part's output went out through LDS
-#pragma unroll
+  // two parts per iteration (with 4 or 8 parts the epilogue's output
+  // addresses, formed once before the loop, spill; they are reloaded only
+  // in the epilogue)
+#pragma unroll 2
   for (int pi = 0; pi < PPW; ++pi) {
   const int part = part0 + pi;
   float top[TD > 0 ? TD : 1][R];
@@ -882,7 +891,9 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   }
   }
   }
-  if constexpr (WN == 4) {
+  if constexpr (PPW > 1) {
+    // no row maxima with several parts per workgroup (the launcher refuses)
+  } else if constexpr (WN == 4) {
     // Exact row maxima of this wave's 64 columns (max is order-free): the
     // logprob path's log-softmax then reads the logits only once.
     if (p.pmax) {
@@ -1151,9 +1162,41 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
 // the operands into LDS runs at nearly twice the rate: the outstanding
 // L1 -> L2 requests per CU grow with the resident waves, and the average L2
 // latency decides the rate at a given count.
+// One group per part (gpp == 1) and 2, 4 or 8 parts, where the tiles alone
+// give every CU one or two workgroups: a workgroup streams all parts of its
+// tile through one ring, writing each part's node as soon as it is complete,
+// instead of one short workgroup per part (M = 4096, K = N = 2048 at tp = 4,
+// 8 leaves per part: 116 -> 95 us).  With more tiles the per-part
+// workgroups win (M = N = K = 4096 at tp = 4 / 8 and the dp = 8 weight
+// gradient ran 9-15% slower this way): the part nodes then leave through the
+// MFMA layout, not as whole lines through LDS, whose ring is still busy with
+// the next part's stages.
+static bool wide_all_parts(const GemmArgs &a) {
+  const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
+  return TBIK_RING_ALL_PARTS && a.gpp == 1 && a.pmax == nullptr &&
+         (a.parts == 2 || a.parts == 4 || a.parts == 8) && tiles >= TBIK_RING_PPW_MIN_WG &&
+         tiles <= 2 * TBIK_RING_PPW_MIN_WG;
+}
+
+// Reachable (group size, parts): a part is one group of GS leaves, and the
+// parts times the groups per part make the tree's 8 top groups, so GS = 4
+// comes with 8 parts (G = 4) and the merged perfect trees GS = 8, 16, 32
+// with the tp that leaves two or more of the original groups in a part.
+template <int GS, int U>
+static int launch_wide_all_parts(const GemmArgs &a, hipStream_t s) {
+  if constexpr (GS != 4) {
+    if (a.parts == 2) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 2>(a, s);
+    if (a.parts == 4) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 4>(a, s);
+  }
+  if constexpr (GS <= 8)
+    if (a.parts == 8) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 8>(a, s);
+  return TBIK_ERR_ARG;
+}
+
 template <int GS, int U = 1>
 static int launch_wide(const GemmArgs &a, hipStream_t s) {
   if constexpr (GS == 16 || GS == 32) {
+    if (wide_all_parts(a)) return launch_wide_all_parts<GS, U>(a, s);
     if (a.gpp == 1) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1>(a, s);
     return TBIK_ERR_ARG;
   } else if constexpr (GS == 28) {
@@ -1170,6 +1213,8 @@ static int launch_wide(const GemmArgs &a, hipStream_t s) {
     }
     return TBIK_ERR_ARG;
   } else {
+    if constexpr (GS == 4 || GS == 8)
+      if (wide_all_parts(a)) return launch_wide_all_parts<GS, 1>(a, s);
     switch (a.gpp) {
       case 1:
       case 2: return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 1, 0, 1, 1>(a, s);
