@@ -137,13 +137,13 @@ def test_mfma_exact_leaves_golden_tree_probes():
             assert torch.all(C == float(expected)), (n, big, M, C.unique().tolist()[:4])
 
 
-@pytest.mark.parametrize("K", (2048, 4096, 8192))
+@pytest.mark.parametrize("K", (2048, 4096, 5632, 8192))
 def test_mfma_exact_leaves_all_shards_per_workgroup(orc, K):
-    """Shapes with at least 256 wide tiles and one tree group per shard,
-    where a workgroup streams every shard of its tile through one ring and
-    writes each shard's node as it completes: K = 2048 (tp 2, 4, 8 give
-    shards of 16, 8 and 4 leaves), K = 4096 (32, 16, 8) and K = 8192 (tp 4:
-    32).  The shard partials and C are bit-exact against the oracle's
+    """Shapes with 256 to 512 wide tiles and one tree group per shard (or
+    11-leaf groups), where a workgroup streams every shard of its tile
+    through one ring and writes each shard's node as it completes: K = 2048
+    (tp 2, 4, 8 give shards of 16, 8 and 4 leaves), K = 4096 (32, 16, 8),
+    K = 5632 (4, 2 or 1 groups of 11 leaves) and K = 8192 (tp 4: 32).  The shard partials and C are bit-exact against the oracle's
     simulated tensor parallelism on sampled columns; M = 4096 rows of A are
     the same 512 rows repeated, so rows 512 apart must agree bit for bit."""
     M, Nw = 4096, 1040                 # 32 x 9 = 288 tiles of 128 x 128, ragged N

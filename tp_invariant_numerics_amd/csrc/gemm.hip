@@ -1173,7 +1173,7 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
 // the next part's stages.
 static bool wide_all_parts(const GemmArgs &a) {
   const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  return TBIK_RING_ALL_PARTS && a.gpp == 1 && a.pmax == nullptr &&
+  return TBIK_RING_ALL_PARTS && (a.gpp == 1 || a.G == 11) && a.pmax == nullptr &&
          (a.parts == 2 || a.parts == 4 || a.parts == 8) && tiles >= TBIK_RING_PPW_MIN_WG &&
          tiles <= 2 * TBIK_RING_PPW_MIN_WG;
 }
@@ -1184,12 +1184,19 @@ static bool wide_all_parts(const GemmArgs &a) {
 // with the tp that leaves two or more of the original groups in a part.
 template <int GS, int U>
 static int launch_wide_all_parts(const GemmArgs &a, hipStream_t s) {
-  if constexpr (GS != 4) {
-    if (a.parts == 2) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 2>(a, s);
-    if (a.parts == 4) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 4>(a, s);
+  if constexpr (GS == 11) {
+    // 11-leaf groups (K = 5632): 8 / parts groups per part, their own stack
+    if (a.parts == 2) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, 11, 1, 0, 2, 1, 2>(a, s);
+    if (a.parts == 4) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, 11, 1, 0, 1, 1, 4>(a, s);
+    if (a.parts == 8) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, 11, 1, 0, 1, 1, 8>(a, s);
+  } else {
+    if constexpr (GS != 4) {
+      if (a.parts == 2) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 2>(a, s);
+      if (a.parts == 4) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 4>(a, s);
+    }
+    if constexpr (GS <= 8)
+      if (a.parts == 8) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 8>(a, s);
   }
-  if constexpr (GS <= 8)
-    if (a.parts == 8) return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, U, 0, 1, 1, 8>(a, s);
   return TBIK_ERR_ARG;
 }
 
@@ -1213,7 +1220,7 @@ static int launch_wide(const GemmArgs &a, hipStream_t s) {
     }
     return TBIK_ERR_ARG;
   } else {
-    if constexpr (GS == 4 || GS == 8)
+    if constexpr (GS == 4 || GS == 8 || GS == 11)
       if (wide_all_parts(a)) return launch_wide_all_parts<GS, 1>(a, s);
     switch (a.gpp) {
       case 1:
