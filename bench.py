@@ -46,12 +46,12 @@ HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # (`bench.py --profile calib`: 524302 KiB fetched, 1048576 KiB written).  Valid
 # only for the GEMM sources the counters were taken on (hash below).
 HEAD_TRAFFIC_BYTES = (1041450 * 2 + 339981) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "a0f7ee2be9d821b44f5704b65670d92a629179d2b1939e4363f02010201ea8b9"
+HEAD_TRAFFIC_SRC_SHA256 = "c5cd66ff8fb9ae58449a3155469cfb3ee5c76bfc364e786ea423938fbe0e2b8f"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
 # k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64842 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000.
 HEAD_TP8_TRAFFIC_BYTES = (64842 * 2 + 32768) * 1024
-HEAD_TP8_TRAFFIC_SRC_SHA256 = "a0f7ee2be9d821b44f5704b65670d92a629179d2b1939e4363f02010201ea8b9"
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "c5cd66ff8fb9ae58449a3155469cfb3ee5c76bfc364e786ea423938fbe0e2b8f"
 
 
 def gemm_source_sha256(root):

@@ -1155,22 +1155,14 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
                          TBIK_RING_S, TBIK_RING_NX, (TBIK_RING_PIPE != 0 && GS > 0), GS, U, GD, TD>(
       a, s);
 }
-// "Wide" tiles: 128 x 128 with 8 waves of 64 x 32, two waves per SIMD (so
-// <= 256 registers per wave: two leaf accumulators plus the tree state of
-// 32 outputs per lane) and a 4-stage ring of 128 KB.  Against 4 waves of
-// 64 x 64 with the same tile (one wave per SIMD, ~460 registers) the copy of
-// the operands into LDS runs at nearly twice the rate: the outstanding
-// L1 -> L2 requests per CU grow with the resident waves, and the average L2
-// latency decides the rate at a given count.
-// One group per part (gpp == 1) and 2, 4 or 8 parts, where the tiles alone
-// give every CU one or two workgroups: a workgroup streams all parts of its
-// tile through one ring, writing each part's node as soon as it is complete,
-// instead of one short workgroup per part (M = 4096, K = N = 2048 at tp = 4,
-// 8 leaves per part: 116 -> 95 us).  With more tiles the per-part
-// workgroups win (M = N = K = 4096 at tp = 4 / 8 and the dp = 8 weight
-// gradient ran 9-15% slower this way): the part nodes then leave through the
-// MFMA layout, not as whole lines through LDS, whose ring is still busy with
-// the next part's stages.
+
+// One group per part (gpp == 1), or 11-leaf groups, and 2, 4 or 8 parts,
+// where the tiles alone give every CU one or two workgroups: a workgroup
+// streams all parts of its tile through one ring, writing each part's node
+// as soon as it is complete, instead of one short workgroup per part
+// (M = 4096, K = N = 2048 at tp = 4, 8 leaves per part: 116 -> 95 us).  With
+// more tiles the per-part workgroups were faster (M = N = K = 4096 at
+// tp = 4 / 8 and the dp = 8 weight gradient ran 9-15% slower this way).
 static bool wide_all_parts(const GemmArgs &a) {
   const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
   return TBIK_RING_ALL_PARTS && (a.gpp == 1 || a.G == 11) && a.pmax == nullptr &&
@@ -1178,10 +1170,10 @@ static bool wide_all_parts(const GemmArgs &a) {
          tiles <= 2 * TBIK_RING_PPW_MIN_WG;
 }
 
-// Reachable (group size, parts): a part is one group of GS leaves, and the
-// parts times the groups per part make the tree's 8 top groups, so GS = 4
-// comes with 8 parts (G = 4) and the merged perfect trees GS = 8, 16, 32
-// with the tp that leaves two or more of the original groups in a part.
+// Reachable (group size, parts): the parts times the groups per part make
+// the tree's 8 top groups.  GS = 4 comes with 8 parts (one group each), the
+// merged perfect trees GS = 8, 16, 32 with the tp that leaves two or more of
+// the original groups in a part, and GS = 11 with any of 2, 4, 8 parts.
 template <int GS, int U>
 static int launch_wide_all_parts(const GemmArgs &a, hipStream_t s) {
   if constexpr (GS == 11) {
@@ -1200,6 +1192,13 @@ static int launch_wide_all_parts(const GemmArgs &a, hipStream_t s) {
   return TBIK_ERR_ARG;
 }
 
+// "Wide" tiles: 128 x 128 with 8 waves of 64 x 32, two waves per SIMD (so
+// <= 256 registers per wave: two leaf accumulators plus the tree state of
+// 32 outputs per lane) and a 4-stage ring of 128 KB.  Against 4 waves of
+// 64 x 64 with the same tile (one wave per SIMD, ~460 registers) the copy of
+// the operands into LDS runs at nearly twice the rate: the outstanding
+// L1 -> L2 requests per CU grow with the resident waves, and the average L2
+// latency decides the rate at a given count.
 template <int GS, int U = 1>
 static int launch_wide(const GemmArgs &a, hipStream_t s) {
   if constexpr (GS == 16 || GS == 32) {
