@@ -143,26 +143,29 @@ def test_mfma_exact_leaves_all_shards_per_workgroup(orc, K):
     11-leaf groups), where a workgroup streams every shard of its tile
     through one ring and writes each shard's node as it completes: K = 2048
     (tp 2, 4, 8 give shards of 16, 8 and 4 leaves), K = 4096 (32, 16, 8),
-    K = 5632 (4, 2 or 1 groups of 11 leaves) and K = 8192 (tp 4: 32).  The shard partials and C are bit-exact against the oracle's
-    simulated tensor parallelism on sampled columns; M = 4096 rows of A are
-    the same 512 rows repeated, so rows 512 apart must agree bit for bit."""
-    M, Nw = 4096, 1040                 # 32 x 9 = 288 tiles of 128 x 128, ragged N
+    K = 5632 (4, 2 or 1 groups of 11 leaves) and K = 8192 (tp 4: 32).  C and
+    every shard partial are bit-exact against the oracle's simulated tensor
+    parallelism on sampled rows and columns; the M = 4000 rows of A repeat
+    the same 512 rows (the last copy cut short), so every row block is
+    compared with the same oracle rows."""
+    M, Nw = 4000, 1040                 # 32 x 9 = 288 tiles of 128 x 128, ragged M and N
     A512 = inputs.one_per_block_bf16((512, K), 11400 + K, spread=12)
-    A = A512.repeat(M // 512, 1)
+    A = A512.repeat(8, 1)[:M]
     W = inputs.normal_bf16((Nw, K), 11401 + K, device=DEV)
     cols = _cols(Nw, K + 1)
     ci = torch.from_numpy(cols).to(DEV)
-    rows = np.unique(np.concatenate([np.arange(0, 512, 37), [0, 127, 128, 511]]))
-    ri = torch.from_numpy(rows).to(DEV)
+    rows = np.unique(np.concatenate([np.arange(0, 512, 37), [0, 127, 128, (M - 1) % 512, 511]]))
     Ad = A.to(DEV)
     for tp in ((2, 4, 8) if K < 8192 else (4,)):
         say("exact leaves, all shards per workgroup: K", K, "tp", tp)
         refC, refP = orc.gemm_tpsim(inputs.bits(A512[rows]),
                                     inputs.bits(W.index_select(0, ci)), tp)
         C, _, ws = tb.tbik_gemm_tpsim(Ad, W, tp)
-        for blk in range(M // 512):
-            got = _u32(C[blk * 512:(blk + 1) * 512].index_select(0, ri).index_select(1, ci))
-            assert np.array_equal(got, refC.view(np.uint32)), ("C", K, tp, blk)
-        for t in range(tp):
-            got = _u32(ws[t].index_select(0, ri).index_select(1, ci))
-            assert np.array_equal(got, refP[t].view(np.uint32)), ("partial", K, tp, t)
+        for blk in range((M + 511) // 512):
+            keep = blk * 512 + rows < M              # the last block is ragged
+            bi = torch.from_numpy(blk * 512 + rows[keep]).to(DEV)
+            got = _u32(C.index_select(0, bi).index_select(1, ci))
+            assert np.array_equal(got, refC.view(np.uint32)[keep]), ("C", K, tp, blk)
+            for t in range(tp):
+                got = _u32(ws[t].index_select(0, bi).index_select(1, ci))
+                assert np.array_equal(got, refP[t].view(np.uint32)[keep]), ("partial", K, tp, t)
