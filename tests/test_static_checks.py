@@ -94,3 +94,47 @@ def test_no_hardware_transcendentals_or_packed_fp32(disassembly):
     assert not any(bad.values()), bad
     # the GEMM does run on the matrix cores
     assert any(m.startswith("v_mfma_f32_16x16x32_bf16") for m in _mnemonics(disassembly["gemm"]))
+
+
+def _functions(dis):
+    """name -> list of mnemonics, from llvm-objdump's per-symbol blocks."""
+    out, cur = {}, None
+    for line in dis.splitlines():
+        m = re.match(r"^[0-9a-f]+ <([^>]+)>:", line)
+        if m:
+            cur = out.setdefault(m.group(1), [])
+            continue
+        m = re.match(r"\s+([a-z_][a-z0-9_]*)\s*(.*?)\s*//", line)
+        if cur is not None and m:
+            cur.append((m.group(1), m.group(2)))
+    return out
+
+
+def test_multi_part_ring_kernels_store_exactly_what_their_waits_count(disassembly):
+    """A ring GEMM workgroup that streams several K parts (the last template
+    argument > 1) writes each part's node as exactly 32 buffer stores per
+    lane (4 x 2 blocks of 16 x 16 per wave), and the first leaves of the next
+    part wait for the ring's loads with those stores counted (vmcnt 8 + 32):
+    the vector-memory counter retires loads and stores in issue order.  The
+    code object must hold exactly that: two inlined copies of the part (the
+    first part, then the loop body) with 32 dword buffer stores each and no
+    other global or buffer store, the extended wait on the three leaves
+    after a part boundary only, and otherwise the ring's ordinary wait
+    (vmcnt 8), the final drain (vmcnt 0) or stricter.  Register spills (scratch) are
+    further vector-memory operations; wherever they fall they can only make
+    a fixed wait stricter, never looser, so they are allowed."""
+    funcs = _functions(disassembly["gemm"])
+    multi = {}
+    for name, ins in funcs.items():
+        m = re.match(r"_ZN4tbik11k_gemm_ringI(.*?)EEvNS_8GemmArgsENS_7TileMapE$", name)
+        if m and re.findall(r"L[ib](\d+)", m.group(1))[-1] != "1":
+            multi[name] = ins
+    assert len(multi) >= 8, sorted(multi)
+    for name, ins in multi.items():
+        stores = [op for op, _ in ins if re.match(r"(buffer|global|flat)_store", op)]
+        assert stores == ["buffer_store_dword"] * 64, (name, sorted(set(stores)), len(stores))
+        waits = [int(v) for op, a in ins if op == "s_waitcnt"
+                 for v in re.findall(r"vmcnt\((\d+)\)", a)]
+        assert waits.count(40) == 3, (name, waits)
+        # (lower counts are the compiler's own waits for spill reloads)
+        assert all(w <= 8 or w == 40 for w in waits), (name, sorted(set(waits)))

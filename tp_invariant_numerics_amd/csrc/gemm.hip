@@ -20,6 +20,8 @@
 // `parts` aligned nodes written to a workspace (simulated tensor
 // parallelism, TBIK "technical framework"); k_tree_combine finishes the tree.
 // No atomics; no data-dependent reduction order.
+#include <type_traits>
+
 #include "tbik_device.h"
 #include "tbik_internal.h"
 #include "../../include/tbik.h"
@@ -50,6 +52,7 @@
 #ifndef TBIK_RING_ALL_PARTS
 #define TBIK_RING_ALL_PARTS 1
 #endif
+
 
 // 32-row ring tiles for 16 < M <= 32 (1 = on)
 #ifndef TBIK_THIN
@@ -421,6 +424,8 @@ struct Ring {
   // LM-head and prefill GEMMs ran 6% faster with the copies last, bitwise
   // the same).  The thin tiles keep them first (3% faster there).
   static constexpr bool LATE = MT >= 64;
+  // store instructions per lane of a part's node on the multi-part path
+  static constexpr int XSTORE = R;
 
   u32x4 *ring;
   __amdgpu_buffer_rsrc_t rsa, rsb;
@@ -489,11 +494,16 @@ struct Ring {
   // previous leaf freed (before or after the MFMAs, see LATE).
   // `static_slot`: the slot is known at compile time (the block started at a
   // multiple of S).
+  // XS: store instructions this wave issued after the loads of the stages
+  // still in flight (a previous part's node, see k_gemm_ring): the first
+  // S - 1 leaves of the next part allow them in the wait, since the
+  // vector-memory counter retires loads and stores in issue order.
+  template <int XS = 0>
   __device__ __forceinline__ void step(float (&acc)[R], int j, bool static_slot) {
     // keep the scheduler inside one leaf: unbounded interleaving across a
     // fully unrolled group raises register pressure into spills
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt<DPW * (S - 2)>();
+    wait_vmcnt<DPW * (S - 2) + XS>();
     ring_barrier();
     if constexpr (PIPE) {
       // stage l+j+1 has landed; leaf l+j's slot is free (its fragments are
@@ -539,10 +549,13 @@ struct Ring {
   // leaf j.  Advances l by U.
   // AL: the block is known to start at a leaf index that is a multiple of
   // U (then, with U % S == 0, its ring slots are known at compile time).
-  template <int U, bool AL = true>
+  // XWN: this subtree's leading leaves that take the extra wait of XSTORE
+  // stores (at most S - 1, the first leaves of a part after a part's node
+  // went out).
+  template <int U, bool AL = true, int XWN = 0>
   __device__ __forceinline__ void block(float (&out)[R]) {
     if constexpr (U == 1) {
-      step(out, 0, false);
+      step<(XWN > 0 ? XSTORE : 0)>(out, 0, false);
       l += 1;
     } else {
       constexpr bool SS = AL && (U % S) == 0;
@@ -550,7 +563,7 @@ struct Ring {
 #define TBIK_LEAF_STEP(J)                                                    \
   if constexpr ((J) < U) {                                                   \
     if constexpr (NX == 2 && (J) > 0) merge_leaf<U, (J) - 1, R, NX>(bt, out); \
-    step(bt.X[(J) % NX], (J), SS);                                           \
+    step<((J) < XWN ? XSTORE : 0)>(bt.X[(J) % NX], (J), SS);                \
     if constexpr (NX == 3 && (J) > 0) merge_leaf<U, (J) - 1, R, NX>(bt, out); \
   }
       TBIK_LEAF_STEP(0) TBIK_LEAF_STEP(1) TBIK_LEAF_STEP(2) TBIK_LEAF_STEP(3)
@@ -563,14 +576,14 @@ struct Ring {
 
   // Perfect tree over N leaves (N a power of two): halves recursively,
   // blocks of at most 8 leaves at the bottom.
-  template <int N, bool AL = true>
+  template <int N, bool AL = true, int XWN = 0>
   __device__ __forceinline__ void perfect(float (&out)[R]) {
     if constexpr (N <= 8) {
-      block<N, AL>(out);
+      block<N, AL, XWN>(out);
     } else {
       float left[R];
-      perfect<N / 2, AL>(left);
-      perfect<N / 2, AL>(out);
+      perfect<N / 2, AL, XWN>(left);
+      perfect<N / 2, AL, (XWN > N / 2 ? XWN - N / 2 : 0)>(out);
 #pragma unroll
       for (int r = 0; r < R; ++r) out[r] = left[r] + out[r];
     }
@@ -579,16 +592,16 @@ struct Ring {
   // PAIR over N leaves: the perfect tree over the largest power-of-two
   // prefix, added to PAIR over the rest (an odd tail moves up unchanged, so
   // PAIR is this right fold of its binary decomposition).
-  template <int N, bool AL = true>
+  template <int N, bool AL = true, int XWN = 0>
   __device__ __forceinline__ void pair(float (&out)[R]) {
     constexpr int H = (N >= 256) ? 256 : (N >= 128) ? 128 : (N >= 64) ? 64 : (N >= 32) ? 32
                     : (N >= 16) ? 16 : (N >= 8) ? 8 : (N >= 4) ? 4 : (N >= 2) ? 2 : 1;
     if constexpr (H == N) {
-      perfect<N, AL>(out);
+      perfect<N, AL, XWN>(out);
     } else {
       float left[R];
-      perfect<H, AL>(left);
-      pair<N - H, AL>(out);
+      perfect<H, AL, XWN>(left);
+      pair<N - H, AL, (XWN > H ? XWN - H : 0)>(out);
 #pragma unroll
       for (int r = 0; r < R; ++r) out[r] = left[r] + out[r];
     }
@@ -613,6 +626,8 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   // the host compilation pass only needs the launch stub.
 #if defined(__HIP_DEVICE_COMPILE__)
   using RG = Ring<WM, WN, WAVES_M, WAVES_N, S, NX, PIPE>;
+  static_assert(PPW == 1 || (RG::LATE && !PIPE),
+                "several parts per workgroup: S - 1 stages in flight at a part's end");
   constexpr int MT = RG::MT, NT = RG::NT, R = RG::R, WAVES = RG::WAVES;
   constexpr int DPW = RG::DPW, DPA = RG::DPA, SEGA = RG::SEGA;
   __shared__ u32x4 ring[S * RG::SLOT];
@@ -686,51 +701,61 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   float node[R];
   const int orow = 4 * (lane >> 4);
   bool staged = false;                  // the last part's output went out through LDS
-  // two parts per iteration (with 4 or 8 parts the epilogue's output
-  // addresses, formed once before the loop, spill; they are reloaded only
-  // in the epilogue)
-#pragma unroll 2
+  // Several parts per workgroup (PPW > 1): every part's node leaves as
+  // exactly RG::XSTORE buffer stores per lane (lanes outside C dropped by the
+  // buffer range, no branch), issued behind the S - 1 stages already in
+  // flight for the next part, whose first S - 1 leaves (the first leaves of
+  // its first group) count them in their waits.
+  //
+  // The tree of one part, its first XWV leaves taking that extra wait:
+#define TBIK_PART_TREE(XWV)                                                        \
+  for (int gi = 0; gi < ngroups; ++gi) {                                           \
+    if constexpr (GS > 0 && U == 0) {                                              \
+      /* the whole group as one compile-time PAIR (perfect trees over the */      \
+      /* binary decomposition of GS, right-folded): one node fewer live */        \
+      /* than blocks of 8 pushed through a stack; same tree, same bits */         \
+      if ((XWV) > 0 && gi == 0) rg.template pair<GS, (GS % S) == 0, (XWV)>(node);  \
+      else rg.template pair<GS, (GS % S) == 0>(node);                              \
+    } else if constexpr (GS > 0) {                                                 \
+      /* full 8-leaf blocks (perfect subtrees, aligned in the group) in a */      \
+      /* loop, then the static tail of GS % 8 leaves; PAIR over the group */      \
+      /* is PAIR over these block values, the tail's PAIR the last item. */       \
+      /* Ring slots are static only if every group starts at a multiple */       \
+      /* of S leaves (GS % S == 0). */                                             \
+      constexpr int NB = GS / 8, TAIL = GS % 8, NI = NB + (TAIL ? 1 : 0);          \
+      constexpr int ID = cbit_length(NI - 1);                                      \
+      constexpr bool AL = (GS % S) == 0;                                           \
+      float st[ID > 0 ? ID : 1][R];                                                \
+      _Pragma("clang loop unroll(disable)")                                        \
+      for (int b = 0; b < NB; ++b) {                                               \
+        if ((XWV) > 0 && gi == 0 && b == 0) rg.template block<8, AL, (XWV)>(node); \
+        else rg.template block<8, AL>(node);                                       \
+        pair_push<R, ID>(st, node, b, NI);                                         \
+      }                                                                            \
+      if constexpr (TAIL > 0) {                                                    \
+        if (NB == 0 && (XWV) > 0 && gi == 0) rg.template pair<TAIL, AL, (XWV)>(node); \
+        else rg.template pair<TAIL, AL>(node);                                     \
+        pair_push<R, ID>(st, node, NB, NI);                                        \
+      }                                                                            \
+    } else {                                                                       \
+      float s[GD > 0 ? GD : 1][R];                                                 \
+      const int nblk = G / U;                                                      \
+      for (int cb = 0; cb < nblk; ++cb) {                                          \
+        rg.template block<U>(node);                                                \
+        pair_push<R, GD>(s, node, cb, nblk);                                       \
+      }                                                                            \
+    }                                                                              \
+    pair_push<R, TD>(top, node, gi, gpp);                                          \
+  }
+
+  if constexpr (PPW == 1) {
+#pragma unroll
   for (int pi = 0; pi < PPW; ++pi) {
   const int part = part0 + pi;
   float top[TD > 0 ? TD : 1][R];
   const int ngroups = gpp;
-  for (int gi = 0; gi < ngroups; ++gi) {
-    if constexpr (GS > 0 && U == 0) {
-      // The whole group as one compile-time PAIR (perfect trees over the
-      // binary decomposition of GS, right-folded): one node fewer live than
-      // blocks of 8 pushed through a stack.  Same tree, same bits.
-      rg.template pair<GS, (GS % S) == 0>(node);
-    } else if constexpr (GS > 0) {
-      // Full 8-leaf blocks (perfect subtrees, aligned in the group) in a
-      // loop, then the static tail of GS % 8 leaves; PAIR over the group is
-      // PAIR over these block values, the tail's PAIR being the last item.
-      // Ring slots are static only if every group starts at a multiple
-      // of S leaves (GS % S == 0); otherwise the second group of a part
-      // would be read from the wrong slots.
-      constexpr int NB = GS / 8, TAIL = GS % 8, NI = NB + (TAIL ? 1 : 0);
-      constexpr int ID = cbit_length(NI - 1);
-      constexpr bool AL = (GS % S) == 0;
-      float st[ID > 0 ? ID : 1][R];
-#pragma clang loop unroll(disable)
-      for (int b = 0; b < NB; ++b) {
-        rg.template block<8, AL>(node);
-        pair_push<R, ID>(st, node, b, NI);
-      }
-      if constexpr (TAIL > 0) {
-        rg.template pair<TAIL, AL>(node);
-        pair_push<R, ID>(st, node, NB, NI);
-      }
-    } else {
-      float s[GD > 0 ? GD : 1][R];
-      const int nblk = G / U;
-      for (int cb = 0; cb < nblk; ++cb) {
-        rg.template block<U>(node);
-        pair_push<R, GD>(s, node, cb, nblk);
-      }
-    }
-    pair_push<R, TD>(top, node, gi, gpp);
-  }
-  if (pi == PPW - 1) wait_vmcnt<0>();     // no load into LDS may outlive the workgroup
+  TBIK_PART_TREE(0)
+  wait_vmcnt<0>();                        // no load into LDS may outlive the workgroup
 
   if (glu) {
     // a wave's 16 * WN columns start at a multiple of 32: block pairs
@@ -891,6 +916,46 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   }
   }
   }
+  } else {
+  // Several parts per workgroup: a part's node leaves as exactly RG::XSTORE
+  // buffer stores per lane (an element outside C sent past the end of the
+  // buffer range, no branch: fp32 only, which the launcher checks), issued
+  // behind the S - 1 stages already in flight for the next part; that
+  // part's first S - 1 leaves count them in their waits (TBIK_PART_TREE).
+  // (The part's tree and its node inside one function: with the tree
+  // outside it, the compiler spills the multi-part kernels heavily.)
+  auto run_part = [&](auto xw_tag, const int pi) {
+    constexpr int XW = decltype(xw_tag)::value;
+    float top[TD > 0 ? TD : 1][R];
+    const int ngroups = gpp;
+    TBIK_PART_TREE(XW)
+    if (pi == PPW - 1) wait_vmcnt<0>();   // no load into LDS may outlive the workgroup
+    float *Cp = p.C + (int64_t)(part0 + pi) * p.part_stride;
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Cp + (int64_t)m0 * p.ldc), (short)0, (int)((int64_t)arows * p.ldc * 4),
+        0x00020000);
+#pragma unroll
+    for (int bm = 0; bm < WM; ++bm) {
+#pragma unroll
+      for (int bn = 0; bn < WN; ++bn) {
+        const int col = n0 + wn * 16 * WN + 16 * bn + (lane & 15);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rl = wm * 16 * WM + 16 * bm + orow + i;
+          const bool in = rl < arows && col < p.N;
+          const unsigned off = in ? (unsigned)(((int64_t)rl * p.ldc + col) * 4) : 0x80000000u;
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t,
+                                                node[(bm * WN + bn) * 4 + i]), rc, off, 0, 0);
+        }
+      }
+    }
+  };
+  run_part(std::integral_constant<int, 0>{}, 0);
+  // the later parts, one per iteration (one copy of their tree)
+#pragma clang loop unroll(disable)
+  for (int pi = 1; pi < PPW; ++pi) run_part(std::integral_constant<int, S - 1>{}, pi);
+  }
+#undef TBIK_PART_TREE
   if constexpr (PPW > 1) {
     // no row maxima with several parts per workgroup (the launcher refuses)
   } else if constexpr (WN == 4) {
@@ -1123,11 +1188,18 @@ static int launch_big(const GemmArgs &a, int batch, hipStream_t s) {
   return TBIK_ERR_ARG;
 }
 
+// Several parts per workgroup write fp32 nodes only (no bf16 copy, no row
+// maxima, no SwiGLU), through a 32-bit buffer range over a tile's rows.
+static bool multi_part_ok(const GemmArgs &a, int MT) {
+  return a.C != nullptr && a.Cb == nullptr && a.pmax == nullptr && a.glu == 0 &&
+         (int64_t)MT * a.ldc * 4 < ((int64_t)1 << 31);
+}
+
 template <int WM, int WN, int WAVES_M, int WAVES_N, int S, int NX, bool PIPE, int GS, int U, int GD,
           int TD, int MINB = 1, int PPW = 1>
 static int launch_ring_cfg(const GemmArgs &a, hipStream_t s) {
   constexpr int MT = 16 * WM * WAVES_M, NT = 16 * WN * WAVES_N;
-  if (a.parts % PPW != 0 || (PPW > 1 && a.pmax != nullptr)) return TBIK_ERR_ARG;
+  if (a.parts % PPW != 0 || (PPW > 1 && !multi_part_ok(a, MT))) return TBIK_ERR_ARG;
   // the fused row maxima exist for 64-column waves and for 32-column waves
   // four to a tile row only
   if (a.pmax != nullptr && !(WN == 4 || (WN == 2 && WAVES_N == 4))) return TBIK_ERR_ARG;
@@ -1165,7 +1237,7 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
 // tp = 4 / 8 and the dp = 8 weight gradient ran 9-15% slower this way).
 static bool wide_all_parts(const GemmArgs &a) {
   const int64_t tiles = (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128);
-  return TBIK_RING_ALL_PARTS && (a.gpp == 1 || a.G == 11) && a.pmax == nullptr &&
+  return TBIK_RING_ALL_PARTS && (a.gpp == 1 || a.G == 11) && multi_part_ok(a, 128) &&
          (a.parts == 2 || a.parts == 4 || a.parts == 8) && tiles >= TBIK_RING_PPW_MIN_WG &&
          tiles <= 2 * TBIK_RING_PPW_MIN_WG;
 }
@@ -1209,7 +1281,7 @@ static int launch_wide(const GemmArgs &a, hipStream_t s) {
     // at most 4 groups per part (8 would spill the group stack).  One group
     // per part (the tp = 8 shards of a 224-leaf K): two parts per workgroup
     // while that still gives every CU a workgroup.
-    if (a.gpp == 1 && a.parts % 2 == 0 && a.pmax == nullptr &&
+    if (a.gpp == 1 && a.parts % 2 == 0 && multi_part_ok(a, 128) &&
         (int64_t)((a.M + 127) / 128) * ((a.N + 127) / 128) * (a.parts / 2) >= TBIK_RING_PPW_MIN_WG)
       return launch_ring_cfg<4, 2, 2, 4, 4, 2, false, GS, 0, 0, 1, 1, 2>(a, s);
     switch (a.gpp) {
