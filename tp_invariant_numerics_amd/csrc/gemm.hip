@@ -1232,7 +1232,7 @@ static int launch_narrow(const GemmArgs &a, hipStream_t s) {
 // where the tiles alone give every CU one or two workgroups: a workgroup
 // streams all parts of its tile through one ring, writing each part's node
 // as soon as it is complete, instead of one short workgroup per part
-// (M = 4096, K = N = 2048 at tp = 4, 8 leaves per part: 116 -> 95 us).  With
+// (M = 4096, K = N = 2048 at tp = 4, 8 leaves per part: 116 -> 82 us).  With
 // more tiles the per-part workgroups were faster (M = N = K = 4096 at
 // tp = 4 / 8 and the dp = 8 weight gradient ran 9-15% slower this way).
 static bool wide_all_parts(const GemmArgs &a) {
