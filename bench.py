@@ -41,17 +41,17 @@ M_HEAD, K_HEAD, V_HEAD, TP_HEAD = 512, 4096, 151936, 4
 HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # HBM bytes per launch of HEAD_KERNEL from two rocprofv3 --pmc runs of
 # `bench.py --profile lmhead` (profiles/k_gemm_ring_lmhead_M512_K4096_N151936.md):
-# FETCH_SIZE 1041450 KiB x 2.000 + WRITE_SIZE 339981 KiB x 1.000, the factors
+# FETCH_SIZE 1035959 KiB x 2.000 + WRITE_SIZE 339916 KiB x 1.000, the factors
 # being what a plain 1 GiB device copy reads on the same counters
-# (`bench.py --profile calib`: 524302 KiB fetched, 1048576 KiB written).  Valid
+# (`bench.py --profile calib`: 524301 KiB fetched, 1048576 KiB written).  Valid
 # only for the GEMM sources the counters were taken on (hash below).
-HEAD_TRAFFIC_BYTES = (1041450 * 2 + 339981) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "c5cd66ff8fb9ae58449a3155469cfb3ee5c76bfc364e786ea423938fbe0e2b8f"
+HEAD_TRAFFIC_BYTES = (1035959 * 2 + 339916) * 1024
+HEAD_TRAFFIC_SRC_SHA256 = "5fe13a0099ed7ccdc333dec9fd21ece41f4d262b7b502627a61575cbe00ef1c6"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
-# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64842 KiB x 2.000
+# k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64794 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000.
-HEAD_TP8_TRAFFIC_BYTES = (64842 * 2 + 32768) * 1024
-HEAD_TP8_TRAFFIC_SRC_SHA256 = "c5cd66ff8fb9ae58449a3155469cfb3ee5c76bfc364e786ea423938fbe0e2b8f"
+HEAD_TP8_TRAFFIC_BYTES = (64794 * 2 + 32768) * 1024
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "5fe13a0099ed7ccdc333dec9fd21ece41f4d262b7b502627a61575cbe00ef1c6"
 
 
 def gemm_source_sha256(root):
