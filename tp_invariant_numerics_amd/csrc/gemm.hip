@@ -701,13 +701,9 @@ k_gemm_ring(GemmArgs p, TileMap tm) {
   float node[R];
   const int orow = 4 * (lane >> 4);
   bool staged = false;                  // the last part's output went out through LDS
-  // Several parts per workgroup (PPW > 1): every part's node leaves as
-  // exactly RG::XSTORE buffer stores per lane (lanes outside C dropped by the
-  // buffer range, no branch), issued behind the S - 1 stages already in
-  // flight for the next part, whose first S - 1 leaves (the first leaves of
-  // its first group) count them in their waits.
-  //
-  // The tree of one part, its first XWV leaves taking that extra wait:
+  // The tree of one part.  Its first XWV leaves (the first leaves of its
+  // first group) also allow the previous part's node stores in their waits
+  // (several parts per workgroup, below).
 #define TBIK_PART_TREE(XWV)                                                        \
   for (int gi = 0; gi < ngroups; ++gi) {                                           \
     if constexpr (GS > 0 && U == 0) {                                              \
